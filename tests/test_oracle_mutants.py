@@ -1,0 +1,103 @@
+"""Planted mistakes: copies of the oracle's attention with one plausible bug
+each must be rejected by the independent pins (the torch SDPA library routine
+and the naive rebuild-every-key path).  This shows the pins are sharp enough
+to catch a dropped term, a wrong sign or index, a transposed operand."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from workloads import V2_MULTI, make_inputs
+
+
+def _attend_variant(q, R, d_c, scale, causal, bug):
+    T, H, W = q.shape
+    N = R.shape[0]
+    o = np.zeros((T, H, d_c))
+    for t in range(T):
+        n = N - T + t + 1 if causal else N
+        if bug == "mask_off_by_one":
+            n -= 1
+        if bug == "scale_squared":
+            sc = scale * scale
+        else:
+            sc = scale
+        if bug == "drop_rope_term":
+            s = (q[t, :, :d_c] @ R[:n, :d_c].T) * sc
+        elif bug == "rope_sign":
+            s = (q[t, :, :d_c] @ R[:n, :d_c].T - q[t, :, d_c:] @ R[:n, d_c:].T) * sc
+        else:
+            s = (q[t] @ R[:n].T) * sc
+        e = np.exp(s - s.max(axis=1, keepdims=True))
+        p = e / e.sum(axis=1, keepdims=True)
+        V = R[:n, W - d_c:] if bug == "values_from_tail" else R[:n, :d_c]
+        o[t] = p @ V
+    return o
+
+
+def _absorb_variant(q_nope, q_rope, w_uk, bug):
+    if bug == "heads_shifted":
+        w_uk = np.roll(w_uk, 1, axis=0)
+    if bug == "transposed_head_block":
+        # reads W^UK[h] as if it were stored [d_c, d_n]
+        H, d_n, d_c = w_uk.shape
+        w_uk = w_uk.reshape(H, d_c, d_n).transpose(0, 2, 1)
+    return np.concatenate([np.einsum("...hd,hdc->...hc", q_nope, w_uk), q_rope], axis=-1)
+
+
+def _sdpa(q_abs_b, rows, d_c, scale):
+    T, H, W = q_abs_b.shape
+    N = rows.shape[0]
+    q = torch.from_numpy(np.ascontiguousarray(q_abs_b.transpose(1, 0, 2)))[None]
+    k = torch.from_numpy(rows)[None, None].expand(1, H, N, W)
+    v = torch.from_numpy(np.ascontiguousarray(rows[:, :d_c]))[None, None].expand(1, H, N, d_c)
+    mask = torch.arange(N)[None, :] <= (N - T + torch.arange(T)[:, None])
+    o = torch.nn.functional.scaled_dot_product_attention(q, k, v, attn_mask=mask, scale=scale)
+    return o[0].permute(1, 0, 2).numpy()
+
+
+@pytest.fixture(scope="module")
+def case():
+    w = V2_MULTI.scaled(B=1, H=4, N=96, d_c=64, d_n=32, d_v=16)
+    bt = make_inputs(w)
+    rows = np.concatenate([bt.rows[0], bt.new_rows[0]]).astype(np.float64)
+    return w, bt, rows
+
+
+def _attend_pin(w, bt, rows, attend):
+    q = bt.q_abs[0].astype(np.float64)
+    got = attend(q, rows, w.d_c, w.scale, True)
+    ref = _sdpa(q, rows, w.d_c, w.scale)
+    return np.max(np.abs(got - ref)) <= 1e-12 * max(1.0, np.max(np.abs(ref)))
+
+
+def _absorb_pin(w, bt, rows, absorb):
+    q_abs = absorb(bt.q_nope[0].astype(np.float64), bt.q_rope[0].astype(np.float64),
+                   bt.w_uk.astype(np.float64))
+    o_lat, _ = oracle.attend_ref(q_abs, rows, w.d_c, w.scale, True)
+    o = oracle.out_proj_ref(o_lat, bt.w_uv)
+    ref = oracle.naive_ref(bt.q_nope[0], bt.q_rope[0], bt.w_uk, bt.w_uv, rows, w.d_c,
+                           w.scale, True)
+    return np.max(np.abs(o - ref)) <= 1e-10 * max(1.0, np.max(np.abs(ref)))
+
+
+def test_true_oracle_passes_pins(case):
+    w, bt, rows = case
+    assert _attend_pin(w, bt, rows, lambda *a: oracle.attend_ref(*a)[0])
+    assert _attend_pin(w, bt, rows, lambda *a: _attend_variant(*a, bug=None))
+    assert _absorb_pin(w, bt, rows, lambda qn, qr, wk: oracle.absorb_q_ref(qn, qr, wk))
+
+
+@pytest.mark.parametrize("bug", ["mask_off_by_one", "scale_squared", "drop_rope_term",
+                                 "rope_sign", "values_from_tail"])
+def test_attend_mutant_rejected(case, bug):
+    w, bt, rows = case
+    assert not _attend_pin(w, bt, rows, lambda *a: _attend_variant(*a, bug=bug))
+
+
+@pytest.mark.parametrize("bug", ["heads_shifted", "transposed_head_block"])
+def test_absorb_mutant_rejected(case, bug):
+    w, bt, rows = case
+    assert not _absorb_pin(w, bt, rows, lambda qn, qr, wk: _absorb_variant(qn, qr, wk, bug))
