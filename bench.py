@@ -1,0 +1,213 @@
+#!/usr/bin/env python3
+"""Benchmark one absorbed-MLA decode step on one MI355X.
+
+A step is the whole path for one batch: mla_absorb_q -> mla_cache_append ->
+mla_decode (split-KV + log-sum-exp merge) -> mla_out_proj, on the DeepSeek-V3
+shape workload (16 sequences x 4,096 cached rows, 128 heads, d_c = 512,
+d_rope = 64, bf16).  Inputs are seeded synthetic draws, resident in HBM before
+timing starts.  To measure HBM rather than the 256 MB last-level cache, the
+timed loop rotates over several independent copies of the cache pool and
+weights (--rotate, default 8 x 109 MB).
+
+Prints one JSON line: whole-step tokens/s, the roofline of the dominant launch
+(mla_decode, timed with HIP events on the stream it runs on), and the CPU
+oracle timed on a bounded sample of the same workload on this host.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import platform
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0        # MI355X HBM3E
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16
+
+
+def _cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or "unknown"
+
+
+def _blas_threads() -> int:
+    try:
+        from threadpoolctl import threadpool_info
+        n = [d.get("num_threads", 0) for d in threadpool_info()
+             if d.get("user_api") == "blas"]
+        return max(n) if n else 1
+    except Exception:
+        return 1
+
+
+def cpu_baseline(w, budget_s: float) -> dict:
+    """The fp64 oracle, as it stands, on a sub-batch of the same workload
+    (k sequences of the same shape and distributions), timed on this host."""
+    import oracle
+    from workloads import make_inputs
+
+    def run(k):
+        bt = make_inputs(w.scaled(B=k), seed=w.seed + 1000)
+        t0 = time.perf_counter()
+        oracle.step_ref(bt.q_nope, bt.q_rope, bt.w_uk, bt.w_uv, bt.pool, bt.block_table,
+                        bt.lengths, bt.new_rows, w.d_c, w.scale, w.causal, w.block_size)
+        return time.perf_counter() - t0
+
+    t1 = run(1)
+    k = int(max(1, min(w.B, budget_s / max(t1, 1e-3))))
+    dt = run(k) if k > 1 else t1
+    return {"value": k * w.T / dt, "unit": "tokens/s", "cores": _blas_threads(),
+            "kind": "oracle",
+            "sample": f"fp64 numpy oracle, whole step (absorb, append, decode, out-proj) on "
+                      f"{k} of {w.B} sequences of the same shape, {dt:.2f} s",
+            "host_cpus": os.cpu_count(), "cpu_model": _cpu_model()}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="v3_decode")
+    ap.add_argument("--rotate", type=int, default=8)
+    ap.add_argument("--num-splits", type=int, default=0)
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported "
+              "(this build has no multi-GPU path)", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    from mla_latent_kv_36_amd import binding as mla
+    from mla_latent_kv_36_amd import build as mbuild
+    from mla_latent_kv_36_amd.step import DecodeStep
+    from workloads import BY_NAME, make_inputs
+    from workloads.device import upload
+
+    if not mbuild.built():
+        mbuild.build()
+    mla.load()
+    w = BY_NAME[args.workload]
+    torch.cuda.set_device(0)
+    bt = make_inputs(w)
+    cfg = mla.make_config(w.H, w.d_c, w.d_r, w.d_n, w.d_v, w.block_size, 0.0, w.dtype)
+    total_tokens = int(bt.seq_lens.sum())
+
+    steps = []
+    base = upload(bt)
+    for r in range(args.rotate):
+        dev = dict(base)
+        if r > 0:   # independent copies of everything large
+            for k in ("pool", "w_uk", "w_uv"):
+                dev[k] = base[k].clone()
+        steps.append(DecodeStep(cfg, q_nope=dev["q_nope"], q_rope=dev["q_rope"],
+                                w_uk=dev["w_uk"], w_uv=dev["w_uv"], pool=dev["pool"],
+                                block_table=dev["block_table"], lengths=dev["lengths"],
+                                new_rows=dev["new_rows"], max_len_after=bt.max_seq_len,
+                                causal=w.causal, num_splits=args.num_splits,
+                                total_tokens=total_tokens))
+    splits = mla.mla_decode_num_splits(cfg, w.B, w.T, bt.max_seq_len, total_tokens) \
+        if args.num_splits == 0 else args.num_splits
+
+    # Each phase (and the whole step) over all rotated copies is captured once in
+    # a HIP graph and replayed, so the timing sees GPU time, not Python launch cost.
+    def capture(fn):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for st in steps:
+                fn(st)
+        return g
+
+    graphs = {
+        "step": capture(lambda st: st.run()),
+        "decode": capture(lambda st: st.decode()),
+        "absorb_q": capture(lambda st: st.absorb()),
+        "cache_append": capture(lambda st: st.append()),
+        "out_proj": capture(lambda st: st.out_proj()),
+    }
+    stream = torch.cuda.current_stream()
+    reps = max(1, -(-args.steps // args.rotate))
+    wreps = max(1, -(-args.warmup // args.rotate))
+
+    def timed(g):
+        for _ in range(wreps):
+            g.replay()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            g.replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / (reps * args.rotate)   # ms per call
+
+    ms_step = timed(graphs["step"])
+    ms_decode = timed(graphs["decode"])
+    ms_absorb = timed(graphs["absorb_q"])
+    ms_append = timed(graphs["cache_append"])
+    ms_out = timed(graphs["out_proj"])
+
+    W = w.d_c + w.d_r
+    elem = 2 if w.dtype == "bf16" else 4
+    cache_bytes = total_tokens * W * elem                       # per decode launch
+    pairs = sum(int(n) * w.T for n in bt.seq_lens)               # (query, cached row) pairs
+    decode_flops = pairs * w.H * (2 * W + 2 * w.d_c)
+    achieved = cache_bytes / (ms_decode * 1e-3) / 1e9
+    tokens = w.B * w.T
+    line = {
+        "metric": "MLA decode tokens/s & latent-cache GB/s (% HBM peak, % MFMA) on 1 MI355X",
+        "value": tokens / (ms_step * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": reps * args.rotate,
+        "warmup": wreps * args.rotate,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic (seeded N(0,1) draws, bf16; no model weights)",
+        "config": {"workload": w.name, "B": w.B, "T": w.T, "H": w.H, "d_c": w.d_c,
+                   "d_rope": w.d_r, "d_nope": w.d_n, "d_v": w.d_v,
+                   "cached_rows_before_step": w.N, "rows_attended": int(bt.seq_lens.max()),
+                   "block_size": w.block_size, "num_splits": splits,
+                   "rotated_copies": args.rotate, "timing": "HIP graph replay"},
+        "roofline": {"kernel": "mla_decode (split-KV kernel + log-sum-exp merge)",
+                     "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS, "traffic": None,
+                     "algorithmic_bytes_per_launch": cache_bytes,
+                     "avg_launch_us": ms_decode * 1e3,
+                     "mfma_tflops": decode_flops / (ms_decode * 1e-3) / 1e12,
+                     "mfma_frac": decode_flops / (ms_decode * 1e-3) / 1e12
+                     / MFMA_BF16_PEAK_TFLOPS},
+        "latent_cache_GBps_step": cache_bytes / (ms_step * 1e-3) / 1e9,
+        "decode_tokens_per_s": tokens / (ms_decode * 1e-3),
+        "phases_us": {"absorb_q": ms_absorb * 1e3, "cache_append": ms_append * 1e3,
+                      "decode": ms_decode * 1e3, "out_proj": ms_out * 1e3},
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
+    else:
+        line["cpu_baseline"] = None
+    print(json.dumps(line))
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

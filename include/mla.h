@@ -1,0 +1,206 @@
+/*
+ * libmla: absorbed multi-head latent attention (MLA) decode on AMD CDNA4 (gfx950).
+ *
+ * One decode step of MLA runs as four calls, in this order:
+ *   mla_absorb_q      fold each head's W^UK into its query, once per new token
+ *   mla_cache_append  write the new tokens' [c | k^R] rows into the paged cache
+ *   mla_decode        score the absorbed queries against every cached row,
+ *                     softmax, and sum the cached latents (split-KV + merge)
+ *   mla_out_proj      up-project the latent output once per head through W^UV
+ *
+ * The method is the inference path of "Attention, Part 2: MQA, GQA and MLA",
+ * section "The trick that makes it fast: never rebuild at all": only the latent c
+ * (width d_c) and the decoupled rotary key k^R (width d_rope) are cached per token
+ * ("Multi-head latent attention (MLA)", sections 2 and 3); the keys and values of
+ * the heads are never rebuilt.
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ *  - Pointers named as device buffers are device (HBM) addresses; the caller owns
+ *    every buffer.  The library never allocates, frees, or keeps a pointer after
+ *    a call returns, and holds no global mutable state: calls are thread-safe.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the default stream).  Calls
+ *    only enqueue work on it: MLA_OK means "validated and launched", not "done".
+ *  - All arguments are checked on the host before anything is launched; a call
+ *    that returns an error has launched nothing (MLA_ERR_HIP aside, which reports
+ *    a failed launch).  Contents of device buffers (block ids, sequence lengths)
+ *    cannot be checked on the host: see each call.
+ *  - Element type: `cfg->dtype` applies to q_nope, q_rope, q_abs, W^UK, W^UV, the
+ *    cache pool, new rows and mla_out_proj's output.  Accumulation is fp32; the
+ *    decode outputs (o_lat, lse) are always fp32.
+ *  - Row-major layouts throughout; the last dimension listed is contiguous.
+ *  - Device buffers must be 16-byte aligned (err_flag: 4-byte), MLA_ERR_ALIGN
+ *    otherwise.
+ */
+#ifndef MLA_H
+#define MLA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MLA_OK = 0,
+  MLA_ERR_NULL = 1,        /* a required pointer is NULL                         */
+  MLA_ERR_DIM = 2,         /* a size or config field is out of range             */
+  MLA_ERR_DTYPE = 3,       /* unknown element type                               */
+  MLA_ERR_CAPACITY = 4,    /* sequence would not fit the block table             */
+  MLA_ERR_WORKSPACE = 5,   /* workspace missing or smaller than required         */
+  MLA_ERR_HIP = 6,         /* the HIP runtime reported an error at launch        */
+  MLA_ERR_ALIGN = 7        /* a device pointer is not 16-byte aligned            */
+} mla_status;
+
+typedef enum { MLA_F32 = 0, MLA_BF16 = 1 } mla_dtype;
+
+/* Shapes of one MLA layer.  A cached row is [c (d_c) | k^R (d_rope)], width
+ * W = d_c + d_rope.  The score scale defaults to 1/sqrt(d_nope + d_rope), the
+ * divisor of the page-3 absorbed path ("Attention, Part 2", section "Why position
+ * needs its own key").                                                          */
+typedef struct {
+  int32_t n_heads;       /* H, query heads                                      */
+  int32_t d_c;           /* latent width                                        */
+  int32_t d_rope;        /* decoupled rotary key width d^R_h (may be 0)         */
+  int32_t d_nope;        /* per-head content query width (rows of W^UK[h])      */
+  int32_t d_v;           /* per-head value width (rows of W^UV[h])              */
+  int32_t block_size;    /* tokens per cache page                               */
+  float softmax_scale;   /* 0 => 1/sqrt(d_nope + d_rope)                        */
+  int32_t dtype;         /* mla_dtype                                           */
+} mla_config;
+
+/* Human-readable text for a status code (static storage; never NULL). */
+const char* mla_status_string(int32_t status);
+
+/* Version of this interface; bumped when a signature or layout changes. */
+int32_t mla_abi_version(void);
+
+/*
+ * mla_absorb_q -- query-side absorption ("Attention, Part 2", section "The trick
+ * that makes it fast": the new query is multiplied once by W^UK(h)^T and then
+ * compared with the cached latents; "Multi-head latent attention (MLA)",
+ * section 2 and Exercise 3).
+ *
+ *   q_abs[m, h, 0:d_c]        = sum_d q_nope[m, h, d] * w_uk[h, d, 0:d_c]
+ *   q_abs[m, h, d_c:d_c+d_r]  = q_rope[m, h, :]
+ *
+ * q_nope [M, H, d_nope], q_rope [M, H, d_rope], w_uk [H, d_nope, d_c] (the
+ * per-head view of a linear weight of shape (H*d_nope, d_c)), q_abs [M, H, d_c +
+ * d_rope]; all device, cfg->dtype.  M = sequences x new tokens.  M == 0 launches
+ * nothing.  q_rope may be NULL only if d_rope == 0.
+ */
+mla_status mla_absorb_q(const mla_config* cfg, const void* q_nope, const void* q_rope,
+                        const void* w_uk, void* q_abs, int32_t M, void* stream);
+
+/*
+ * mla_cache_append -- store the new tokens' cache rows.  Only [c | k^R] is kept
+ * per token ("Attention, Part 2", section "The MLA equations": the cache per
+ * token is d_c + d_r numbers).
+ *
+ * The cache is a pool of pages, pool [num_blocks, block_size, W] (device).  Row j
+ * of sequence b lives in page block_table[b, j / block_size] (device int32
+ * [B, max_blocks]) at slot j % block_size.  For i < T_new:
+ *     pool[block_table[b, p / bs], p % bs, :] = new_rows[b, i, :],  p = seq_lens[b] + i
+ * seq_lens (device int32 [B]) holds the lengths BEFORE the append and is not
+ * modified; the caller advances it.  max_seq_len_host is the host-side bound
+ * max_b(seq_lens[b]) + T_new; it must be <= max_blocks * block_size
+ * (MLA_ERR_CAPACITY).  On the device, a row whose page index or page id would
+ * fall outside [0, max_blocks) or [0, num_blocks) is skipped, never written.
+ */
+mla_status mla_cache_append(const mla_config* cfg, void* pool, int32_t num_blocks,
+                            const int32_t* block_table, int32_t max_blocks,
+                            const int32_t* seq_lens, const void* new_rows, int32_t B,
+                            int32_t T_new, int32_t max_seq_len_host, void* stream);
+
+/*
+ * Split-KV planning for mla_decode.  The cached rows of each sequence are cut
+ * into `num_splits` contiguous page ranges of equal page count (the last may be
+ * shorter or empty); each range is attended on its own and the partial results
+ * are merged by log-sum-exp.  mla_decode_num_splits returns the number the
+ * library would choose (>= 1) for this batch; total_tokens_host is the sum of the
+ * sequence lengths if the caller knows it, else 0.
+ *
+ * mla_decode_workspace_size returns the device workspace mla_decode needs for a
+ * given num_splits (0 = the library's choice, as above); 0 bytes when no merge
+ * is needed.  Returns (size_t)-1 for an invalid config.
+ */
+int32_t mla_decode_num_splits(const mla_config* cfg, int32_t B, int32_t T,
+                              int32_t max_seq_len_host, int64_t total_tokens_host);
+size_t mla_decode_workspace_size(const mla_config* cfg, int32_t B, int32_t T,
+                                 int32_t max_seq_len_host, int64_t total_tokens_host,
+                                 int32_t num_splits);
+
+/*
+ * mla_decode -- attention in latent space ("Attention, Part 2", sections "The
+ * trick that makes it fast" and "Why position needs its own key"; "How DeepSeek
+ * Rewrote the Transformer", section "Absorbed projections", point 3: the values
+ * are the first d_c columns of the cached row).  For every sequence b, new token
+ * t < T and head h, with R_j = the j-th cached row of b:
+ *
+ *   n      = causal ? seq_lens[b] - T + t + 1 : seq_lens[b]   (rows visible)
+ *   s_j    = scale * <q_abs[b, t, h, :], R_j>                 j < n
+ *   p_j    = exp(s_j - max s) / sum_k exp(s_k - max s)
+ *   o_lat[b, t, h, :] = sum_j p_j R_j[0:d_c]
+ *   lse[b, t, h]      = max s + log sum_k exp(s_k - max s)    (natural log)
+ *
+ * A query that sees no row gets o_lat = 0 and lse = -inf.
+ *
+ * q_abs [B, T, H, W] (cfg->dtype), pool / block_table as in mla_cache_append,
+ * seq_lens [B] (device, lengths INCLUDING the T new tokens), o_lat [B, T, H, d_c]
+ * fp32, lse [B, T, H] fp32 or NULL.  max_seq_len_host >= max_b seq_lens[b] and <=
+ * max_blocks * block_size; rows past it are not attended.  On the device a page
+ * id outside [0, num_blocks) is clamped into range (memory safety only: the
+ * result is then meaningless).  causal is 0 or 1.  num_splits: 0 = library's
+ * choice, else the split count to use.  workspace: device memory of at least
+ * mla_decode_workspace_size(...) bytes for the same arguments, may be NULL when
+ * that size is 0.  The workspace is scratch: its contents on entry do not matter.
+ */
+mla_status mla_decode(const mla_config* cfg, const void* q_abs, const void* pool,
+                      int32_t num_blocks, const int32_t* block_table, int32_t max_blocks,
+                      const int32_t* seq_lens, int32_t max_seq_len_host, int32_t B,
+                      int32_t T, int32_t causal, int32_t num_splits,
+                      int64_t total_tokens_host, void* workspace, size_t workspace_bytes,
+                      float* o_lat, float* lse, void* stream);
+
+/*
+ * mla_out_proj -- output-side up-projection, applied once per head after the
+ * latent-space sum ("Attention, Part 2", section "The trick that makes it fast":
+ * W_uv(h) is applied just once at the end).
+ *
+ *   out[m, h, v] = sum_c w_uv[h, v, c] * o_lat[m, h, c]
+ *
+ * o_lat [M, H, d_c] fp32, w_uv [H, d_v, d_c] (cfg->dtype; the per-head view of a
+ * linear weight of shape (H*d_v, d_c)), out [M, H, d_v] (cfg->dtype).  M == 0
+ * launches nothing.
+ */
+mla_status mla_out_proj(const mla_config* cfg, const float* o_lat, const void* w_uv,
+                        void* out, int32_t M, void* stream);
+
+/*
+ * Debug and test helpers.
+ *
+ * mla_gather_rows: dense[b, j, :] = the j-th cached row of sequence b, for
+ * j < min(seq_lens[b], max_seq_len_host), through the same page addressing as
+ * mla_decode.  dense [B, max_seq_len_host, W] device, cfg->dtype; rows at or past a
+ * sequence's length are left untouched.
+ *
+ * mla_validate_block_table: checks on the device that every page a sequence
+ * uses (p < ceil(seq_lens[b] / block_size)) has p < max_blocks and an id in
+ * [0, num_blocks).  *err_flag (device int32) is set to 0, then bit 0 is set for a
+ * bad page id and bit 1 for a sequence longer than the table.
+ */
+mla_status mla_gather_rows(const mla_config* cfg, const void* pool, int32_t num_blocks,
+                           const int32_t* block_table, int32_t max_blocks,
+                           const int32_t* seq_lens, int32_t B, int32_t max_seq_len_host,
+                           void* dense, void* stream);
+mla_status mla_validate_block_table(const int32_t* block_table, int32_t B,
+                                    int32_t max_blocks, const int32_t* seq_lens,
+                                    int32_t block_size, int32_t num_blocks,
+                                    int32_t* err_flag, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MLA_H */

@@ -1,0 +1,200 @@
+"""Python binding of libmla: the C ABI calls under the same names, taking
+torch tensors for device buffers.
+
+Argument marshalling only: each wrapper checks that tensors are contiguous and
+of the element type the call expects, passes their device addresses and the
+current HIP stream to the C function, and raises ``RuntimeError`` with the
+library's message on an error status.  Every step of the computation runs in
+the library's HIP kernels.  If ``libmla.so`` is missing, loading fails loudly:
+there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmla.so")
+
+MLA_F32 = 0
+MLA_BF16 = 1
+_TORCH_DTYPE = {MLA_F32: torch.float32, MLA_BF16: torch.bfloat16}
+
+
+class MlaConfig(ctypes.Structure):
+    _fields_ = [("n_heads", ctypes.c_int32), ("d_c", ctypes.c_int32),
+                ("d_rope", ctypes.c_int32), ("d_nope", ctypes.c_int32),
+                ("d_v", ctypes.c_int32), ("block_size", ctypes.c_int32),
+                ("softmax_scale", ctypes.c_float), ("dtype", ctypes.c_int32)]
+
+
+def make_config(n_heads: int, d_c: int, d_rope: int, d_nope: int, d_v: int,
+                block_size: int = 64, softmax_scale: float = 0.0,
+                dtype: str | int = "bf16") -> MlaConfig:
+    if isinstance(dtype, str):
+        dtype = {"f32": MLA_F32, "bf16": MLA_BF16}[dtype]
+    return MlaConfig(n_heads, d_c, d_rope, d_nope, d_v, block_size, softmax_scale, dtype)
+
+
+_lib: Optional[ctypes.CDLL] = None
+
+_P = ctypes.c_void_p
+_I = ctypes.c_int32
+_CFG = ctypes.POINTER(MlaConfig)
+_SIGNATURES = {
+    "mla_status_string": (ctypes.c_char_p, [_I]),
+    "mla_abi_version": (_I, []),
+    "mla_absorb_q": (_I, [_CFG, _P, _P, _P, _P, _I, _P]),
+    "mla_cache_append": (_I, [_CFG, _P, _I, _P, _I, _P, _P, _I, _I, _I, _P]),
+    "mla_decode_num_splits": (_I, [_CFG, _I, _I, _I, ctypes.c_int64]),
+    "mla_decode_workspace_size": (ctypes.c_size_t, [_CFG, _I, _I, _I, ctypes.c_int64, _I]),
+    "mla_decode": (_I, [_CFG, _P, _P, _I, _P, _I, _P, _I, _I, _I, _I, _I, ctypes.c_int64, _P,
+                        ctypes.c_size_t, _P, _P, _P]),
+    "mla_out_proj": (_I, [_CFG, _P, _P, _P, _I, _P]),
+    "mla_gather_rows": (_I, [_CFG, _P, _I, _P, _I, _P, _I, _I, _P, _P]),
+    "mla_validate_block_table": (_I, [_P, _I, _I, _P, _I, _I, _P, _P]),
+}
+
+
+def load(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load libmla.so (once).  Raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(path):
+            raise ImportError(f"{path} not found: build it with "
+                              "`python -m mla_latent_kv_36_amd.build`")
+        lib = ctypes.CDLL(path)
+        for name, (res, args) in _SIGNATURES.items():
+            fn = getattr(lib, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = lib
+    return _lib
+
+
+def _check(status: int) -> None:
+    if status != 0:
+        raise RuntimeError(load().mla_status_string(status).decode())
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _dev(t: torch.Tensor, dtype: torch.dtype, name: str) -> torch.Tensor:
+    if t.dtype != dtype:
+        raise TypeError(f"{name}: expected {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name}: must be contiguous")
+    return t
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def mla_status_string(code: int) -> str:
+    return load().mla_status_string(code).decode()
+
+
+def mla_abi_version() -> int:
+    return int(load().mla_abi_version())
+
+
+def mla_absorb_q(cfg: MlaConfig, q_nope: torch.Tensor, q_rope: Optional[torch.Tensor],
+                 w_uk: torch.Tensor, q_abs: torch.Tensor, stream=None) -> None:
+    """q_abs[m,h] = [q_nope[m,h] . W^UK[h] | q_rope[m,h]]; shapes [M,H,*]."""
+    dt = _TORCH_DTYPE[cfg.dtype]
+    M = q_nope.shape[0]
+    _dev(q_nope, dt, "q_nope"), _dev(w_uk, dt, "w_uk"), _dev(q_abs, dt, "q_abs")
+    if q_rope is not None:
+        _dev(q_rope, dt, "q_rope")
+    _check(load().mla_absorb_q(ctypes.byref(cfg), _ptr(q_nope), _ptr(q_rope), _ptr(w_uk),
+                               _ptr(q_abs), M, _stream(stream)))
+
+
+def mla_cache_append(cfg: MlaConfig, pool: torch.Tensor, block_table: torch.Tensor,
+                     seq_lens: torch.Tensor, new_rows: torch.Tensor, max_seq_len_host: int,
+                     stream=None) -> None:
+    """Write new_rows [B, T_new, W] after each sequence's seq_lens[b] rows."""
+    dt = _TORCH_DTYPE[cfg.dtype]
+    _dev(pool, dt, "pool"), _dev(new_rows, dt, "new_rows")
+    _dev(block_table, torch.int32, "block_table"), _dev(seq_lens, torch.int32, "seq_lens")
+    B, T_new = new_rows.shape[0], new_rows.shape[1]
+    _check(load().mla_cache_append(ctypes.byref(cfg), _ptr(pool), pool.shape[0],
+                                   _ptr(block_table), block_table.shape[1], _ptr(seq_lens),
+                                   _ptr(new_rows), B, T_new, int(max_seq_len_host),
+                                   _stream(stream)))
+
+
+def mla_decode_num_splits(cfg: MlaConfig, B: int, T: int, max_seq_len_host: int,
+                          total_tokens_host: int = 0) -> int:
+    return int(load().mla_decode_num_splits(ctypes.byref(cfg), B, T, int(max_seq_len_host),
+                                            int(total_tokens_host)))
+
+
+def mla_decode_workspace_size(cfg: MlaConfig, B: int, T: int, max_seq_len_host: int,
+                              total_tokens_host: int = 0, num_splits: int = 0) -> int:
+    n = load().mla_decode_workspace_size(ctypes.byref(cfg), B, T, int(max_seq_len_host),
+                                         int(total_tokens_host), int(num_splits))
+    if n == ctypes.c_size_t(-1).value:
+        raise RuntimeError("mla_decode_workspace_size: invalid configuration")
+    return int(n)
+
+
+def mla_decode(cfg: MlaConfig, q_abs: torch.Tensor, pool: torch.Tensor,
+               block_table: torch.Tensor, seq_lens: torch.Tensor, max_seq_len_host: int,
+               o_lat: torch.Tensor, lse: Optional[torch.Tensor] = None, *, causal: bool = True,
+               num_splits: int = 0, total_tokens_host: int = 0,
+               workspace: Optional[torch.Tensor] = None, stream=None) -> None:
+    """Latent attention of q_abs [B,T,H,W] over the paged cache -> o_lat [B,T,H,d_c] f32."""
+    dt = _TORCH_DTYPE[cfg.dtype]
+    _dev(q_abs, dt, "q_abs"), _dev(pool, dt, "pool"), _dev(o_lat, torch.float32, "o_lat")
+    _dev(block_table, torch.int32, "block_table"), _dev(seq_lens, torch.int32, "seq_lens")
+    if lse is not None:
+        _dev(lse, torch.float32, "lse")
+    B, T = q_abs.shape[0], q_abs.shape[1]
+    ws_bytes = 0
+    if workspace is not None:
+        ws_bytes = workspace.numel() * workspace.element_size()
+    _check(load().mla_decode(ctypes.byref(cfg), _ptr(q_abs), _ptr(pool), pool.shape[0],
+                             _ptr(block_table), block_table.shape[1], _ptr(seq_lens),
+                             int(max_seq_len_host), B, T, 1 if causal else 0, int(num_splits),
+                             int(total_tokens_host), _ptr(workspace), ws_bytes, _ptr(o_lat),
+                             _ptr(lse), _stream(stream)))
+
+
+def mla_out_proj(cfg: MlaConfig, o_lat: torch.Tensor, w_uv: torch.Tensor, out: torch.Tensor,
+                 stream=None) -> None:
+    """out[m,h,v] = sum_c W^UV[h,v,c] o_lat[m,h,c]; o_lat [M,H,d_c] f32."""
+    dt = _TORCH_DTYPE[cfg.dtype]
+    _dev(o_lat, torch.float32, "o_lat"), _dev(w_uv, dt, "w_uv"), _dev(out, dt, "out")
+    _check(load().mla_out_proj(ctypes.byref(cfg), _ptr(o_lat), _ptr(w_uv), _ptr(out),
+                               o_lat.shape[0], _stream(stream)))
+
+
+def mla_gather_rows(cfg: MlaConfig, pool: torch.Tensor, block_table: torch.Tensor,
+                    seq_lens: torch.Tensor, max_seq_len_host: int, dense: torch.Tensor,
+                    stream=None) -> None:
+    dt = _TORCH_DTYPE[cfg.dtype]
+    _dev(pool, dt, "pool"), _dev(dense, dt, "dense")
+    _dev(block_table, torch.int32, "block_table"), _dev(seq_lens, torch.int32, "seq_lens")
+    _check(load().mla_gather_rows(ctypes.byref(cfg), _ptr(pool), pool.shape[0],
+                                  _ptr(block_table), block_table.shape[1], _ptr(seq_lens),
+                                  block_table.shape[0], int(max_seq_len_host), _ptr(dense),
+                                  _stream(stream)))
+
+
+def mla_validate_block_table(block_table: torch.Tensor, seq_lens: torch.Tensor,
+                             block_size: int, num_blocks: int, err_flag: torch.Tensor,
+                             stream=None) -> None:
+    _dev(block_table, torch.int32, "block_table"), _dev(seq_lens, torch.int32, "seq_lens")
+    _dev(err_flag, torch.int32, "err_flag")
+    _check(load().mla_validate_block_table(_ptr(block_table), block_table.shape[0],
+                                           block_table.shape[1], _ptr(seq_lens), block_size,
+                                           num_blocks, _ptr(err_flag), _stream(stream)))

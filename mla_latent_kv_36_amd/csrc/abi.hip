@@ -1,0 +1,276 @@
+// The C ABI of libmla: argument checks on the host, split planning, dispatch.
+// Every check runs before the first launch, so a call that fails launches
+// nothing.  No call allocates, frees or keeps device memory.
+#include <math.h>
+#include <stdint.h>
+
+#include "launch.h"
+#include "mla.h"
+
+namespace {
+
+constexpr int kCUs = 256;            // compute units of one MI355X
+constexpr int kMaxDc = 2048;         // generic kernel: latent columns per row
+constexpr int kMaxDnope = 4096;      // absorb kernel: LDS holds 16 rows of q_nope
+constexpr int kMaxSplits = 65535;
+
+bool aligned16(const void* ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15u) == 0; }
+
+size_t elem_size(int dtype) { return dtype == MLA_F32 ? 4 : 2; }
+
+mla_status check_cfg(const mla_config* c) {
+  if (c == nullptr) return MLA_ERR_NULL;
+  if (c->dtype != MLA_F32 && c->dtype != MLA_BF16) return MLA_ERR_DTYPE;
+  if (c->n_heads <= 0 || c->n_heads > 65535 || c->d_c <= 0 || c->d_c > kMaxDc ||
+      c->d_rope < 0 || c->d_rope > kMaxDc || c->block_size <= 0 || c->block_size > 65536 ||
+      c->d_nope < 0 || c->d_v < 0)
+    return MLA_ERR_DIM;
+  if (!(c->softmax_scale >= 0.0f) || !isfinite(c->softmax_scale)) return MLA_ERR_DIM;
+  if (c->softmax_scale == 0.0f && c->d_nope + c->d_rope <= 0) return MLA_ERR_DIM;
+  return MLA_OK;
+}
+
+float softmax_scale(const mla_config* c) {
+  return c->softmax_scale > 0.0f ? c->softmax_scale
+                                 : 1.0f / sqrtf((float)(c->d_nope + c->d_rope));
+}
+
+bool use_mfma(const mla_config* c, int T) {
+  return mla::decode_mfma_supported(c->dtype, c->d_c, c->d_rope, c->block_size, T, c->n_heads);
+}
+
+// Split plan: the rows of the longest sequence are cut into `splits` ranges of
+// `chunk` pages each.  Shorter sequences use the leading ranges only.
+struct Plan {
+  int splits;
+  int chunk;
+};
+
+int heuristic_splits(const mla_config* c, int B, int T, int pages_max, int64_t total_tokens) {
+  if (pages_max <= 1) return 1;
+  const int64_t bs = c->block_size;
+  const int64_t pages_total =
+      total_tokens > 0 ? (total_tokens + bs - 1) / bs + B : (int64_t)B * pages_max;
+  if (use_mfma(c, T)) {
+    // Units of work are (row group, page).  Aim for about two workgroups per
+    // compute unit, but keep at least 4 pages per workgroup so the partial
+    // outputs (128 KiB per workgroup) stay well below the cache bytes read.
+    const int64_t groups = (int64_t)T * c->n_heads / 64;
+    const int64_t work = pages_total * groups;
+    int64_t chunk = (work + 2 * kCUs - 1) / (2 * kCUs);
+    if (chunk < 4) chunk = 4;
+    return (int)((pages_max + chunk - 1) / chunk);
+  }
+  const int64_t rows = (int64_t)B * T * c->n_heads;
+  int64_t s = (4 * kCUs + rows - 1) / rows;
+  if (s > pages_max) s = pages_max;
+  return (int)(s < 1 ? 1 : s);
+}
+
+Plan make_plan(const mla_config* c, int B, int T, int max_seq_len, int64_t total_tokens,
+               int num_splits) {
+  const int bs = c->block_size;
+  const int pages_max = max_seq_len > 0 ? (max_seq_len + bs - 1) / bs : 0;
+  int want = num_splits > 0 ? num_splits : heuristic_splits(c, B, T, pages_max, total_tokens);
+  if (want > pages_max) want = pages_max;
+  if (want < 1) want = 1;
+  const int chunk = pages_max > 0 ? (pages_max + want - 1) / want : 1;
+  const int splits = pages_max > 0 ? (pages_max + chunk - 1) / chunk : 1;
+  return Plan{splits, chunk};
+}
+
+size_t round256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+size_t partial_bytes(const mla_config* c, int B, int T, int splits, size_t* lse_offset) {
+  const size_t rows = (size_t)B * splits * T * c->n_heads;
+  const size_t o_bytes = round256(rows * c->d_c * sizeof(float));
+  if (lse_offset) *lse_offset = o_bytes;
+  return o_bytes + round256(rows * sizeof(float));
+}
+
+mla_status hip_status(hipError_t e) { return e == hipSuccess ? MLA_OK : MLA_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+const char* mla_status_string(int32_t status) {
+  switch (status) {
+    case MLA_OK: return "MLA_OK: success";
+    case MLA_ERR_NULL: return "MLA_ERR_NULL: a required pointer is NULL";
+    case MLA_ERR_DIM: return "MLA_ERR_DIM: a size or config field is out of range";
+    case MLA_ERR_DTYPE: return "MLA_ERR_DTYPE: unknown element type";
+    case MLA_ERR_CAPACITY: return "MLA_ERR_CAPACITY: sequence would not fit the block table";
+    case MLA_ERR_WORKSPACE: return "MLA_ERR_WORKSPACE: workspace missing or too small";
+    case MLA_ERR_HIP: return "MLA_ERR_HIP: the HIP runtime reported an error at launch";
+    case MLA_ERR_ALIGN: return "MLA_ERR_ALIGN: a device pointer is not 16-byte aligned";
+    default: return "unknown mla_status";
+  }
+}
+
+int32_t mla_abi_version(void) { return 1; }
+
+mla_status mla_absorb_q(const mla_config* cfg, const void* q_nope, const void* q_rope,
+                        const void* w_uk, void* q_abs, int32_t M, void* stream) {
+  mla_status st = check_cfg(cfg);
+  if (st != MLA_OK) return st;
+  if (M < 0 || cfg->d_nope <= 0 || cfg->d_nope > kMaxDnope) return MLA_ERR_DIM;
+  if (M == 0) return MLA_OK;
+  if (q_nope == nullptr || w_uk == nullptr || q_abs == nullptr ||
+      (cfg->d_rope > 0 && q_rope == nullptr))
+    return MLA_ERR_NULL;
+  if (!aligned16(q_nope) || !aligned16(w_uk) || !aligned16(q_abs) ||
+      (q_rope != nullptr && !aligned16(q_rope)))
+    return MLA_ERR_ALIGN;
+  if ((int64_t)(M + 15) / 16 > 65535) return MLA_ERR_DIM;
+  return hip_status(mla::launch_absorb_q(cfg->dtype, q_nope, q_rope, w_uk, q_abs, M,
+                                         cfg->n_heads, cfg->d_nope, cfg->d_c, cfg->d_rope,
+                                         static_cast<hipStream_t>(stream)));
+}
+
+mla_status mla_cache_append(const mla_config* cfg, void* pool, int32_t num_blocks,
+                            const int32_t* block_table, int32_t max_blocks,
+                            const int32_t* seq_lens, const void* new_rows, int32_t B,
+                            int32_t T_new, int32_t max_seq_len_host, void* stream) {
+  mla_status st = check_cfg(cfg);
+  if (st != MLA_OK) return st;
+  if (B < 0 || T_new < 0 || num_blocks <= 0 || max_blocks <= 0 || max_seq_len_host < 0)
+    return MLA_ERR_DIM;
+  if ((int64_t)max_seq_len_host > (int64_t)max_blocks * cfg->block_size) return MLA_ERR_CAPACITY;
+  if (B == 0 || T_new == 0) return MLA_OK;
+  if (pool == nullptr || block_table == nullptr || seq_lens == nullptr || new_rows == nullptr)
+    return MLA_ERR_NULL;
+  if (!aligned16(pool) || !aligned16(new_rows) || !aligned16(block_table) || !aligned16(seq_lens))
+    return MLA_ERR_ALIGN;
+  if ((int64_t)B * T_new > 0x7fffffffLL) return MLA_ERR_DIM;
+  const int row_bytes = (cfg->d_c + cfg->d_rope) * (int)elem_size(cfg->dtype);
+  return hip_status(mla::launch_append(pool, num_blocks, block_table, max_blocks, seq_lens,
+                                       new_rows, B, T_new, cfg->block_size, row_bytes,
+                                       static_cast<hipStream_t>(stream)));
+}
+
+int32_t mla_decode_num_splits(const mla_config* cfg, int32_t B, int32_t T,
+                              int32_t max_seq_len_host, int64_t total_tokens_host) {
+  if (check_cfg(cfg) != MLA_OK || B < 0 || T < 1 || max_seq_len_host < 0) return 1;
+  return make_plan(cfg, B, T, max_seq_len_host, total_tokens_host, 0).splits;
+}
+
+size_t mla_decode_workspace_size(const mla_config* cfg, int32_t B, int32_t T,
+                                 int32_t max_seq_len_host, int64_t total_tokens_host,
+                                 int32_t num_splits) {
+  if (check_cfg(cfg) != MLA_OK || B < 0 || T < 1 || max_seq_len_host < 0 || num_splits < 0)
+    return (size_t)-1;
+  const Plan pl = make_plan(cfg, B, T, max_seq_len_host, total_tokens_host, num_splits);
+  if (pl.splits <= 1) return 0;
+  return partial_bytes(cfg, B, T, pl.splits, nullptr);
+}
+
+mla_status mla_decode(const mla_config* cfg, const void* q_abs, const void* pool,
+                      int32_t num_blocks, const int32_t* block_table, int32_t max_blocks,
+                      const int32_t* seq_lens, int32_t max_seq_len_host, int32_t B,
+                      int32_t T, int32_t causal, int32_t num_splits,
+                      int64_t total_tokens_host, void* workspace, size_t workspace_bytes,
+                      float* o_lat, float* lse, void* stream) {
+  mla_status st = check_cfg(cfg);
+  if (st != MLA_OK) return st;
+  if (B < 0 || T < 1 || num_blocks <= 0 || max_blocks <= 0 || max_seq_len_host < 0 ||
+      num_splits < 0 || num_splits > kMaxSplits || (causal != 0 && causal != 1))
+    return MLA_ERR_DIM;
+  if ((int64_t)max_seq_len_host > (int64_t)max_blocks * cfg->block_size) return MLA_ERR_CAPACITY;
+  if ((int64_t)B * T * cfg->n_heads > 0x7fffffffLL) return MLA_ERR_DIM;
+  if (B == 0) return MLA_OK;
+  if (q_abs == nullptr || pool == nullptr || block_table == nullptr || seq_lens == nullptr ||
+      o_lat == nullptr)
+    return MLA_ERR_NULL;
+  if (!aligned16(q_abs) || !aligned16(pool) || !aligned16(o_lat) || !aligned16(block_table) ||
+      !aligned16(seq_lens) || (lse != nullptr && !aligned16(lse)) ||
+      (workspace != nullptr && !aligned16(workspace)))
+    return MLA_ERR_ALIGN;
+
+  const Plan pl = make_plan(cfg, B, T, max_seq_len_host, total_tokens_host, num_splits);
+  size_t lse_off = 0;
+  const size_t need = pl.splits > 1 ? partial_bytes(cfg, B, T, pl.splits, &lse_off) : 0;
+  if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return MLA_ERR_WORKSPACE;
+
+  mla::DecodeParams p{};
+  p.q_abs = q_abs;
+  p.pool = pool;
+  p.block_table = block_table;
+  p.seq_lens = seq_lens;
+  p.o_lat = o_lat;
+  p.lse = lse;
+  p.part_o = need > 0 ? static_cast<float*>(workspace) : nullptr;
+  p.part_lse = need > 0 ? reinterpret_cast<float*>(static_cast<char*>(workspace) + lse_off)
+                        : nullptr;
+  p.B = B;
+  p.T = T;
+  p.H = cfg->n_heads;
+  p.d_c = cfg->d_c;
+  p.d_r = cfg->d_rope;
+  p.block_size = cfg->block_size;
+  p.num_blocks = num_blocks;
+  p.max_blocks = max_blocks;
+  p.cap = max_seq_len_host;
+  p.causal = causal;
+  p.num_splits = pl.splits;
+  p.chunk_pages = pl.chunk;
+  p.scale_log2 = softmax_scale(cfg) * 1.4426950408889634f;
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = use_mfma(cfg, T) ? mla::launch_decode_mfma(p, s)
+                                  : mla::launch_decode_generic(p, cfg->dtype, s);
+  if (e != hipSuccess) return MLA_ERR_HIP;
+  if (pl.splits > 1) {
+    e = mla::launch_combine(p, s);
+    if (e != hipSuccess) return MLA_ERR_HIP;
+  }
+  return MLA_OK;
+}
+
+mla_status mla_out_proj(const mla_config* cfg, const float* o_lat, const void* w_uv, void* out,
+                        int32_t M, void* stream) {
+  mla_status st = check_cfg(cfg);
+  if (st != MLA_OK) return st;
+  if (M < 0 || cfg->d_v <= 0) return MLA_ERR_DIM;
+  if (M == 0) return MLA_OK;
+  if (o_lat == nullptr || w_uv == nullptr || out == nullptr) return MLA_ERR_NULL;
+  if (!aligned16(o_lat) || !aligned16(w_uv) || !aligned16(out)) return MLA_ERR_ALIGN;
+  if ((int64_t)(M + 15) / 16 > 65535 || (int64_t)(cfg->d_v + 15) / 16 > 65535)
+    return MLA_ERR_DIM;
+  return hip_status(mla::launch_out_proj(cfg->dtype, o_lat, w_uv, out, M, cfg->n_heads,
+                                         cfg->d_c, cfg->d_v, static_cast<hipStream_t>(stream)));
+}
+
+mla_status mla_gather_rows(const mla_config* cfg, const void* pool, int32_t num_blocks,
+                           const int32_t* block_table, int32_t max_blocks,
+                           const int32_t* seq_lens, int32_t B, int32_t max_seq_len_host,
+                           void* dense, void* stream) {
+  mla_status st = check_cfg(cfg);
+  if (st != MLA_OK) return st;
+  if (B < 0 || num_blocks <= 0 || max_blocks <= 0 || max_seq_len_host < 0 || B > 65535)
+    return MLA_ERR_DIM;
+  if ((int64_t)max_seq_len_host > (int64_t)max_blocks * cfg->block_size) return MLA_ERR_CAPACITY;
+  if (B == 0 || max_seq_len_host == 0) return MLA_OK;
+  if (pool == nullptr || block_table == nullptr || seq_lens == nullptr || dense == nullptr)
+    return MLA_ERR_NULL;
+  if (!aligned16(pool) || !aligned16(dense) || !aligned16(block_table) || !aligned16(seq_lens))
+    return MLA_ERR_ALIGN;
+  const int row_bytes = (cfg->d_c + cfg->d_rope) * (int)elem_size(cfg->dtype);
+  return hip_status(mla::launch_gather(pool, num_blocks, block_table, max_blocks, seq_lens, B,
+                                       max_seq_len_host, cfg->block_size, row_bytes, dense,
+                                       static_cast<hipStream_t>(stream)));
+}
+
+mla_status mla_validate_block_table(const int32_t* block_table, int32_t B, int32_t max_blocks,
+                                    const int32_t* seq_lens, int32_t block_size,
+                                    int32_t num_blocks, int32_t* err_flag, void* stream) {
+  if (B < 0 || B > 65535 || max_blocks <= 0 || block_size <= 0 || num_blocks <= 0)
+    return MLA_ERR_DIM;
+  if (err_flag == nullptr || (B > 0 && (block_table == nullptr || seq_lens == nullptr)))
+    return MLA_ERR_NULL;
+  if ((reinterpret_cast<uintptr_t>(err_flag) & 3u) != 0) return MLA_ERR_ALIGN;
+  return hip_status(mla::launch_validate(block_table, B, max_blocks, seq_lens, block_size,
+                                         num_blocks, err_flag, static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

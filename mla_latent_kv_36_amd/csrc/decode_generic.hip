@@ -1,0 +1,198 @@
+// Split-KV latent-attention decode for any shape and element type (fp32 or
+// bf16): the path for shapes the MFMA kernel does not cover (for example fp32
+// caches or latent widths other than 512).  It is a plain flash-decoding loop:
+// one workgroup = one query row (b, t, h) x one split, 256 rows of the cache
+// per step, fp32 throughout.
+//
+// Per step: each thread scores one cached row against the absorbed query held
+// in LDS (content and rotary terms in one dot product, "Attention, Part 2: MQA,
+// GQA and MLA", section "Why position needs its own key"), the block takes the
+// step maximum, rescales its running sum and accumulator, and accumulates the
+// weighted latents (the first d_c columns of each row, "How DeepSeek Rewrote
+// the Transformer", section "Absorbed projections", point 3).
+#include "common.h"
+#include "launch.h"
+
+namespace mla {
+namespace {
+
+constexpr int NT = 256;
+constexpr int MAX_DC_PER_THREAD = 8;  // d_c <= 2048
+
+__device__ __forceinline__ float block_max(float v, float* red) {
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+  const int w = threadIdx.x >> 6;
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) red[w] = v;
+  __syncthreads();
+  float r = red[0];
+  for (int i = 1; i < NT / 64; ++i) r = fmaxf(r, red[i]);
+  return r;
+}
+
+__device__ __forceinline__ float block_sum(float v, float* red) {
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+  const int w = threadIdx.x >> 6;
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) red[w] = v;
+  __syncthreads();
+  float r = 0.0f;
+  for (int i = 0; i < NT / 64; ++i) r += red[i];
+  return r;
+}
+
+template <typename E>
+__global__ __launch_bounds__(NT) void decode_generic_kernel(const DecodeParams p) {
+  extern __shared__ float smem[];
+  const int W = p.d_c + p.d_r;
+  float* sq = smem;          // [W] query
+  float* sp = smem + W;      // [NT] probabilities of the current step
+  float* red = sp + NT;      // [NT / 64]
+
+  const int tid = threadIdx.x;
+  const int TH = p.T * p.H;
+  const int row = blockIdx.x;  // (b, t, h) flattened
+  const int s = blockIdx.y;
+  const int b = row / TH;
+  const int rr = row - b * TH;
+  const int t = rr / p.H;
+  const int bs = p.block_size;
+  const int n_valid = visible_rows(p.seq_lens[b], p.T, t, p.causal, p.cap);
+  const int pages = (n_valid + bs - 1) / bs;
+  const int p0 = s * p.chunk_pages;
+  const int p1 = min(p0 + p.chunk_pages, pages);
+  const bool direct = (p.num_splits == 1);
+  float* dst = direct ? p.o_lat + (size_t)row * p.d_c
+                      : p.part_o + (((size_t)b * p.num_splits + s) * TH + rr) * p.d_c;
+
+  if (p0 >= p1) {
+    if (direct) {
+      for (int d = tid; d < p.d_c; d += NT) dst[d] = 0.0f;
+      if (tid == 0 && p.lse != nullptr) p.lse[row] = -INFINITY;
+    }
+    return;
+  }
+  const int j0 = p0 * bs;
+  const int j1 = min(p1 * bs, n_valid);
+
+  const E* q = static_cast<const E*>(p.q_abs) + (size_t)row * W;
+  for (int k = tid; k < W; k += NT) sq[k] = Elem<E>::load(q, k);
+  __syncthreads();
+
+  const E* pool = static_cast<const E*>(p.pool);
+  const int32_t* table = p.block_table + (size_t)b * p.max_blocks;
+  auto row_ptr = [&](int j) {
+    const int blk = clamp_block(table[j / bs], p.num_blocks);
+    return pool + ((size_t)blk * bs + (j % bs)) * W;
+  };
+
+  float acc[MAX_DC_PER_THREAD];
+#pragma unroll
+  for (int i = 0; i < MAX_DC_PER_THREAD; ++i) acc[i] = 0.0f;
+  float m_run = -INFINITY, l_run = 0.0f;
+
+  for (int jb = j0; jb < j1; jb += NT) {
+    const int j = jb + tid;
+    float sc = -INFINITY;
+    if (j < j1) {
+      const E* r = row_ptr(j);
+      float dot = 0.0f;
+      for (int k = 0; k < W; ++k) dot += sq[k] * Elem<E>::load(r, k);
+      sc = dot * p.scale_log2;
+    }
+    const float m_new = fmaxf(m_run, block_max(sc, red));
+    const float alpha = exp2f(m_run - m_new);  // 0 on the first step
+    const float e = (j < j1) ? exp2f(sc - m_new) : 0.0f;
+    sp[tid] = e;
+    l_run = l_run * alpha + block_sum(e, red);  // block_sum synchronises sp too
+    m_run = m_new;
+    const int n = min(NT, j1 - jb);
+#pragma unroll
+    for (int i = 0; i < MAX_DC_PER_THREAD; ++i) {
+      const int d = tid + i * NT;
+      if (d < p.d_c) {
+        float a = acc[i] * alpha;
+        for (int jj = 0; jj < n; ++jj) a += sp[jj] * Elem<E>::load(row_ptr(jb + jj), d);
+        acc[i] = a;
+      }
+    }
+    __syncthreads();
+  }
+
+  const float inv = 1.0f / l_run;
+#pragma unroll
+  for (int i = 0; i < MAX_DC_PER_THREAD; ++i) {
+    const int d = tid + i * NT;
+    if (d < p.d_c) dst[d] = acc[i] * inv;
+  }
+  if (tid == 0) {
+    const float v = (m_run + log2f(l_run)) * kLn2;
+    if (direct) {
+      if (p.lse != nullptr) p.lse[row] = v;
+    } else {
+      p.part_lse[((size_t)b * p.num_splits + s) * TH + rr] = v;
+    }
+  }
+}
+
+// Log-sum-exp merge of the splits of one query row: with M = max_s lse_s and
+// w_s = exp(lse_s - M), o = sum_s w_s o_s / sum_s w_s, lse = M + log sum_s w_s.
+// Only splits that hold rows of this query are read (the same page arithmetic
+// as the split kernels), in split order, so the result is deterministic.
+__global__ __launch_bounds__(128) void combine_kernel(const DecodeParams p) {
+  const int TH = p.T * p.H;
+  const int row = blockIdx.x;
+  const int b = row / TH;
+  const int rr = row - b * TH;
+  const int t = rr / p.H;
+  const int n_valid = visible_rows(p.seq_lens[b], p.T, t, p.causal, p.cap);
+  const int pages = (n_valid + p.block_size - 1) / p.block_size;
+  const int ns = min(p.num_splits, (pages + p.chunk_pages - 1) / p.chunk_pages);
+  float* out = p.o_lat + (size_t)row * p.d_c;
+  const size_t sstride = (size_t)TH;
+  const float* lse_b = p.part_lse + (size_t)b * p.num_splits * TH + rr;
+  const float* po_b = p.part_o + ((size_t)b * p.num_splits * TH + rr) * p.d_c;
+
+  if (ns <= 0) {
+    for (int d = threadIdx.x; d < p.d_c; d += blockDim.x) out[d] = 0.0f;
+    if (threadIdx.x == 0 && p.lse != nullptr) p.lse[row] = -INFINITY;
+    return;
+  }
+  float M = -INFINITY;
+  for (int s = 0; s < ns; ++s) M = fmaxf(M, lse_b[s * sstride]);
+  float den = 0.0f;
+  for (int s = 0; s < ns; ++s) den += exp2f((lse_b[s * sstride] - M) * kLog2e);
+  const float inv = 1.0f / den;
+  for (int d = threadIdx.x; d < p.d_c; d += blockDim.x) {
+    float a = 0.0f;
+    for (int s = 0; s < ns; ++s) {
+      const float w = exp2f((lse_b[s * sstride] - M) * kLog2e);
+      a += w * po_b[s * sstride * p.d_c + d];
+    }
+    out[d] = a * inv;
+  }
+  if (threadIdx.x == 0 && p.lse != nullptr) p.lse[row] = M + logf(den);
+}
+
+}  // namespace
+
+hipError_t launch_decode_generic(const DecodeParams& p, int dtype, hipStream_t stream) {
+  const long long rows = (long long)p.B * p.T * p.H;
+  if (rows <= 0) return hipSuccess;
+  const size_t shmem = (size_t)(p.d_c + p.d_r + NT + NT / 64) * sizeof(float);
+  const dim3 grid((unsigned)rows, (unsigned)p.num_splits);
+  if (dtype == 0)
+    hipLaunchKernelGGL(decode_generic_kernel<float>, grid, dim3(NT), shmem, stream, p);
+  else
+    hipLaunchKernelGGL(decode_generic_kernel<uint16_t>, grid, dim3(NT), shmem, stream, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_combine(const DecodeParams& p, hipStream_t stream) {
+  const long long rows = (long long)p.B * p.T * p.H;
+  if (rows <= 0) return hipSuccess;
+  hipLaunchKernelGGL(combine_kernel, dim3((unsigned)rows), dim3(128), 0, stream, p);
+  return hipGetLastError();
+}
+
+}  // namespace mla

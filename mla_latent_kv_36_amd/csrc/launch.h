@@ -1,0 +1,52 @@
+// Internal launch interface between the C ABI (abi.hip) and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace mla {
+
+// Everything one decode launch needs; built and checked on the host.
+struct DecodeParams {
+  const void* q_abs;          // [B, T, H, W] storage type
+  const void* pool;           // [num_blocks, block_size, W]
+  const int32_t* block_table; // [B, max_blocks]
+  const int32_t* seq_lens;    // [B], rows including the T new tokens
+  float* o_lat;               // [B, T, H, d_c]
+  float* lse;                 // [B, T, H] or nullptr
+  float* part_o;              // [B, S, T*H, d_c] when S > 1
+  float* part_lse;            // [B, S, T*H]      when S > 1
+  int B, T, H, d_c, d_r, block_size;
+  int num_blocks, max_blocks;
+  int cap;                    // host bound on rows attended per sequence
+  int causal;
+  int num_splits;             // S
+  int chunk_pages;            // pages per split
+  float scale_log2;           // softmax scale * log2(e)
+};
+
+// The MFMA kernel covers bf16, d_c = 512, d_rope = 64, 64-token pages and
+// T*H a multiple of 64.
+bool decode_mfma_supported(int dtype, int d_c, int d_r, int block_size, int T, int H);
+hipError_t launch_decode_mfma(const DecodeParams& p, hipStream_t stream);
+hipError_t launch_decode_generic(const DecodeParams& p, int dtype, hipStream_t stream);
+hipError_t launch_combine(const DecodeParams& p, hipStream_t stream);
+
+hipError_t launch_absorb_q(int dtype, const void* q_nope, const void* q_rope,
+                           const void* w_uk, void* q_abs, int M, int H, int d_n, int d_c,
+                           int d_r, hipStream_t stream);
+hipError_t launch_out_proj(int dtype, const float* o_lat, const void* w_uv, void* out,
+                           int M, int H, int d_c, int d_v, hipStream_t stream);
+hipError_t launch_append(void* pool, int num_blocks, const int32_t* block_table,
+                         int max_blocks, const int32_t* seq_lens, const void* new_rows,
+                         int B, int T_new, int block_size, int row_bytes,
+                         hipStream_t stream);
+hipError_t launch_gather(const void* pool, int num_blocks, const int32_t* block_table,
+                         int max_blocks, const int32_t* seq_lens, int B, int cap,
+                         int block_size, int row_bytes, void* dense, hipStream_t stream);
+hipError_t launch_validate(const int32_t* block_table, int B, int max_blocks,
+                           const int32_t* seq_lens, int block_size, int num_blocks,
+                           int32_t* err_flag, hipStream_t stream);
+
+}  // namespace mla

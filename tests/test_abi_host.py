@@ -1,0 +1,160 @@
+"""The C ABI on the host: the library loads without a GPU, exports every call
+the header declares, and rejects bad arguments before launching anything.
+
+No test here reaches a kernel launch: every call either fails validation or
+has nothing to launch, so these run on a machine without a GPU.  Device
+pointers are stand-in addresses that are never dereferenced.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import mla_latent_kv_36_amd as mla
+from mla_latent_kv_36_amd import binding
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+OK, NULL, DIM, DTYPE, CAP, WS, HIP, ALIGN = range(8)
+FAKE = 0x10000          # aligned stand-in device address (never dereferenced)
+FAKE_MIS = 0x10008      # misaligned stand-in
+
+
+@pytest.fixture(scope="module")
+def lib():
+    from mla_latent_kv_36_amd import build
+    if not build.built():
+        build.build()
+    return mla.load()
+
+
+def v3_cfg(**kw):
+    d = dict(n_heads=128, d_c=512, d_rope=64, d_nope=128, d_v=128, block_size=64,
+             softmax_scale=0.0, dtype="bf16")
+    d.update(kw)
+    return mla.make_config(**d)
+
+
+def test_header_symbols_are_exported(lib):
+    text = open(os.path.join(ROOT, "include", "mla.h")).read()
+    names = set(re.findall(r"\b(mla_[a-z_0-9]+)\s*\(", text))
+    assert {"mla_absorb_q", "mla_cache_append", "mla_decode", "mla_out_proj"} <= names
+    for n in sorted(names):
+        assert hasattr(lib, n), f"{n} declared in include/mla.h but not exported"
+    # the binding wraps every declared call under the same name
+    for n in names:
+        assert hasattr(binding, n), f"binding lacks {n}"
+
+
+def test_status_strings(lib):
+    for code in range(8):
+        s = mla.mla_status_string(code)
+        assert s.startswith("MLA_")
+    assert "unknown" in mla.mla_status_string(99)
+    assert mla.mla_abi_version() == 1
+
+
+def _decode(lib, cfg, q=FAKE, pool=FAKE, nb=10, bt=FAKE, mb=4, sl=FAKE, cap=256, B=2, T=1,
+            causal=1, ns=0, tot=0, ws=None, wsb=0, o=FAKE, lse=None):
+    return lib.mla_decode(ctypes.byref(cfg) if cfg is not None else None, q, pool, nb, bt, mb,
+                          sl, cap, B, T, causal, ns, tot, ws, wsb, o, lse, None)
+
+
+def test_decode_validation(lib):
+    cfg = v3_cfg()
+    assert _decode(lib, None) == NULL
+    assert _decode(lib, v3_cfg(dtype=7)) == DTYPE
+    assert _decode(lib, v3_cfg(n_heads=0)) == DIM
+    assert _decode(lib, v3_cfg(block_size=0)) == DIM
+    assert _decode(lib, v3_cfg(softmax_scale=-1.0)) == DIM
+    assert _decode(lib, v3_cfg(softmax_scale=float("nan"))) == DIM
+    assert _decode(lib, cfg, T=0) == DIM
+    assert _decode(lib, cfg, causal=2) == DIM
+    assert _decode(lib, cfg, ns=-1) == DIM
+    assert _decode(lib, cfg, nb=0) == DIM
+    assert _decode(lib, cfg, cap=4 * 64 + 1) == CAP          # longer than the table holds
+    assert _decode(lib, cfg, q=None) == NULL
+    assert _decode(lib, cfg, o=None) == NULL
+    assert _decode(lib, cfg, sl=None) == NULL
+    assert _decode(lib, cfg, q=FAKE_MIS) == ALIGN
+    assert _decode(lib, cfg, lse=FAKE_MIS) == ALIGN
+    # a split plan needs a workspace; too small or missing is refused
+    need = mla.mla_decode_workspace_size(cfg, 2, 1, 256, 0, 4)
+    assert need > 0
+    assert _decode(lib, cfg, ns=4) == WS
+    assert _decode(lib, cfg, ns=4, ws=FAKE, wsb=need - 1) == WS
+    # nothing to do: no launch, success
+    assert _decode(lib, cfg, B=0) == OK
+
+
+def test_workspace_and_split_plan(lib):
+    cfg = v3_cfg()
+    # one split needs no workspace
+    assert mla.mla_decode_workspace_size(cfg, 16, 1, 4097, 0, 1) == 0
+    # S splits of B x T x H rows: d_c floats + one lse each, both rounded up to 256 B
+    for B, T, cap, S in [(16, 1, 4097, 8), (4, 1, 131073, 64), (32, 4, 8196, 3)]:
+        pages = -(-cap // 64)
+        chunk = -(-pages // S)
+        s_eff = -(-pages // chunk)
+        rows = B * s_eff * T * 128
+        r256 = lambda x: -(-x // 256) * 256
+        want = r256(rows * 512 * 4) + r256(rows * 4)
+        assert mla.mla_decode_workspace_size(cfg, B, T, cap, 0, S) == want
+    # the library's own choice is a valid split count and sized consistently
+    s = mla.mla_decode_num_splits(cfg, 16, 1, 4097, 0)
+    assert 1 <= s <= 65
+    assert mla.mla_decode_workspace_size(cfg, 16, 1, 4097, 0, 0) == \
+        mla.mla_decode_workspace_size(cfg, 16, 1, 4097, 0, s)
+    # more splits than pages collapse to one split per page
+    assert mla.mla_decode_workspace_size(cfg, 1, 1, 64, 0, 8) == 0
+    with pytest.raises(RuntimeError):
+        mla.mla_decode_workspace_size(v3_cfg(d_c=0), 1, 1, 64)
+
+
+def test_append_validation(lib):
+    cfg = v3_cfg()
+    f = lib.mla_cache_append
+    c = ctypes.byref(cfg)
+    assert f(c, FAKE, 10, FAKE, 4, FAKE, FAKE, 2, 1, 4 * 64 + 1, None) == CAP
+    assert f(c, None, 10, FAKE, 4, FAKE, FAKE, 2, 1, 10, None) == NULL
+    assert f(c, FAKE, 0, FAKE, 4, FAKE, FAKE, 2, 1, 10, None) == DIM
+    assert f(c, FAKE, 10, FAKE, 4, FAKE, FAKE_MIS, 2, 1, 10, None) == ALIGN
+    assert f(c, FAKE, 10, FAKE, 4, FAKE, FAKE, 2, 0, 10, None) == OK     # no new rows
+    assert f(c, FAKE, 10, FAKE, 4, FAKE, FAKE, -1, 1, 10, None) == DIM
+
+
+def test_absorb_and_out_proj_validation(lib):
+    cfg = v3_cfg()
+    c = ctypes.byref(cfg)
+    assert lib.mla_absorb_q(c, None, FAKE, FAKE, FAKE, 4, None) == NULL
+    assert lib.mla_absorb_q(c, FAKE, None, FAKE, FAKE, 4, None) == NULL   # d_rope > 0
+    assert lib.mla_absorb_q(ctypes.byref(v3_cfg(d_nope=0)), FAKE, FAKE, FAKE, FAKE, 4,
+                            None) == DIM
+    assert lib.mla_absorb_q(c, FAKE, FAKE, FAKE_MIS, FAKE, 4, None) == ALIGN
+    assert lib.mla_absorb_q(c, FAKE, FAKE, FAKE, FAKE, 0, None) == OK
+    assert lib.mla_absorb_q(c, FAKE, FAKE, FAKE, FAKE, -1, None) == DIM
+    assert lib.mla_out_proj(c, None, FAKE, FAKE, 4, None) == NULL
+    assert lib.mla_out_proj(ctypes.byref(v3_cfg(d_v=0)), FAKE, FAKE, FAKE, 4, None) == DIM
+    assert lib.mla_out_proj(c, FAKE, FAKE, FAKE_MIS, 4, None) == ALIGN
+    assert lib.mla_out_proj(c, FAKE, FAKE, FAKE, 0, None) == OK
+
+
+def test_debug_helpers_validation(lib):
+    cfg = v3_cfg()
+    c = ctypes.byref(cfg)
+    assert lib.mla_gather_rows(c, FAKE, 10, FAKE, 4, FAKE, 2, 4 * 64 + 1, FAKE, None) == CAP
+    assert lib.mla_gather_rows(c, FAKE, 10, FAKE, 4, FAKE, 2, 10, None, None) == NULL
+    assert lib.mla_gather_rows(c, FAKE, 10, FAKE, 4, FAKE, 0, 10, FAKE, None) == OK
+    assert lib.mla_validate_block_table(FAKE, 2, 4, FAKE, 64, 10, None, None) == NULL
+    assert lib.mla_validate_block_table(FAKE, 2, 4, FAKE, 64, 10, FAKE + 2, None) == ALIGN
+    assert lib.mla_validate_block_table(FAKE, 2, 0, FAKE, 64, 10, FAKE, None) == DIM
+
+
+def test_binding_rejects_wrong_tensor_types(lib):
+    import torch
+    cfg = v3_cfg()
+    q = torch.zeros(1, 1, 128, 576, dtype=torch.float32)   # wrong dtype for a bf16 config
+    with pytest.raises(TypeError):
+        mla.mla_decode(cfg, q, q, torch.zeros(1, 1, dtype=torch.int32),
+                       torch.zeros(1, dtype=torch.int32), 1, q)

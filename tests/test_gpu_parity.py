@@ -1,0 +1,265 @@
+"""GPU parity: the HIP path through the C ABI against the fp64 oracle on the
+same seeded inputs.
+
+* paged append and page-table addressing: bit-exact;
+* decode (o_lat, lse), absorption and the output projection: max |error| <=
+  2e-2 * max |reference| for bf16 workloads, 1e-4 * max |reference| for fp32;
+* invariances: split count (within tolerance), page permutation and reruns
+  (bit-exact);
+* edge cases: one cached row, empty sequences, queries that see nothing,
+  ragged last pages, stale NaN in unused slots.
+
+Reduced workloads keep the real head count and widths (so the MFMA kernel
+runs) and shrink batch and length to sizes the oracle finishes in seconds
+while still spanning several pages and a ragged tail.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from mla_latent_kv_36_amd import binding as mla
+from workloads import LONG, TINY, V2_MULTI, V3, VARLEN, make_inputs
+from workloads.device import to_dev, torch_dtype, upload
+
+from gpu_util import (cfg_of, dev_bits, make_step, max_err_ratio, note, oracle_decode,
+                      oracle_pool_after, pool_bits, run_decode, tol_of)
+
+pytestmark = pytest.mark.gpu
+BF16 = 2e-2
+
+REDUCED = {
+    "tiny_f32": TINY,
+    "v3": V3.scaled(B=3, N=700),
+    "varlen": VARLEN.scaled(B=5, N=900),
+    "long": LONG.scaled(B=2, N=1500),
+    "v2_multi": V2_MULTI.scaled(B=3, N=300),
+    "bf16_h16": V3.scaled(B=2, H=16, N=200),        # bf16 through the generic kernel
+}
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    mla.load()
+
+
+# ------------------------------------------------------------------ paged cache
+
+@pytest.mark.parametrize("name", list(REDUCED))
+def test_append_bit_exact(name):
+    w = REDUCED[name]
+    bt = make_inputs(w)
+    note(f"append {name}")
+    dev = upload(bt)
+    step = make_step(bt, dev)
+    step.append()
+    torch.cuda.synchronize()
+    want = pool_bits(oracle_pool_after(bt), w.dtype)
+    assert np.array_equal(dev_bits(dev["pool"]), want)
+
+
+@pytest.mark.parametrize("name", ["tiny_f32", "varlen", "v2_multi"])
+def test_gather_bit_exact(name):
+    w = REDUCED[name]
+    bt = make_inputs(w)
+    pool_after = oracle_pool_after(bt)
+    dt = torch_dtype(bt)
+    cap = bt.max_seq_len
+    note(f"gather {name}")
+    dense = torch.zeros(w.B, cap, w.W, dtype=dt, device="cuda")
+    mla.mla_gather_rows(cfg_of(w), to_dev(pool_after, dt, "cuda"),
+                        torch.from_numpy(bt.block_table).cuda(),
+                        torch.from_numpy(bt.seq_lens).cuda(), cap, dense)
+    torch.cuda.synchronize()
+    got = dev_bits(dense)
+    for b in range(w.B):
+        n = int(bt.seq_lens[b])
+        rows = oracle.gather_rows_ref(pool_after, bt.block_table, b, n, w.block_size)
+        assert np.array_equal(got[b, :n], pool_bits(rows, w.dtype))
+        assert np.all(got[b, n:] == 0)       # rows past the length are left untouched
+
+
+def test_validate_block_table():
+    w = REDUCED["varlen"]
+    bt = make_inputs(w, with_rows=False)
+    tbl = torch.from_numpy(bt.block_table).cuda()
+    sl = torch.from_numpy(bt.seq_lens).cuda()
+    flag = torch.full((4,), 7, dtype=torch.int32, device="cuda")
+    note("validate_block_table")
+    mla.mla_validate_block_table(tbl, sl, w.block_size, bt.num_blocks, flag)
+    torch.cuda.synchronize()
+    assert int(flag[0]) == 0
+    bad = bt.block_table.copy()
+    bad[1, 0] = bt.num_blocks + 5
+    mla.mla_validate_block_table(torch.from_numpy(bad).cuda(), sl, w.block_size, bt.num_blocks,
+                                 flag)
+    torch.cuda.synchronize()
+    assert int(flag[0]) == 1
+    long_sl = bt.seq_lens.copy()
+    long_sl[0] = bt.max_blocks * w.block_size + 1
+    mla.mla_validate_block_table(tbl, torch.from_numpy(long_sl).cuda(), w.block_size,
+                                 bt.num_blocks, flag)
+    torch.cuda.synchronize()
+    assert int(flag[0]) & 2
+
+
+# ------------------------------------------------------------------ decode
+
+@pytest.mark.parametrize("splits", [0, 1, 3])
+@pytest.mark.parametrize("name", list(REDUCED))
+def test_decode_parity(name, splits):
+    w = REDUCED[name]
+    bt = make_inputs(w)
+    pool_after = oracle_pool_after(bt)
+    note(f"decode {name} splits={splits}")
+    o, lse = run_decode(bt, pool_after, bt.q_abs, bt.seq_lens, num_splits=splits)
+    o_ref, lse_ref = oracle_decode(bt, pool_after, bt.q_abs)
+    assert max_err_ratio(o, o_ref) <= tol_of(w)
+    assert np.max(np.abs(lse - lse_ref)) <= (1e-3 if w.dtype == "bf16" else 1e-5)
+
+
+@pytest.mark.parametrize("name", list(REDUCED))
+def test_step_parity(name):
+    """absorb -> append -> decode -> out_proj against the oracle's whole step."""
+    w = REDUCED[name]
+    bt = make_inputs(w)
+    note(f"step {name}")
+    dev = upload(bt)
+    step = make_step(bt, dev)
+    step.run()
+    torch.cuda.synchronize()
+    pool_r, q_abs_r, o_lat_r, lse_r, out_r = oracle.step_ref(
+        bt.q_nope, bt.q_rope, bt.w_uk, bt.w_uv, bt.pool, bt.block_table, bt.lengths,
+        bt.new_rows, w.d_c, w.scale, w.causal, w.block_size)
+    tol = tol_of(w)
+    assert max_err_ratio(step.q_abs.float().cpu().numpy(), q_abs_r) <= tol
+    assert max_err_ratio(step.o_lat.cpu().numpy(), o_lat_r) <= tol
+    assert max_err_ratio(step.out.float().cpu().numpy().reshape(out_r.shape), out_r) <= tol
+    assert np.max(np.abs(step.lse.cpu().numpy() - lse_r)) <= (5e-2 if w.dtype == "bf16"
+                                                              else 1e-4)
+    assert np.array_equal(dev_bits(dev["pool"]), pool_bits(pool_r, w.dtype))
+
+
+# ------------------------------------------------------------------ invariances
+
+def test_split_count_invariance():
+    w = REDUCED["long"]
+    bt = make_inputs(w)
+    pool_after = oracle_pool_after(bt)
+    o_ref, _ = oracle_decode(bt, pool_after, bt.q_abs)
+    outs = []
+    for s in (1, 2, 5, 24):
+        note(f"split invariance splits={s}")
+        o, lse = run_decode(bt, pool_after, bt.q_abs, bt.seq_lens, num_splits=s)
+        assert max_err_ratio(o, o_ref) <= tol_of(w)
+        outs.append((o, lse))
+    for o, lse in outs[1:]:
+        assert max_err_ratio(o, outs[0][0]) <= 1e-2
+        assert np.max(np.abs(lse - outs[0][1])) <= 1e-4
+
+
+def test_page_permutation_and_rerun_bit_exact():
+    w = V3.scaled(B=3, N=600)
+    a = make_inputs(w)
+    b = make_inputs(w.scaled(table="permuted"))
+    note("permutation invariance")
+    oa, la = run_decode(a, oracle_pool_after(a), a.q_abs, a.seq_lens, num_splits=2)
+    ob, lb = run_decode(b, oracle_pool_after(b), b.q_abs, b.seq_lens, num_splits=2)
+    oa2, la2 = run_decode(a, oracle_pool_after(a), a.q_abs, a.seq_lens, num_splits=2)
+    assert np.array_equal(oa, ob) and np.array_equal(la, lb)
+    assert np.array_equal(oa, oa2) and np.array_equal(la, la2)
+
+
+# ------------------------------------------------------------------ edge cases
+
+@pytest.mark.parametrize("name", ["v3", "tiny_f32"])
+def test_single_row_is_that_latent_exactly(name):
+    w = REDUCED[name].scaled(B=2, N=0, var_len=False, T=1)
+    bt = make_inputs(w)
+    pool_after = oracle_pool_after(bt)
+    note(f"single row {name}")
+    o, lse = run_decode(bt, pool_after, bt.q_abs, bt.seq_lens, num_splits=1)
+    for b in range(w.B):
+        c0 = bt.new_rows[b, 0, : w.d_c]
+        assert np.array_equal(o[b, 0], np.broadcast_to(c0, (w.H, w.d_c)).astype(np.float32))
+    _, lse_ref = oracle_decode(bt, pool_after, bt.q_abs)
+    assert np.max(np.abs(lse - lse_ref)) <= 1e-4
+
+
+@pytest.mark.parametrize("name", ["v3", "v2_multi", "tiny_f32"])
+@pytest.mark.parametrize("splits", [1, 4])
+def test_empty_and_short_sequences(name, splits):
+    """seq_len 0 gives o = 0 and lse = -inf; with T new tokens and fewer rows
+    than T, the first queries see nothing and the others see a prefix."""
+    w = REDUCED[name]
+    bt = make_inputs(w)
+    pool_after = oracle_pool_after(bt)
+    sl = bt.seq_lens.copy()
+    sl[0] = 0
+    if w.B > 1:
+        sl[1] = min(2, int(sl[1]))
+    note(f"empty/short {name} splits={splits}")
+    o, lse = run_decode(bt, pool_after, bt.q_abs, sl, num_splits=splits)
+    bt.seq_lens = sl
+    o_ref, lse_ref = oracle_decode(bt, pool_after, bt.q_abs)
+    assert np.all(o[0] == 0.0) and np.all(np.isneginf(lse[0]))
+    assert max_err_ratio(o, o_ref) <= tol_of(w)
+    fin = np.isfinite(lse_ref)
+    assert np.array_equal(np.isfinite(lse), fin)
+    assert np.max(np.abs(lse[fin] - lse_ref[fin])) <= 1e-3
+
+
+def test_ragged_lengths_every_page_offset():
+    """Lengths that end on every slot position of a page, including full pages."""
+    w = V3.scaled(B=8, N=200, var_len=False)
+    bt = make_inputs(w)
+    pool_after = oracle_pool_after(bt)
+    sl = np.array([1, 63, 64, 65, 127, 128, 129, 201], dtype=np.int32)
+    bt.seq_lens = sl
+    note("ragged lengths")
+    for splits in (1, 2):
+        o, lse = run_decode(bt, pool_after, bt.q_abs, sl, num_splits=splits)
+        o_ref, lse_ref = oracle_decode(bt, pool_after, bt.q_abs)
+        assert max_err_ratio(o, o_ref) <= BF16
+        assert np.max(np.abs(lse - lse_ref)) <= 1e-3
+
+
+def test_non_causal_multi_token():
+    w = REDUCED["v2_multi"].scaled(causal=False)
+    bt = make_inputs(w)
+    pool_after = oracle_pool_after(bt)
+    note("non-causal T=4")
+    o, lse = run_decode(bt, pool_after, bt.q_abs, bt.seq_lens, num_splits=2, causal=False)
+    o_ref, lse_ref = oracle_decode(bt, pool_after, bt.q_abs)
+    assert max_err_ratio(o, o_ref) <= BF16
+    assert np.max(np.abs(lse - lse_ref)) <= 1e-3
+
+
+def test_graph_replay_matches_eager():
+    """The whole step captured in a HIP graph: several replays, with eager work
+    and synchronisation between them, each equal bit for bit to the eager run."""
+    w = REDUCED["v3"]
+    bt = make_inputs(w)
+    dev = upload(bt)
+    step = make_step(bt, dev, num_splits=3)
+    note("graph replay")
+    step.run()
+    torch.cuda.synchronize()
+    ref = [step.q_abs.clone(), step.o_lat.clone(), step.lse.clone(), step.out.clone(),
+           dev["pool"].clone()]
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step.run()
+    for rep in range(3):
+        for t in (step.q_abs, step.o_lat, step.lse, step.out):
+            t.fill_(float("nan") if t.is_floating_point() else 0)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        got = [step.q_abs, step.o_lat, step.lse, step.out, dev["pool"]]
+        for a, b in zip(got, ref):
+            assert torch.equal(a.view(torch.int16) if a.dtype == torch.bfloat16 else a,
+                               b.view(torch.int16) if b.dtype == torch.bfloat16 else b), rep
+        _ = (torch.randn(1000, device="cuda") * 2).sum().item()   # eager work between replays
