@@ -63,13 +63,17 @@ def cpu_baseline(w, budget_s: float) -> dict:
                         bt.lengths, bt.new_rows, w.d_c, w.scale, w.causal, w.block_size)
         return time.perf_counter() - t0
 
+    # one sequence first, to size the sample: whole batches of the workload's
+    # shape, repeated until about budget_s of CPU work
     t1 = run(1)
     k = int(max(1, min(w.B, budget_s / max(t1, 1e-3))))
-    dt = run(k) if k > 1 else t1
-    return {"value": k * w.T / dt, "unit": "tokens/s", "cores": _blas_threads(),
+    reps = int(max(1, round(budget_s / max(t1 * k, 1e-3))))
+    dt = sum(run(k) for _ in range(reps))
+    return {"value": reps * k * w.T / dt, "unit": "tokens/s", "cores": _blas_threads(),
             "kind": "oracle",
-            "sample": f"fp64 numpy oracle, whole step (absorb, append, decode, out-proj) on "
-                      f"{k} of {w.B} sequences of the same shape, {dt:.2f} s",
+            "sample": f"fp64 numpy oracle, whole step (absorb, append, decode, out-proj), "
+                      f"{reps} x {k} sequences of the workload's shape (fresh seeded draws), "
+                      f"{dt:.1f} s",
             "host_cpus": os.cpu_count(), "cpu_model": _cpu_model()}
 
 

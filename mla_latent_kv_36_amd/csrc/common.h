@@ -42,6 +42,26 @@ template <> struct Elem<uint16_t> {
   }
 };
 
+// Reductions across lane l and lane l ^ 32 (or l ^ 16) on the VALU with the
+// gfx950 lane-swap instructions: each lane gets back {x[l], x[l ^ 32]} (resp.
+// {x[l], x[l ^ 16]}), so a symmetric operation of the pair is the reduction.
+__device__ __forceinline__ float xor32_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float xor32_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float xor16_max(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float xor16_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 // Rows a query of new token t may attend to, capped by the host-side bound.
 __device__ __forceinline__ int visible_rows(int seq_len, int T, int t, int causal,
                                             int cap) {

@@ -139,39 +139,76 @@ __global__ __launch_bounds__(NT) void decode_generic_kernel(const DecodeParams p
 // w_s = exp(lse_s - M), o = sum_s w_s o_s / sum_s w_s, lse = M + log sum_s w_s.
 // Only splits that hold rows of this query are read (the same page arithmetic
 // as the split kernels), in split order, so the result is deterministic.
-__global__ __launch_bounds__(128) void combine_kernel(const DecodeParams p) {
+// One wave per query row; each lane owns 4 consecutive latent columns per
+// 256-column block and streams the splits' partials with 128-bit loads.
+constexpr int CMB_ROWS = 4;  // query rows (waves) per workgroup
+
+__global__ __launch_bounds__(64 * CMB_ROWS) void combine_kernel(const DecodeParams p) {
   const int TH = p.T * p.H;
-  const int row = blockIdx.x;
-  const int b = row / TH;
-  const int rr = row - b * TH;
+  const long long nrows = (long long)p.B * TH;
+  const long long row = (long long)blockIdx.x * CMB_ROWS + (threadIdx.x >> 6);
+  if (row >= nrows) return;
+  const int lane = threadIdx.x & 63;
+  const int b = (int)(row / TH);
+  const int rr = (int)(row - (long long)b * TH);
   const int t = rr / p.H;
   const int n_valid = visible_rows(p.seq_lens[b], p.T, t, p.causal, p.cap);
   const int pages = (n_valid + p.block_size - 1) / p.block_size;
   const int ns = min(p.num_splits, (pages + p.chunk_pages - 1) / p.chunk_pages);
   float* out = p.o_lat + (size_t)row * p.d_c;
-  const size_t sstride = (size_t)TH;
   const float* lse_b = p.part_lse + (size_t)b * p.num_splits * TH + rr;
   const float* po_b = p.part_o + ((size_t)b * p.num_splits * TH + rr) * p.d_c;
+  const size_t sstride = (size_t)TH * p.d_c;  // floats between splits of one row
 
   if (ns <= 0) {
-    for (int d = threadIdx.x; d < p.d_c; d += blockDim.x) out[d] = 0.0f;
-    if (threadIdx.x == 0 && p.lse != nullptr) p.lse[row] = -INFINITY;
+    for (int d = lane; d < p.d_c; d += 64) out[d] = 0.0f;
+    if (lane == 0 && p.lse != nullptr) p.lse[row] = -INFINITY;
     return;
   }
   float M = -INFINITY;
-  for (int s = 0; s < ns; ++s) M = fmaxf(M, lse_b[s * sstride]);
+  for (int s = 0; s < ns; ++s) M = fmaxf(M, lse_b[(size_t)s * TH]);
   float den = 0.0f;
-  for (int s = 0; s < ns; ++s) den += exp2f((lse_b[s * sstride] - M) * kLog2e);
+  for (int s = 0; s < ns; ++s) den += exp2f((lse_b[(size_t)s * TH] - M) * kLog2e);
   const float inv = 1.0f / den;
-  for (int d = threadIdx.x; d < p.d_c; d += blockDim.x) {
-    float a = 0.0f;
-    for (int s = 0; s < ns; ++s) {
-      const float w = exp2f((lse_b[s * sstride] - M) * kLog2e);
-      a += w * po_b[s * sstride * p.d_c + d];
+  if ((p.d_c & 3) == 0) {
+    for (int d = 4 * lane; d < p.d_c; d += 256) {
+      float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
+      int s = 0;
+      for (; s + 4 <= ns; s += 4) {
+        float4 v[4];
+        float w[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          v[k] = *reinterpret_cast<const float4*>(po_b + (size_t)(s + k) * sstride + d);
+          w[k] = exp2f((lse_b[(size_t)(s + k) * TH] - M) * kLog2e);
+        }
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          a.x += w[k] * v[k].x;
+          a.y += w[k] * v[k].y;
+          a.z += w[k] * v[k].z;
+          a.w += w[k] * v[k].w;
+        }
+      }
+      for (; s < ns; ++s) {
+        const float4 v = *reinterpret_cast<const float4*>(po_b + (size_t)s * sstride + d);
+        const float w = exp2f((lse_b[(size_t)s * TH] - M) * kLog2e);
+        a.x += w * v.x;
+        a.y += w * v.y;
+        a.z += w * v.z;
+        a.w += w * v.w;
+      }
+      *reinterpret_cast<float4*>(out + d) = make_float4(a.x * inv, a.y * inv, a.z * inv, a.w * inv);
     }
-    out[d] = a * inv;
+  } else {
+    for (int d = lane; d < p.d_c; d += 64) {
+      float a = 0.0f;
+      for (int s = 0; s < ns; ++s)
+        a += exp2f((lse_b[(size_t)s * TH] - M) * kLog2e) * po_b[(size_t)s * sstride + d];
+      out[d] = a * inv;
+    }
   }
-  if (threadIdx.x == 0 && p.lse != nullptr) p.lse[row] = M + logf(den);
+  if (lane == 0 && p.lse != nullptr) p.lse[row] = M + logf(den);
 }
 
 }  // namespace
@@ -191,7 +228,8 @@ hipError_t launch_decode_generic(const DecodeParams& p, int dtype, hipStream_t s
 hipError_t launch_combine(const DecodeParams& p, hipStream_t stream) {
   const long long rows = (long long)p.B * p.T * p.H;
   if (rows <= 0) return hipSuccess;
-  hipLaunchKernelGGL(combine_kernel, dim3((unsigned)rows), dim3(128), 0, stream, p);
+  const long long blocks = (rows + CMB_ROWS - 1) / CMB_ROWS;
+  hipLaunchKernelGGL(combine_kernel, dim3((unsigned)blocks), dim3(64 * CMB_ROWS), 0, stream, p);
   return hipGetLastError();
 }
 

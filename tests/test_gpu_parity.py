@@ -208,7 +208,8 @@ def test_empty_and_short_sequences(name, splits):
     assert max_err_ratio(o, o_ref) <= tol_of(w)
     fin = np.isfinite(lse_ref)
     assert np.array_equal(np.isfinite(lse), fin)
-    assert np.max(np.abs(lse[fin] - lse_ref[fin])) <= 1e-3
+    if fin.any():
+        assert np.max(np.abs(lse[fin] - lse_ref[fin])) <= 1e-3
 
 
 def test_ragged_lengths_every_page_offset():
