@@ -52,12 +52,13 @@ int heuristic_splits(const mla_config* c, int B, int T, int pages_max, int64_t t
   const int64_t pages_total =
       total_tokens > 0 ? (total_tokens + bs - 1) / bs + B : (int64_t)B * pages_max;
   if (use_mfma(c, T)) {
-    // Units of work are (row group, page).  Aim for about two workgroups per
-    // compute unit, but keep at least 4 pages per workgroup so the partial
-    // outputs (128 KiB per workgroup) stay well below the cache bytes read.
+    // Units of work are (row group, page).  The kernel's LDS ring fits one
+    // workgroup per compute unit, so aim for one wave of workgroups over the
+    // chip, but keep at least 4 pages per workgroup so the partial outputs
+    // (128 KiB per workgroup) stay well below the cache bytes read.
     const int64_t groups = (int64_t)T * c->n_heads / 64;
     const int64_t work = pages_total * groups;
-    int64_t chunk = (work + 2 * kCUs - 1) / (2 * kCUs);
+    int64_t chunk = (work + kCUs - 1) / kCUs;
     if (chunk < 4) chunk = 4;
     return (int)((pages_max + chunk - 1) / chunk);
   }

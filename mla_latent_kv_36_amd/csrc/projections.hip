@@ -8,8 +8,17 @@
 //   applied once per head after the latent-space sum (same section).
 //
 // Both are small batched GEMMs whose weights dominate the bytes at decode
-// batch sizes; each workgroup streams one head's weight slice once and reuses
-// it across a block of query rows held in LDS.  fp32 accumulation.
+// batch sizes (M = sequences x new tokens is small, each head's weight is d_n x
+// d_c or d_v x d_c).  For bf16 they run on MFMA (v_mfma_f32_16x16x32_bf16):
+// a workgroup reads its head's weight slice from HBM once, keeps it in
+// registers, and streams the query rows through it 16 at a time.  Both
+// compute the transposed tile (weight as the A operand, rows as B), so that a
+// lane ends up holding 4 consecutive output columns of one row: one 8-byte
+// store.  fp32 accumulation throughout; the fp32 kernels below cover fp32
+// caches and shapes outside the MFMA kernels' constraints.
+//
+// MFMA 16x16x32 operand layout (lane l): A row l & 15, k 8(l >> 4) .. +7;
+// B column l & 15, the same k; D column l & 15, rows 4(l >> 4) .. +3.
 #include "common.h"
 #include "launch.h"
 
@@ -94,12 +103,224 @@ __global__ __launch_bounds__(256) void out_proj_kernel(const float* __restrict__
   if (m < M && v < d_v) Elem<E>::store(out, ((size_t)m * H + h) * d_v + v, acc);
 }
 
+// ------------------------------------------------------------------ MFMA ---
+
+typedef __attribute__((__vector_size__(4 * sizeof(short)))) short s16x4;
+typedef __attribute__((__vector_size__(4 * sizeof(uint16_t)))) uint16_t u16x4;
+
+__device__ __forceinline__ f32x4 mfma16(const bf16x8& a, const bf16x8& b, const f32x4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// Transposing LDS read: in each 16-lane group, lane 4k + q addresses element
+// [r0 + k][c0 + 4q] of a row-major bf16 tile; lane i of the group receives
+// [r0 .. r0 + 3][c0 + i].
+__device__ __forceinline__ s16x4 lds_tr16(const uint8_t* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) s16x4*)(p));
+}
+
+__device__ __forceinline__ bf16x8 load_bf16x8(const uint16_t* p) {
+  return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(p));
+}
+
+__device__ __forceinline__ void store_bf16x4(uint16_t* p, const f32x4& v) {
+  u16x4 h;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) h[i] = f32_to_bf16(v[i]);
+  *reinterpret_cast<u16x4*>(p) = h;
+}
+
+constexpr int PJ_NT = 256;        // 4 waves
+constexpr int PJ_MW = 64;         // query rows per workgroup (4 tiles of 16)
+constexpr int AB_CT = 128;        // latent columns per absorb workgroup (32 per wave)
+constexpr int AB_KS = 6;          // at most 6 k-steps of 32: d_nope <= 192 (55 KiB staged)
+constexpr int AB_LD = 2 * AB_CT + 32;  // LDS row stride (bytes) of the staged weight
+constexpr int OP_VT = 64;         // value columns per out-proj workgroup (16 per wave)
+constexpr int OP_KS = 16;         // at most 16 k-steps of 32: d_c <= 512
+
+// absorb_q on MFMA.  Workgroup (h, cb, mz): latent columns cb*128 .. +127 of
+// head h for query rows mz*64 .. +63.  The weight slice W^UK[h][:, cols] is
+// staged in LDS (rows past d_nope zeroed, so the contraction is padded to a
+// multiple of 32), then each wave takes its 32 columns x all d_nope into
+// registers with transposing reads: the A operand, rows = latent columns.
+__global__ __launch_bounds__(PJ_NT) void absorb_q_mfma_kernel(
+    const uint16_t* __restrict__ q_nope, const uint16_t* __restrict__ q_rope,
+    const uint16_t* __restrict__ w_uk, uint16_t* __restrict__ q_abs, int M, int H, int d_n,
+    int d_c, int d_r) {
+  extern __shared__ __align__(16) uint8_t wl[];  // [KP][AB_LD]
+  const int h = blockIdx.x, cb = blockIdx.y;
+  const int mbeg = blockIdx.z * PJ_MW, mend = min(M, mbeg + PJ_MW);
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int i16 = lane & 15, g = lane >> 4;
+  const int nks = (d_n + 31) >> 5;
+  const int W = d_c + d_r;
+
+  // B fragments (query rows) of the first tile are requested before the
+  // weight, so both loads are in flight together.
+  auto load_q = [&](int m0, bf16x8* bq) {
+    const int m = m0 + i16;
+    const uint16_t* qrow = q_nope + ((size_t)m * H + h) * d_n;
+#pragma unroll
+    for (int ks = 0; ks < AB_KS; ++ks) {
+      bq[ks] = bf16x8{};
+      const int d = 32 * ks + 8 * g;
+      if (ks < nks && m < mend && d < d_n) bq[ks] = load_bf16x8(qrow + d);
+    }
+  };
+  bf16x8 bq[AB_KS];
+  load_q(mbeg, bq);
+
+  const uint16_t* wsrc = w_uk + (size_t)h * d_n * d_c + cb * AB_CT;
+  for (int i = tid; i < nks * 32 * (AB_CT / 8); i += PJ_NT) {
+    const int d = i / (AB_CT / 8), ch = i % (AB_CT / 8);
+    u32x4 v = {0u, 0u, 0u, 0u};
+    if (d < d_n) v = *reinterpret_cast<const u32x4*>(wsrc + (size_t)d * d_c + ch * 8);
+    *reinterpret_cast<u32x4*>(wl + d * AB_LD + ch * 16) = v;
+  }
+  __syncthreads();
+
+  bf16x8 a[2][AB_KS];
+#pragma unroll
+  for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+    for (int ks = 0; ks < AB_KS; ++ks) {
+      if (ks < nks) {
+        const int col = 32 * wave + 16 * ct + 4 * (i16 & 3);
+        const int d = 32 * ks + 8 * g + (i16 >> 2);
+        const s16x4 v0 = lds_tr16(wl + d * AB_LD + 2 * col);
+        const s16x4 v1 = lds_tr16(wl + (d + 4) * AB_LD + 2 * col);
+        const short vv[8] = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
+        a[ct][ks] = __builtin_bit_cast(bf16x8, vv);
+      }
+    }
+
+  const int col0 = cb * AB_CT + 32 * wave + 4 * g;  // + 16 ct: this lane's 4 columns
+  for (int m0 = mbeg; m0 < mend; m0 += 16) {
+    const int m = m0 + i16;
+    const bool mok = m < mend;
+    f32x4 acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+    for (int ks = 0; ks < AB_KS; ++ks) {
+      if (ks < nks) {
+        acc[0] = mfma16(a[0][ks], bq[ks], acc[0]);
+        acc[1] = mfma16(a[1][ks], bq[ks], acc[1]);
+      }
+    }
+    if (m0 + 16 < mend) load_q(m0 + 16, bq);
+    if (mok) {
+      uint16_t* dst = q_abs + ((size_t)m * H + h) * W + col0;
+      store_bf16x4(dst, acc[0]);
+      store_bf16x4(dst + 16, acc[1]);
+    }
+  }
+
+  if (cb == 0) {  // the rotary part is carried over unchanged, 16 bytes at a time
+    const int chunks = d_r / 8;
+    for (int i = tid; i < (mend - mbeg) * chunks; i += PJ_NT) {
+      const int m = mbeg + i / chunks, r = 8 * (i % chunks);
+      *reinterpret_cast<u32x4*>(q_abs + ((size_t)m * H + h) * W + d_c + r) =
+          *reinterpret_cast<const u32x4*>(q_rope + ((size_t)m * H + h) * d_r + r);
+    }
+  }
+}
+
+// out_proj on MFMA.  Workgroup (h, vb, mz): value columns vb*64 .. +63 of head h
+// for query rows mz*64 .. +63; wave w holds W^UV[h][v][:] for its 16 columns v
+// (the A operand, loaded straight from HBM: both operands are contiguous along
+// the latent axis).  o_lat is fp32: each element is split once, when its
+// 16-row tile is staged in LDS, as hi = bf16(x), lo = bf16(x - hi), and both
+// halves are multiplied, so the product keeps about 16 significant bits of
+// o_lat instead of 8.  Staged rows are padded by 16 bytes so that the 16
+// rows a 16-lane group reads at one latent offset fall in distinct banks.
+constexpr int OP_LD = 2 * 32 * OP_KS + 16;  // bytes per staged row (d_c <= 512)
+
+__global__ __launch_bounds__(PJ_NT) void out_proj_mfma_kernel(
+    const float* __restrict__ o_lat, const uint16_t* __restrict__ w_uv,
+    uint16_t* __restrict__ out, int M, int H, int d_c, int d_v) {
+  __shared__ __align__(16) uint8_t st[2][16 * OP_LD];  // hi, lo
+  const int h = blockIdx.x, vb = blockIdx.y;
+  const int mbeg = blockIdx.z * PJ_MW, mend = min(M, mbeg + PJ_MW);
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int i16 = lane & 15, g = lane >> 4;
+  const int nks = d_c >> 5;
+  const int vrow = vb * OP_VT + 16 * wave + i16;  // A row of this lane
+
+  bf16x8 a[OP_KS];
+  const uint16_t* wrow = w_uv + ((size_t)h * d_v + vrow) * d_c + 8 * g;
+#pragma unroll
+  for (int ks = 0; ks < OP_KS; ++ks) {
+    a[ks] = bf16x8{};
+    if (ks < nks && vrow < d_v) a[ks] = load_bf16x8(wrow + 32 * ks);
+  }
+
+  const int v0 = vb * OP_VT + 16 * wave + 4 * g;  // this lane's 4 output columns
+  const int q4 = d_c >> 2;                        // float4 chunks per row
+  for (int m0 = mbeg; m0 < mend; m0 += 16) {
+    // stage rows m0 .. m0+15 (zeros past mend) as bf16 hi / lo
+    for (int i = tid; i < 16 * q4; i += PJ_NT) {
+      const int r = i / q4, c4 = i - r * q4;
+      f32x4 x = {0.f, 0.f, 0.f, 0.f};
+      if (m0 + r < mend)
+        x = *reinterpret_cast<const f32x4*>(o_lat + ((size_t)(m0 + r) * H + h) * d_c + 4 * c4);
+      u16x4 hb, lb;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        hb[e] = f32_to_bf16(x[e]);
+        lb[e] = f32_to_bf16(x[e] - bf16_to_f32(hb[e]));
+      }
+      *reinterpret_cast<u16x4*>(st[0] + r * OP_LD + 8 * c4) = hb;
+      *reinterpret_cast<u16x4*>(st[1] + r * OP_LD + 8 * c4) = lb;
+    }
+    __syncthreads();
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    const int boff = i16 * OP_LD + 16 * g;
+#pragma unroll
+    for (int ks = 0; ks < OP_KS; ++ks) {
+      if (ks < nks) {
+        const bf16x8 bh = *reinterpret_cast<const bf16x8*>(st[0] + boff + 64 * ks);
+        const bf16x8 bl = *reinterpret_cast<const bf16x8*>(st[1] + boff + 64 * ks);
+        acc = mfma16(a[ks], bh, acc);
+        acc = mfma16(a[ks], bl, acc);
+      }
+    }
+    const int m = m0 + i16;
+    if (m < mend) {
+      uint16_t* dst = out + ((size_t)m * H + h) * d_v + v0;
+      if (v0 + 3 < d_v) {
+        store_bf16x4(dst, acc);
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (v0 + i < d_v) dst[i] = f32_to_bf16(acc[i]);
+      }
+    }
+    __syncthreads();  // the next tile overwrites the staging buffer
+  }
+}
+
+bool absorb_mfma_fits(int d_n, int d_c, int d_r) {
+  return d_c % AB_CT == 0 && d_n % 8 == 0 && d_n > 0 && d_n <= 32 * AB_KS && d_r % 8 == 0;
+}
+
+bool out_proj_mfma_fits(int d_c, int d_v) {
+  return d_c % 32 == 0 && d_c > 0 && d_c <= 32 * OP_KS && d_v % 4 == 0;
+}
+
 }  // namespace
 
 hipError_t launch_absorb_q(int dtype, const void* q_nope, const void* q_rope, const void* w_uk,
                            void* q_abs, int M, int H, int d_n, int d_c, int d_r,
                            hipStream_t stream) {
   if (M <= 0) return hipSuccess;
+  if (dtype == 1 && absorb_mfma_fits(d_n, d_c, d_r)) {
+    const dim3 grid(H, d_c / AB_CT, (M + PJ_MW - 1) / PJ_MW);
+    const size_t shmem = (size_t)((d_n + 31) & ~31) * AB_LD;
+    hipLaunchKernelGGL(absorb_q_mfma_kernel, grid, dim3(PJ_NT), shmem, stream,
+                       (const uint16_t*)q_nope, (const uint16_t*)q_rope, (const uint16_t*)w_uk,
+                       (uint16_t*)q_abs, M, H, d_n, d_c, d_r);
+    return hipGetLastError();
+  }
   const dim3 grid(H, (d_c + ABS_NT - 1) / ABS_NT, (M + ABS_MT - 1) / ABS_MT);
   const size_t shmem = (size_t)ABS_MT * d_n * sizeof(float);
   if (dtype == 0)
@@ -116,6 +337,12 @@ hipError_t launch_absorb_q(int dtype, const void* q_nope, const void* q_rope, co
 hipError_t launch_out_proj(int dtype, const float* o_lat, const void* w_uv, void* out, int M,
                            int H, int d_c, int d_v, hipStream_t stream) {
   if (M <= 0) return hipSuccess;
+  if (dtype == 1 && out_proj_mfma_fits(d_c, d_v)) {
+    const dim3 grid(H, (d_v + OP_VT - 1) / OP_VT, (M + PJ_MW - 1) / PJ_MW);
+    hipLaunchKernelGGL(out_proj_mfma_kernel, grid, dim3(PJ_NT), 0, stream, o_lat,
+                       (const uint16_t*)w_uv, (uint16_t*)out, M, H, d_c, d_v);
+    return hipGetLastError();
+  }
   const dim3 grid(H, (d_v + OP_T - 1) / OP_T, (M + OP_T - 1) / OP_T);
   if (dtype == 0)
     hipLaunchKernelGGL(out_proj_kernel<float>, grid, dim3(256), 0, stream, o_lat,

@@ -142,6 +142,44 @@ def test_step_parity(name):
     assert np.array_equal(dev_bits(dev["pool"]), pool_bits(pool_r, w.dtype))
 
 
+# ------------------------------------------------------------------ projections
+
+@pytest.mark.parametrize("name,M", [("v3", 1), ("v3", 150), ("v2_multi", 77),
+                                    ("tiny_f32", 35)])
+def test_projections_elementwise(name, M):
+    """mla_absorb_q and mla_out_proj alone, with M rows ragged against the
+    kernels' 16-row tiles and 64-row workgroups.  Each output element is held
+    to what its arithmetic allows, not to the decode tolerance: the fp64
+    oracle on the same (rounded) inputs, plus the rounding of the output to
+    the storage type (half an ulp: 2^-9 relative in bf16) and fp32
+    accumulation.  For out_proj the fp32 latent input must enter the product
+    with far more than bf16's 8 bits: the absolute slack 1e-4 * max|ref| is
+    below what rounding o_lat to bf16 would cost at d_c = 512."""
+    w = REDUCED[name].scaled(B=M, T=1, N=8)
+    bt = make_inputs(w, with_rows=False)
+    note(f"projections {name} M={M}")
+    cfg = cfg_of(w)
+    dt = torch_dtype(bt)
+    q_nope = to_dev(bt.q_nope.reshape(M, w.H, w.d_n), dt, "cuda")
+    q_rope = to_dev(bt.q_rope.reshape(M, w.H, w.d_r), dt, "cuda")
+    w_uk = to_dev(bt.w_uk, dt, "cuda")
+    w_uv = to_dev(bt.w_uv, dt, "cuda")
+    q_abs = torch.full((M, w.H, w.W), float("nan"), dtype=dt, device="cuda")
+    mla.mla_absorb_q(cfg, q_nope, q_rope, w_uk, q_abs)
+    o_lat_h = np.random.default_rng(11).standard_normal((M, w.H, w.d_c)).astype(np.float32)
+    out = torch.full((M, w.H, w.d_v), float("nan"), dtype=dt, device="cuda")
+    mla.mla_out_proj(cfg, torch.from_numpy(o_lat_h).cuda(), w_uv, out)
+    torch.cuda.synchronize()
+    rel = 2.0 ** -8 if w.dtype == "bf16" else 1e-6
+    qa_ref = oracle.absorb_q_ref(bt.q_nope.reshape(M, w.H, w.d_n),
+                                 bt.q_rope.reshape(M, w.H, w.d_r), bt.w_uk)
+    qa = q_abs.float().cpu().numpy().astype(np.float64)
+    assert np.all(np.abs(qa - qa_ref) <= rel * np.abs(qa_ref) + 1e-5 * np.max(np.abs(qa_ref)))
+    out_ref = oracle.out_proj_ref(o_lat_h, bt.w_uv)
+    o = out.float().cpu().numpy().astype(np.float64)
+    assert np.all(np.abs(o - out_ref) <= rel * np.abs(out_ref) + 1e-4 * np.max(np.abs(out_ref)))
+
+
 # ------------------------------------------------------------------ invariances
 
 def test_split_count_invariance():
