@@ -87,6 +87,9 @@ def main() -> int:
     ap.add_argument("--num-splits", type=int, default=0)
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="only run a plain device copy of this many MiB five times "
+                         "(the known-size reference for HBM byte counters) and exit")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -96,6 +99,18 @@ def main() -> int:
 
     import numpy as np
     import torch
+
+    if args.copy_probe_mib > 0:
+        # One elementwise kernel per call that reads n bytes and writes n bytes.
+        n = args.copy_probe_mib << 20
+        src = torch.ones(n // 4, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            torch.mul(src, 1.0, out=dst)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_probe_bytes_read": n, "copy_probe_bytes_written": n,
+                          "launches": 5}))
+        return 0
 
     from mla_latent_kv_36_amd import binding as mla
     from mla_latent_kv_36_amd import build as mbuild

@@ -40,44 +40,49 @@ bool use_mfma(const mla_config* c, int T) {
 }
 
 // Split plan: the rows of the longest sequence are cut into `splits` ranges of
-// `chunk` pages each.  Shorter sequences use the leading ranges only.
+// `chunk` rows each (a multiple of the decode kernel's granule: its 32-row
+// pipeline unit for the MFMA kernel, a page for the generic one).  Shorter
+// sequences use the leading ranges only.
 struct Plan {
   int splits;
-  int chunk;
+  int chunk;  // rows per split
 };
 
-int heuristic_splits(const mla_config* c, int B, int T, int pages_max, int64_t total_tokens) {
-  if (pages_max <= 1) return 1;
-  const int64_t bs = c->block_size;
-  const int64_t pages_total =
-      total_tokens > 0 ? (total_tokens + bs - 1) / bs + B : (int64_t)B * pages_max;
+int granule(const mla_config* c, int T) { return use_mfma(c, T) ? 32 : c->block_size; }
+
+int heuristic_splits(const mla_config* c, int B, int T, int gran_max, int64_t total_tokens) {
+  if (gran_max <= 1) return 1;
+  const int64_t g = granule(c, T);
+  const int64_t gran_total =
+      total_tokens > 0 ? (total_tokens + g - 1) / g + B : (int64_t)B * gran_max;
   if (use_mfma(c, T)) {
-    // Units of work are (row group, page).  The kernel's LDS ring fits one
-    // workgroup per compute unit, so aim for one wave of workgroups over the
-    // chip, but keep at least 4 pages per workgroup so the partial outputs
-    // (128 KiB per workgroup) stay well below the cache bytes read.
+    // Units of work are (64-row query group, 32-row unit of the cache).  The
+    // kernel's LDS ring fits one workgroup per compute unit, so aim for one
+    // wave of workgroups over the chip, but keep at least 8 units per
+    // workgroup so the partial outputs (128 KiB per workgroup) stay well below
+    // the cache bytes read.
     const int64_t groups = (int64_t)T * c->n_heads / 64;
-    const int64_t work = pages_total * groups;
+    const int64_t work = gran_total * groups;
     int64_t chunk = (work + kCUs - 1) / kCUs;
-    if (chunk < 4) chunk = 4;
-    return (int)((pages_max + chunk - 1) / chunk);
+    if (chunk < 8) chunk = 8;
+    return (int)((gran_max + chunk - 1) / chunk);
   }
   const int64_t rows = (int64_t)B * T * c->n_heads;
   int64_t s = (4 * kCUs + rows - 1) / rows;
-  if (s > pages_max) s = pages_max;
+  if (s > gran_max) s = gran_max;
   return (int)(s < 1 ? 1 : s);
 }
 
 Plan make_plan(const mla_config* c, int B, int T, int max_seq_len, int64_t total_tokens,
                int num_splits) {
-  const int bs = c->block_size;
-  const int pages_max = max_seq_len > 0 ? (max_seq_len + bs - 1) / bs : 0;
-  int want = num_splits > 0 ? num_splits : heuristic_splits(c, B, T, pages_max, total_tokens);
-  if (want > pages_max) want = pages_max;
+  const int g = granule(c, T);
+  const int gran_max = max_seq_len > 0 ? (max_seq_len + g - 1) / g : 0;
+  int want = num_splits > 0 ? num_splits : heuristic_splits(c, B, T, gran_max, total_tokens);
+  if (want > gran_max) want = gran_max;
   if (want < 1) want = 1;
-  const int chunk = pages_max > 0 ? (pages_max + want - 1) / want : 1;
-  const int splits = pages_max > 0 ? (pages_max + chunk - 1) / chunk : 1;
-  return Plan{splits, chunk};
+  const int chunk = gran_max > 0 ? (gran_max + want - 1) / want : 1;
+  const int splits = gran_max > 0 ? (gran_max + chunk - 1) / chunk : 1;
+  return Plan{splits, chunk * g};
 }
 
 size_t round256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -214,7 +219,7 @@ mla_status mla_decode(const mla_config* cfg, const void* q_abs, const void* pool
   p.cap = max_seq_len_host;
   p.causal = causal;
   p.num_splits = pl.splits;
-  p.chunk_pages = pl.chunk;
+  p.chunk_rows = pl.chunk;
   p.scale_log2 = softmax_scale(cfg) * 1.4426950408889634f;
 
   hipStream_t s = static_cast<hipStream_t>(stream);

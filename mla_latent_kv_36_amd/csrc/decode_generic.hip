@@ -58,22 +58,19 @@ __global__ __launch_bounds__(NT) void decode_generic_kernel(const DecodeParams p
   const int t = rr / p.H;
   const int bs = p.block_size;
   const int n_valid = visible_rows(p.seq_lens[b], p.T, t, p.causal, p.cap);
-  const int pages = (n_valid + bs - 1) / bs;
-  const int p0 = s * p.chunk_pages;
-  const int p1 = min(p0 + p.chunk_pages, pages);
+  const int j0 = s * p.chunk_rows;
+  const int j1 = min(j0 + p.chunk_rows, n_valid);
   const bool direct = (p.num_splits == 1);
   float* dst = direct ? p.o_lat + (size_t)row * p.d_c
                       : p.part_o + (((size_t)b * p.num_splits + s) * TH + rr) * p.d_c;
 
-  if (p0 >= p1) {
+  if (j0 >= j1) {
     if (direct) {
       for (int d = tid; d < p.d_c; d += NT) dst[d] = 0.0f;
       if (tid == 0 && p.lse != nullptr) p.lse[row] = -INFINITY;
     }
     return;
   }
-  const int j0 = p0 * bs;
-  const int j1 = min(p1 * bs, n_valid);
 
   const E* q = static_cast<const E*>(p.q_abs) + (size_t)row * W;
   for (int k = tid; k < W; k += NT) sq[k] = Elem<E>::load(q, k);
@@ -136,12 +133,16 @@ __global__ __launch_bounds__(NT) void decode_generic_kernel(const DecodeParams p
 }
 
 // Log-sum-exp merge of the splits of one query row: with M = max_s lse_s and
-// w_s = exp(lse_s - M), o = sum_s w_s o_s / sum_s w_s, lse = M + log sum_s w_s.
-// Only splits that hold rows of this query are read (the same page arithmetic
-// as the split kernels), in split order, so the result is deterministic.
-// One wave per query row; each lane owns 4 consecutive latent columns per
-// 256-column block and streams the splits' partials with 128-bit loads.
-constexpr int CMB_ROWS = 4;  // query rows (waves) per workgroup
+// w_s = exp(lse_s - M), o = sum_s w_s o_s / sum_s w_s, lse = M + log sum_s w_s
+// ("Attention, Part 2: MQA, GQA and MLA": the partial results of disjoint row
+// ranges combine exactly through their log-sum-exp).  Only splits that hold
+// rows of this query are read (the same row arithmetic as the split
+// kernels), in split order, so the result is deterministic.  One wave per
+// query row; each lane owns 4 consecutive latent columns per 256-column block.
+// For up to CMB_FAST splits and d_c <= 512 every partial load of a lane is
+// issued before the first one is used.
+constexpr int CMB_ROWS = 4;   // query rows (waves) per workgroup
+constexpr int CMB_FAST = 16;  // splits merged with all loads in flight
 
 __global__ __launch_bounds__(64 * CMB_ROWS) void combine_kernel(const DecodeParams p) {
   const int TH = p.T * p.H;
@@ -153,8 +154,7 @@ __global__ __launch_bounds__(64 * CMB_ROWS) void combine_kernel(const DecodePara
   const int rr = (int)(row - (long long)b * TH);
   const int t = rr / p.H;
   const int n_valid = visible_rows(p.seq_lens[b], p.T, t, p.causal, p.cap);
-  const int pages = (n_valid + p.block_size - 1) / p.block_size;
-  const int ns = min(p.num_splits, (pages + p.chunk_pages - 1) / p.chunk_pages);
+  const int ns = min(p.num_splits, (n_valid + p.chunk_rows - 1) / p.chunk_rows);
   float* out = p.o_lat + (size_t)row * p.d_c;
   const float* lse_b = p.part_lse + (size_t)b * p.num_splits * TH + rr;
   const float* po_b = p.part_o + ((size_t)b * p.num_splits * TH + rr) * p.d_c;
@@ -170,36 +170,32 @@ __global__ __launch_bounds__(64 * CMB_ROWS) void combine_kernel(const DecodePara
   float den = 0.0f;
   for (int s = 0; s < ns; ++s) den += exp2f((lse_b[(size_t)s * TH] - M) * kLog2e);
   const float inv = 1.0f / den;
-  if ((p.d_c & 3) == 0) {
-    for (int d = 4 * lane; d < p.d_c; d += 256) {
-      float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
-      int s = 0;
-      for (; s + 4 <= ns; s += 4) {
-        float4 v[4];
-        float w[4];
+
+  if ((p.d_c & 255) == 0 && p.d_c <= 512 && ns <= CMB_FAST) {
+    const int nblk = p.d_c >> 8;  // 1 or 2 blocks of 256 columns
+    f32x4 v[CMB_FAST][2];
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          v[k] = *reinterpret_cast<const float4*>(po_b + (size_t)(s + k) * sstride + d);
-          w[k] = exp2f((lse_b[(size_t)(s + k) * TH] - M) * kLog2e);
-        }
+    for (int s = 0; s < CMB_FAST; ++s) {
+      if (s < ns) {
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          a.x += w[k] * v[k].x;
-          a.y += w[k] * v[k].y;
-          a.z += w[k] * v[k].z;
-          a.w += w[k] * v[k].w;
-        }
+        for (int k = 0; k < 2; ++k)
+          if (k < nblk)
+            v[s][k] = *reinterpret_cast<const f32x4*>(po_b + (size_t)s * sstride + 256 * k + 4 * lane);
       }
-      for (; s < ns; ++s) {
-        const float4 v = *reinterpret_cast<const float4*>(po_b + (size_t)s * sstride + d);
-        const float w = exp2f((lse_b[(size_t)s * TH] - M) * kLog2e);
-        a.x += w * v.x;
-        a.y += w * v.y;
-        a.z += w * v.z;
-        a.w += w * v.w;
-      }
-      *reinterpret_cast<float4*>(out + d) = make_float4(a.x * inv, a.y * inv, a.z * inv, a.w * inv);
     }
+    f32x4 a[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+    for (int s = 0; s < CMB_FAST; ++s) {
+      if (s < ns) {
+        const float w = exp2f((lse_b[(size_t)s * TH] - M) * kLog2e);
+#pragma unroll
+        for (int k = 0; k < 2; ++k)
+          if (k < nblk) a[k] += w * v[s][k];
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < 2; ++k)
+      if (k < nblk) *reinterpret_cast<f32x4*>(out + 256 * k + 4 * lane) = a[k] * inv;
   } else {
     for (int d = lane; d < p.d_c; d += 64) {
       float a = 0.0f;

@@ -43,6 +43,8 @@
 // token(lhi, e) = 4*(e & 3) + 2*lhi + (e >> 2) for k-slot 8*lhi + e, and P is
 // written in that order (the sum over tokens does not depend on it).  Layouts
 // were chosen by measuring SQ_LDS_BANK_CONFLICT on gfx950.
+#include <type_traits>
+
 #include "common.h"
 #include "launch.h"
 
@@ -61,22 +63,33 @@ constexpr int TILE_BYTES = BS * ROW_BYTES;  // 73728 per page in HBM
 constexpr int LAT_SLOTS = 4;
 constexpr int ROT_SLOTS = 3;
 constexpr int P_LD = 40;                    // bf16 per row of a P tile (32 + pad)
-constexpr int QSTEPS = W / 32;              // 18 k-steps of 32 columns
-constexpr int COPIES = 9;                   // direct-to-LDS copies per value wave per unit
+constexpr int QSTEPS = W / 32;              // 18 k-steps of 32 columns (score MFMA)
+constexpr int COPIES = 18;                  // direct-to-LDS copies per copy wave per unit
 constexpr float kRescaleSlack = 8.0f;       // log2 units
+
+constexpr int S_LD = 36;                    // floats per row of the score tile (32 + pad)
+constexpr int A_SPLIT = 9;                  // score k-steps of unit j+2 run between M(j) and E(j)
 
 struct __align__(16) Smem {
   uint8_t lat[LAT_SLOTS][UNIT * 1024];
   uint8_t rot[ROT_SLOTS][UNIT * 128];
-  uint16_t p[2][ROWS * P_LD];  // [unit parity]
-  float alpha[2][ROWS];
+  float s[ROWS * S_LD];        // raw scores of one unit, [row][token]
+  uint16_t p[ROWS * P_LD];     // probabilities of one unit (bf16), [row][k-slot]
+  float alpha[ROWS];           // per-row rescale factor of that unit
   float lrow[ROWS];
-  float mrow[ROWS];
-  int flag[2][4];  // [unit parity][score wave]: some row of the wave raised its max
+  int flag[2];                 // [copy wave]: some row of its 32 raised its max
 };
 
 __device__ __forceinline__ int lat_sw(int t) { return t & 15; }
 __device__ __forceinline__ int rot_sw(int t) { return (t >> 1) & 7; }
+
+// Token (within a 16-token k-step of P.V) held at P k-slot m, 0 <= m < 16.
+// The value waves' transposing reads take the 4 tokens of a slot quad 4
+// apart (which keeps those reads free of bank conflicts), so slot 8h + e
+// holds token 4(e & 3) + 2h + (e >> 2).
+__device__ __forceinline__ int tok_of(int m) {
+  return 4 * (m & 3) + 2 * (m >> 3) + ((m >> 2) & 1);
+}
 
 __device__ __forceinline__ f32x16 mfma32(const bf16x8& a, const bf16x8& b, const f32x16& c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
@@ -86,6 +99,7 @@ __device__ __forceinline__ f32x4 mfma16(const bf16x8& a, const bf16x8& b, const 
 }
 
 typedef __attribute__((__vector_size__(4 * sizeof(short)))) short s16x4;
+typedef __attribute__((__vector_size__(8 * sizeof(uint16_t)))) uint16_t u16x8;
 
 __device__ __forceinline__ s16x4 lds_tr16(const uint8_t* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
@@ -147,22 +161,37 @@ __global__ __launch_bounds__(NT, 1) void decode_mfma_kernel(const DecodeParams p
 
   const int G = (p.T * p.H) / ROWS;
   const int S = p.num_splits;
-  int idx = blockIdx.x;
-  const int g = idx % G;
-  idx /= G;
-  const int s = idx % S;
-  const int b = idx / S;
+  // Workgroup i is dispatched to XCD i % 8, and each XCD has its own L2.  XCD
+  // x gets a contiguous block of (sequence, split) pairs, and all G 64-row
+  // groups of each: the pages of a pair and the absorbed queries of a
+  // sequence then come from HBM once per XCD and from L2 for the other
+  // workgroups that read them.  Ids past the last full set of 8G keep the
+  // plain order.
+  constexpr int XCDS = 8;
+  const int i = blockIdx.x;
+  const int full = (int)gridDim.x - (int)gridDim.x % (XCDS * G);
+  int g, pair;
+  if (i < full) {
+    const int r = i / XCDS;
+    g = r % G;
+    pair = (i % XCDS) * (full / G / XCDS) + r / G;
+  } else {
+    g = i % G;
+    pair = i / G;
+  }
+  const int s = pair % S;
+  const int b = pair / S;
 
   const int TH = p.T * p.H;
   const int rb = g * ROWS;  // first query row (t*H + h) of the group
   const int t = rb / p.H;
   const int n_valid = visible_rows(p.seq_lens[b], p.T, t, p.causal, p.cap);
-  const int pages = (n_valid + BS - 1) / BS;
-  const int p0 = s * p.chunk_pages;
-  const int p1 = min(p0 + p.chunk_pages, pages);
+  // this range: cache rows tok0 .. tok_end-1 (tok0 is a multiple of UNIT)
+  const int tok0 = s * p.chunk_rows;
+  const int tok_end = min(tok0 + p.chunk_rows, n_valid);
   const bool direct = (S == 1);
 
-  if (p0 >= p1) {
+  if (tok0 >= tok_end) {
     if (direct) {  // no visible row: o = 0, lse = -inf
       float* dst = p.o_lat + ((size_t)b * TH + rb) * DC;
       for (int i = tid; i < ROWS * DC; i += NT) dst[i] = 0.0f;
@@ -170,128 +199,123 @@ __global__ __launch_bounds__(NT, 1) void decode_mfma_kernel(const DecodeParams p
     }
     return;
   }
-  // units of this range: 32-token halves of pages p0.., up to the last visible token
-  const int tok0 = p0 * BS;
-  const int U = min(2 * (p1 - p0), (n_valid - tok0 + UNIT - 1) / UNIT);
-  auto unit_valid = [&](int u) { return min(UNIT, n_valid - tok0 - u * UNIT); };
+  // its 32-row units; only the last unit of the sequence can be partial
+  const int U = (tok_end - tok0 + UNIT - 1) / UNIT;
+  auto unit_valid = [&](int u) { return min(UNIT, tok_end - tok0 - u * UNIT); };
 
-  if (wave < 4) {
+  // Two barriers per unit.  Barrier schedule, the same for every wave: B0,
+  // then M(j) and E(j) for j = -1 .. U-1, then F.
+  //   E(j-1) .. M(j): score waves finish the scores of unit j+1 and store them
+  //     raw (fp32) in sm.s; value waves read P(j) and V(j) into registers and
+  //     start O += P(j) V(j); copy waves issue the copies of unit j+3 and
+  //     wait for unit j+2.
+  //   M(j) .. E(j): copy waves turn sm.s into P(j+1) (softmax, 32 rows each),
+  //     on the same SIMDs where the score waves start on unit j+2, so that
+  //     VALU and MFMA work overlap there; value waves finish O += P(j) V(j).
+  // Each of sm.s, sm.p and sm.alpha is written in one phase and read in the
+  // other, so one buffer of each suffices.
+  if (wave < 2) {
     // =============================== score waves ===============================
-    const int r16 = lane & 15;  // row within the wave's 16, and token within a 16-token tile
-    const int g4 = lane >> 4;   // 8-column group of a k-step; 4-token group of an output
-    const int srow = 16 * wave + r16;
-
-    bf16x8 qf[QSTEPS];  // B operand: Q[srow][32kk + 8*g4 .. +7]
-    {
-      const uint16_t* q = static_cast<const uint16_t*>(p.q_abs) +
-                          ((size_t)b * TH + rb + srow) * W + 8 * g4;
+    // Wave w owns query rows 32w .. 32w+31 as two 16-row tiles rt.  S^T = K . Q^T
+    // on v_mfma_f32_16x16x32_bf16 over all 576 columns, for two 16-token tiles
+    // ti: A = 16 tokens x 32 columns of K (lane l: token l & 15, columns
+    // 8(l >> 4) .. +7), B = the same columns of Q^T for one row tile, held in
+    // registers for the whole range (2 x 18 k-steps, 144 VGPRs).  Each K
+    // fragment feeds both row tiles; the four (rt, ti) accumulators are four
+    // independent MFMA chains.  A lane's results are query row 32w + 16rt +
+    // (l & 15), tokens 16ti + 4(l >> 4) .. +3: one 16-byte store each.
+    const int n16 = lane & 15;
+    const int g4 = lane >> 4;
+    bf16x8 qf[2][QSTEPS];  // Q[32w + 16rt + n16][32kk + 8*g4 .. +7]
 #pragma unroll
-      for (int kk = 0; kk < QSTEPS; ++kk) qf[kk] = *reinterpret_cast<const bf16x8*>(q + 32 * kk);
+    for (int rt = 0; rt < 2; ++rt) {
+      const uint16_t* q = static_cast<const uint16_t*>(p.q_abs) +
+                          ((size_t)b * TH + rb + 32 * wave + 16 * rt + n16) * W + 8 * g4;
+#pragma unroll
+      for (int kk = 0; kk < QSTEPS; ++kk)
+        qf[rt][kk] = *reinterpret_cast<const bf16x8*>(q + 32 * kk);
     }
-    // A operand: K[token r16 (+16 ti)][32kk + 8*g4 .. +7]: latent chunk
-    // c = 4kk + g4, stored at position c ^ lat_sw(r16); rotary chunk
-    // c = 4(kk-16) + g4 at position c ^ rot_sw(r16).
-    const int tsw = lat_sw(r16);
+    // K fragment offsets: latent chunk c = 4kk + g4 of token n16 sits at chunk
+    // position c ^ lat_sw(n16) (only the low 4 bits of c take part), rotary
+    // chunk c = 4(kk - 16) + g4 at c ^ rot_sw(n16); token tile ti adds 16 KiB
+    // (latent) or 2 KiB (rotary).
     int loff[4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) loff[j] = r16 * 1024 + (((4 * j + g4) ^ tsw) << 4);
+    for (int j = 0; j < 4; ++j) loff[j] = n16 * 1024 + (((4 * j + g4) ^ lat_sw(n16)) << 4);
     int roff[2];
 #pragma unroll
-    for (int j = 0; j < 2; ++j) roff[j] = r16 * 128 + (((4 * j + g4) ^ rot_sw(r16)) << 4);
+    for (int j = 0; j < 2; ++j) roff[j] = n16 * 128 + (((4 * j + g4) ^ rot_sw(n16)) << 4);
 
-    float m_run = -INFINITY;  // reference max (log2 units) of row srow
-    float l_run = 0.0f;       // running sum in that reference
-
-    auto score_softmax = [&](int u) {
-      const uint8_t* lat = sm.lat[u & 3];
-      const uint8_t* rot = sm.rot[u % 3];
-      f32x4 acc[2];
+    f32x4 acc[2][2];  // [rt][ti], carried from the first k-steps to the rest
+    auto kfrag = [&](int u, int kk, int ti) {
+      const uint8_t* a = kk < 16 ? sm.lat[u & 3] + loff[kk & 3] + ti * 16 * 1024 + ((kk >> 2) << 8)
+                                 : sm.rot[u % 3] + roff[kk - 16] + ti * 16 * 128;
+      return *reinterpret_cast<const bf16x8*>(a);
+    };
+    // k-steps [KB, KE) of unit u, fragments read KDEPTH k-steps ahead
+    auto steps = [&](int u, auto kb_tag, auto ke_tag) {
+      constexpr int KB = decltype(kb_tag)::value, KE = decltype(ke_tag)::value;
+      constexpr int KDEPTH = 4;
+      bf16x8 kf[KDEPTH][2];
 #pragma unroll
-      for (int ti = 0; ti < 2; ++ti)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) acc[ti][i] = 0.0f;
-#pragma unroll
-      for (int kk = 0; kk < 16; ++kk) {  // content term: latent chunks 0..63
-#pragma unroll
-        for (int ti = 0; ti < 2; ++ti) {
-          const bf16x8 k = *reinterpret_cast<const bf16x8*>(
-              lat + loff[kk & 3] + ti * 16 * 1024 + ((4 * kk & ~15) << 4));
-          acc[ti] = mfma16(k, qf[kk], acc[ti]);
-        }
+      for (int kk = KB; kk < KB + KDEPTH && kk < KE; ++kk) {
+        kf[kk % KDEPTH][0] = kfrag(u, kk, 0);
+        kf[kk % KDEPTH][1] = kfrag(u, kk, 1);
       }
 #pragma unroll
-      for (int kk = 16; kk < QSTEPS; ++kk) {  // rotary term
-#pragma unroll
-        for (int ti = 0; ti < 2; ++ti) {
-          const bf16x8 k =
-              *reinterpret_cast<const bf16x8*>(rot + roff[kk - 16] + ti * 16 * 128);
-          acc[ti] = mfma16(k, qf[kk], acc[ti]);
+      for (int kk = KB; kk < KE; ++kk) {
+        const bf16x8 k0 = kf[kk % KDEPTH][0];
+        const bf16x8 k1 = kf[kk % KDEPTH][1];
+        if (kk + KDEPTH < KE) {
+          kf[kk % KDEPTH][0] = kfrag(u, kk + KDEPTH, 0);
+          kf[kk % KDEPTH][1] = kfrag(u, kk + KDEPTH, 1);
         }
+        acc[0][0] = mfma16(k0, qf[0][kk], acc[0][0]);
+        acc[1][0] = mfma16(k0, qf[1][kk], acc[1][0]);
+        acc[0][1] = mfma16(k1, qf[0][kk], acc[0][1]);
+        acc[1][1] = mfma16(k1, qf[1][kk], acc[1][1]);
+        __builtin_amdgcn_sched_barrier(0);
       }
-      // lane holds row srow, tokens 16ti + 4*g4 + i of the unit
-      const int valid = unit_valid(u);
-      float mx = -INFINITY;
+    };
+    using K0 = std::integral_constant<int, 0>;
+    using KA = std::integral_constant<int, A_SPLIT>;
+    using KN = std::integral_constant<int, QSTEPS>;
+    auto first_steps = [&](int u) {
 #pragma unroll
-      for (int ti = 0; ti < 2; ++ti)
+      for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int tk = 16 * ti + 4 * g4 + i;
-          const float v = (tk < valid) ? acc[ti][i] * p.scale_log2 : -INFINITY;
-          acc[ti][i] = v;
-          mx = fmaxf(mx, v);
-        }
-      mx = xor32_max(xor16_max(mx));
-      const bool raise = mx > m_run + kRescaleSlack;  // always on the first unit
-      const float m_new = raise ? mx : m_run;
-      const float alpha = raise ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.0f;
-      m_run = m_new;
-      float sum = 0.0f;
-      // token 16ti + 4*g4 + i goes to k-slot 16ti + 4i + g4 (see the LDS notes)
-      uint16_t* prow = sm.p[u & 1] + srow * P_LD + g4;
+        for (int ti = 0; ti < 2; ++ti)
 #pragma unroll
-      for (int ti = 0; ti < 2; ++ti) {
+          for (int i = 0; i < 4; ++i) acc[rt][ti][i] = 0.0f;
+      steps(u, K0{}, KA{});
+    };
+    auto finish_and_store = [&](int u) {
+      steps(u, KA{}, KN{});
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float e = __builtin_amdgcn_exp2f(acc[ti][i] - m_new);
-          sum += e;
-          prow[16 * ti + 4 * i] = f32_to_bf16(e);
-        }
-      }
-      sum = xor32_sum(xor16_sum(sum));
-      l_run = l_run * alpha + sum;
-      if (lane < 16) sm.alpha[u & 1][srow] = alpha;
-      const bool any_raise = __any(raise);
-      if (lane == 0) sm.flag[u & 1][wave] = any_raise ? 1 : 0;
+      for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+        for (int ti = 0; ti < 2; ++ti)
+          *reinterpret_cast<f32x4*>(&sm.s[(32 * wave + 16 * rt + n16) * S_LD + 16 * ti + 4 * g4]) =
+              acc[rt][ti];
     };
 
-    // prologue: unit 0 (copies issued by the value waves)
     lds_barrier();                         // B0: unit 0 landed
-    if (unit_valid(0) < UNIT) lds_barrier();
-    score_softmax(0);
-    lds_barrier();                         // E
-    if (U > 1 && unit_valid(1) < UNIT) lds_barrier();
-    for (int j = 0; j < U; ++j) {
-      if (j + 1 < U) score_softmax(j + 1);
-      lds_barrier();                       // E
-      if (j + 2 < U && unit_valid(j + 2) < UNIT) lds_barrier();
-    }
-
-    if (lane < 16) {
-      sm.lrow[srow] = l_run;
-      sm.mrow[srow] = m_run;
+    first_steps(0);
+    for (int j = -1; j < U; ++j) {
+      if (j + 1 < U) finish_and_store(j + 1);
+      lds_barrier();                       // M(j)
+      if (j + 2 < U) first_steps(j + 2);
+      lds_barrier();                       // E(j)
     }
     lds_barrier();                         // F
-    if (tid < ROWS) {
-      const float v = (sm.mrow[tid] + log2f(sm.lrow[tid])) * kLn2;
-      if (direct) {
-        if (p.lse != nullptr) p.lse[(size_t)b * TH + rb + tid] = v;
-      } else {
-        p.part_lse[((size_t)b * S + s) * TH + rb + tid] = v;
-      }
-    }
-  } else {
-    // =============================== value waves ===============================
-    const int v = wave - 4;
+  } else if (wave >= 4 && wave < 6) {
+    // ============================ copy / softmax waves ===========================
+    // Copy wave c fills latent rows t = c + 2i (i < 16) and the rotary rows
+    // 16c .. 16c+15 of a unit: 18 direct-to-LDS copies of 1 KiB.  Lane l
+    // fetches the chunk that belongs at LDS chunk position l of its row
+    // (latent), or at slot l & 7 of row 8q + (l >> 3) (rotary).  It also runs
+    // the softmax of query rows 32c .. 32c+31.
+    const int c = wave - 4;
     const int32_t* table = p.block_table + (size_t)b * p.max_blocks;
     // Page ids are read through the constant address space: the index is
     // uniform, so this is a scalar load (lgkmcnt), and the wait for it does not
@@ -299,45 +323,144 @@ __global__ __launch_bounds__(NT, 1) void decode_mfma_kernel(const DecodeParams p
     const int32_t __attribute__((address_space(4)))* ctable =
         (const int32_t __attribute__((address_space(4)))*)table;
     const uint8_t* pool = static_cast<const uint8_t*>(p.pool);
-
-    // Copies: value wave v fills latent rows t = v + 4i (i < 8) and the rotary
-    // rows 8v..8v+7 of a unit; lane l fetches the chunk that belongs at LDS
-    // chunk position l of its row (latent) or slot l of its 8-row block (rotary).
-    int cl[4];
+    int cl[8];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) cl[i] = (lane ^ lat_sw(v + 4 * i)) << 4;
-    const int rt_row = 8 * v + (lane >> 3);
-    const int cr = rt_row * ROW_BYTES + 1024 + (((lane & 7) ^ rot_sw(rt_row)) << 4);
+    for (int i = 0; i < 8; ++i) cl[i] = (lane ^ lat_sw(c + 2 * i)) << 4;
+    int cr[2];
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const int row = 8 * (2 * c + e) + (lane >> 3);
+      cr[e] = row * ROW_BYTES + 1024 + (((lane & 7) ^ rot_sw(row)) << 4);
+    }
     // Page-table entry of unit u (clamped to the range's last unit, so the
-    // read stays inside the range's pages).  Inside the loop it is read one
-    // step ahead, before the barrier whose wait covers the scalar load, and
-    // range-checked only where the copies use it.
+    // read stays inside the range's pages); read one step ahead in the loop.
     auto page_raw = [&](int u) { return ctable[(tok0 + min(u, U - 1) * UNIT) / BS]; };
     const uint32_t lat_base = (uint32_t)(uintptr_t)&sm.lat[0][0];
     const uint32_t rot_base = (uint32_t)(uintptr_t)&sm.rot[0][0];
     auto issue = [&](int u, int raw) {
       const int blk = clamp_block(raw, p.num_blocks);
-      const uint8_t* src =
-          pool + (size_t)blk * TILE_BYTES + ((tok0 + u * UNIT) % BS) * ROW_BYTES;
+      const uint8_t* src = pool + (size_t)blk * TILE_BYTES + ((tok0 + u * UNIT) % BS) * ROW_BYTES;
       const uint32_t lat = lat_base + (u & 3) * (UNIT * 1024);
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int row = v + 4 * i;
-        copy16_to_lds(src + row * ROW_BYTES, (uint32_t)cl[i & 3], lat + row * 1024);
+      for (int i = 0; i < 16; ++i) {
+        const int row = c + 2 * i;
+        copy16_to_lds(src + row * ROW_BYTES, (uint32_t)cl[i & 7], lat + row * 1024);
       }
-      copy16_to_lds(src, (uint32_t)cr, rot_base + (u % 3) * (UNIT * 128) + v * 1024);
+#pragma unroll
+      for (int e = 0; e < 2; ++e)
+        copy16_to_lds(src, (uint32_t)cr[e],
+                      rot_base + (u % 3) * (UNIT * 128) + (2 * c + e) * 1024);
     };
-    // Rows past the visible length of a partial unit are zeroed once it has
-    // landed: stale contents (possibly NaN) must not reach P.V.
+    // Rows past the visible length of the range's last unit are zeroed once
+    // it has landed and before V is read from it: stale contents (possibly
+    // NaN) must not reach P.V.  The score waves may read those rows
+    // meanwhile; their scores are masked out.
     auto zero_tail = [&](int u) {
       const int valid = unit_valid(u);
+      if (valid >= UNIT) return;
+      const int zt = lane + 64 * c;
       const u32x4 z = {0u, 0u, 0u, 0u};
       u32x4* dl = reinterpret_cast<u32x4*>(sm.lat[u & 3]);
-      for (int q = valid * 64 + tid - 256; q < UNIT * 64; q += 256) dl[q] = z;
+      for (int q = valid * 64 + zt; q < UNIT * 64; q += 128) dl[q] = z;
       u32x4* dr = reinterpret_cast<u32x4*>(sm.rot[u % 3]);
-      for (int q = valid * 8 + tid - 256; q < UNIT * 8; q += 256) dr[q] = z;
+      for (int q = valid * 8 + zt; q < UNIT * 8; q += 128) dr[q] = z;
     };
 
+    // softmax lanes: query row 32c + (l & 31), P k-slots 8h + e (+16ks),
+    // h = l >> 5, e < 8, ks < 2: 16 scores per lane, the other 16 of the row
+    // in lane l ^ 32
+    const int srow = 32 * c + l32;
+    float m_run = -INFINITY;  // reference max (log2 units) of row srow
+    float l_run = 0.0f;       // running sum in that reference
+    const float c_log2 = p.scale_log2;
+    auto softmax = [&](int u) {
+      // Scale and subtract stay separate operations, so the maximal score
+      // gives exactly exp2(0) = 1.
+#pragma clang fp contract(off)
+      float x[2][8];
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        // slot 8h + e of k-step ks holds token 16ks + tok_of(8h + e): token
+        // pairs 16ks + 2h + 4q, +1 give slots e = q and e = q + 4
+        const float* srd = &sm.s[srow * S_LD + 16 * ks + 2 * lhi];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const float2 pr = *reinterpret_cast<const float2*>(srd + 4 * q);
+          x[ks][q] = pr.x * c_log2;
+          x[ks][q + 4] = pr.y * c_log2;
+        }
+      }
+      const int valid = unit_valid(u);
+      if (valid < UNIT) {  // only the range's last unit can be partial
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            if (16 * ks + tok_of(8 * lhi + e) >= valid) x[ks][e] = -INFINITY;
+      }
+      float mx = -INFINITY;
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) mx = fmaxf(mx, x[ks][e]);
+      mx = xor32_max(mx);
+      const bool raise = mx > m_run + kRescaleSlack;  // always on the first unit
+      const float m_new = raise ? mx : m_run;
+      const float alpha = raise ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.0f;
+      m_run = m_new;
+      float sum = 0.0f;
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        u16x8 pb;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float ex = __builtin_amdgcn_exp2f(x[ks][e] - m_new);
+          sum += ex;
+          pb[e] = f32_to_bf16(ex);
+        }
+        *reinterpret_cast<u16x8*>(&sm.p[srow * P_LD + 16 * ks + 8 * lhi]) = pb;
+      }
+      sum = xor32_sum(sum);
+      l_run = l_run * alpha + sum;
+      if (lhi == 0) sm.alpha[srow] = alpha;
+      const bool any_raise = __any(raise);
+      if (lane == 0) sm.flag[c] = any_raise ? 1 : 0;
+    };
+
+    issue(0, page_raw(0));
+    if (U > 1) issue(1, page_raw(1));
+    if (U > 2) issue(2, page_raw(2));
+    int raw_next = page_raw(3);
+    if (U > 2) wait_vmcnt<2 * COPIES>(); else if (U > 1) wait_vmcnt<COPIES>(); else wait_vmcnt<0>();
+    lds_barrier();                         // B0: unit 0 landed
+    zero_tail(0);
+    for (int j = -1; j < U; ++j) {
+      if (j >= 0 && j + 3 < U) {
+        issue(j + 3, raw_next);
+        raw_next = page_raw(j + 4);
+      }
+      if (j + 2 < U) {  // unit j+2 landed: only unit j+3 may still be in flight
+        if (j + 3 < U) wait_vmcnt<COPIES>(); else wait_vmcnt<0>();
+      }
+      lds_barrier();                       // M(j)
+      if (j + 1 < U) softmax(j + 1);
+      if (j + 2 < U) zero_tail(j + 2);
+      lds_barrier();                       // E(j)
+    }
+    if (lhi == 0) {
+      sm.lrow[srow] = l_run;
+      const float lse = (m_run + log2f(l_run)) * kLn2;
+      if (direct) {
+        if (p.lse != nullptr) p.lse[(size_t)b * TH + rb + srow] = lse;
+      } else {
+        p.part_lse[((size_t)b * S + s) * TH + rb + srow] = lse;
+      }
+    }
+    lds_barrier();                         // F
+  } else {
+    // =============================== value waves ===============================
+    // Value wave v owns latent columns 128v .. 128v+127 of O for all 64 rows.
+    const int v = (wave & 1) + 2 * (wave >> 2);
     // Transposing-read offsets of this lane: in 16-lane group gq, lane i points
     // at token 4*(i >> 2) + 2*lhi + sel (+ 16*ks), columns 128v + 32dt + 16*gq
     // + 4*(i & 3); result lane i holds column .. + i for the 4 tokens.
@@ -348,10 +471,10 @@ __global__ __launch_bounds__(NT, 1) void decode_mfma_kernel(const DecodeParams p
     for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
       for (int sel = 0; sel < 2; ++sel) {
-        const int tk = 4 * (i16 >> 2) + 2 * lhi + sel;  // + 16*ks (multiple of 16)
+        const int tkv = 4 * (i16 >> 2) + 2 * lhi + sel;  // + 16*ks (multiple of 16)
         const int col = 128 * v + 32 * dt + 16 * gq + 4 * (i16 & 3);
         const int chunk = col >> 3;
-        voff[dt][sel] = tk * 1024 + ((chunk ^ lat_sw(tk)) << 4) + ((col & 4) << 1);
+        voff[dt][sel] = tkv * 1024 + ((chunk ^ lat_sw(tkv)) << 4) + ((col & 4) << 1);
       }
     const int poff = l32 * P_LD + 8 * lhi;  // bf16 elements
 
@@ -363,39 +486,30 @@ __global__ __launch_bounds__(NT, 1) void decode_mfma_kernel(const DecodeParams p
 #pragma unroll
         for (int r = 0; r < 16; ++r) o[rt][dt][r] = 0.0f;
 
-    // prologue: copies of units 0..2, wait for unit 0, then unit 1
-    issue(0, page_raw(0));
-    if (U > 1) issue(1, page_raw(1));
-    if (U > 2) issue(2, page_raw(2));
-    int raw_next = page_raw(3);
-    if (U > 2) wait_vmcnt<2 * COPIES>(); else if (U > 1) wait_vmcnt<COPIES>(); else wait_vmcnt<0>();
-    lds_barrier();                         // B0
-    if (unit_valid(0) < UNIT) {
-      zero_tail(0);
-      lds_barrier();
-    }
-    if (U > 1) {
-      if (U > 2) wait_vmcnt<COPIES>(); else wait_vmcnt<0>();
-    }
-    lds_barrier();                         // E
-    if (U > 1 && unit_valid(1) < UNIT) {
-      zero_tail(1);
-      lds_barrier();
-    }
-
-    for (int j = 0; j < U; ++j) {
-      const bool ahead = j + 3 < U;
-      if (ahead) issue(j + 3, raw_next);
+    bf16x8 pf[2][2], vf[2][4];
+    // P(j), the rescale flags and V(j) into registers, rescale O if a row of
+    // unit j raised its reference max, and the MFMAs of k-step 0.
+    auto pv_first = [&](int j) {
       const uint8_t* lat = sm.lat[j & 3];
-      const uint16_t* pp = sm.p[j & 1];
-      const int4 fl = *reinterpret_cast<const int4*>(sm.flag[j & 1]);
-      if (fl.x | fl.y | fl.z | fl.w) {
+      const int2 fl = *reinterpret_cast<const int2*>(sm.flag);
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        pf[ks][0] = *reinterpret_cast<const bf16x8*>(sm.p + poff + 16 * ks);
+        pf[ks][1] = *reinterpret_cast<const bf16x8*>(sm.p + 32 * P_LD + poff + 16 * ks);
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt) {
+          const s16x4 v0 = lds_tr16(lat + voff[dt][0] + 16 * ks * 1024);
+          const s16x4 v1 = lds_tr16(lat + voff[dt][1] + 16 * ks * 1024);
+          const short vv[8] = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
+          vf[ks][dt] = __builtin_bit_cast(bf16x8, vv);
+        }
+      }
+      if (fl.x | fl.y) {
 #pragma unroll
         for (int rt = 0; rt < 2; ++rt) {
 #pragma unroll
           for (int r4 = 0; r4 < 4; ++r4) {
-            const float4 al =
-                *reinterpret_cast<const float4*>(&sm.alpha[j & 1][32 * rt + 8 * r4 + 4 * lhi]);
+            const float4 al = *reinterpret_cast<const float4*>(&sm.alpha[32 * rt + 8 * r4 + 4 * lhi]);
 #pragma unroll
             for (int dt = 0; dt < 4; ++dt) {
               o[rt][dt][4 * r4 + 0] *= al.x;
@@ -407,28 +521,25 @@ __global__ __launch_bounds__(NT, 1) void decode_mfma_kernel(const DecodeParams p
         }
       }
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        const bf16x8 pf0 = *reinterpret_cast<const bf16x8*>(pp + poff + 16 * ks);
-        const bf16x8 pf1 = *reinterpret_cast<const bf16x8*>(pp + 32 * P_LD + poff + 16 * ks);
+      for (int dt = 0; dt < 4; ++dt) {
+        o[0][dt] = mfma32(pf[0][0], vf[0][dt], o[0][dt]);
+        o[1][dt] = mfma32(pf[0][1], vf[0][dt], o[1][dt]);
+      }
+    };
+    auto pv_second = [&]() {
 #pragma unroll
-        for (int dt = 0; dt < 4; ++dt) {
-          const s16x4 v0 = lds_tr16(lat + voff[dt][0] + 16 * ks * 1024);
-          const s16x4 v1 = lds_tr16(lat + voff[dt][1] + 16 * ks * 1024);
-          const short vv[8] = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
-          const bf16x8 vf = __builtin_bit_cast(bf16x8, vv);
-          o[0][dt] = mfma32(pf0, vf, o[0][dt]);
-          o[1][dt] = mfma32(pf1, vf, o[1][dt]);
-        }
+      for (int dt = 0; dt < 4; ++dt) {
+        o[0][dt] = mfma32(pf[1][0], vf[1][dt], o[0][dt]);
+        o[1][dt] = mfma32(pf[1][1], vf[1][dt], o[1][dt]);
       }
-      raw_next = page_raw(j + 4);
-      if (j + 2 < U) {
-        if (ahead) wait_vmcnt<COPIES>(); else wait_vmcnt<0>();
-      }
-      lds_barrier();                       // E
-      if (j + 2 < U && unit_valid(j + 2) < UNIT) {
-        zero_tail(j + 2);
-        lds_barrier();
-      }
+    };
+
+    lds_barrier();                         // B0
+    for (int j = -1; j < U; ++j) {
+      if (j >= 0) pv_first(j);
+      lds_barrier();                       // M(j)
+      if (j >= 0) pv_second();
+      lds_barrier();                       // E(j)
     }
 
     lds_barrier();                         // F

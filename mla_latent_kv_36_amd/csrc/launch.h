@@ -22,7 +22,7 @@ struct DecodeParams {
   int cap;                    // host bound on rows attended per sequence
   int causal;
   int num_splits;             // S
-  int chunk_pages;            // pages per split
+  int chunk_rows;             // cache rows per split (a multiple of the kernel granule)
   float scale_log2;           // softmax scale * log2(e)
 };
 

@@ -92,22 +92,24 @@ def test_workspace_and_split_plan(lib):
     cfg = v3_cfg()
     # one split needs no workspace
     assert mla.mla_decode_workspace_size(cfg, 16, 1, 4097, 0, 1) == 0
-    # S splits of B x T x H rows: d_c floats + one lse each, both rounded up to 256 B
+    # S splits of B x T x H rows: d_c floats + one lse each, both rounded up to
+    # 256 B.  The MFMA kernel splits the longest sequence into ranges of whole
+    # 32-row units, so S is first reduced to the number of ranges that cover it.
     for B, T, cap, S in [(16, 1, 4097, 8), (4, 1, 131073, 64), (32, 4, 8196, 3)]:
-        pages = -(-cap // 64)
-        chunk = -(-pages // S)
-        s_eff = -(-pages // chunk)
+        units = -(-cap // 32)
+        chunk = -(-units // S)
+        s_eff = -(-units // chunk)
         rows = B * s_eff * T * 128
         r256 = lambda x: -(-x // 256) * 256
         want = r256(rows * 512 * 4) + r256(rows * 4)
         assert mla.mla_decode_workspace_size(cfg, B, T, cap, 0, S) == want
     # the library's own choice is a valid split count and sized consistently
     s = mla.mla_decode_num_splits(cfg, 16, 1, 4097, 0)
-    assert 1 <= s <= 65
+    assert 1 <= s <= 129
     assert mla.mla_decode_workspace_size(cfg, 16, 1, 4097, 0, 0) == \
         mla.mla_decode_workspace_size(cfg, 16, 1, 4097, 0, s)
-    # more splits than pages collapse to one split per page
-    assert mla.mla_decode_workspace_size(cfg, 1, 1, 64, 0, 8) == 0
+    # more splits than 32-row units collapse to one split per unit
+    assert mla.mla_decode_workspace_size(cfg, 1, 1, 32, 0, 8) == 0
     with pytest.raises(RuntimeError):
         mla.mla_decode_workspace_size(v3_cfg(d_c=0), 1, 1, 64)
 
