@@ -139,10 +139,7 @@ __global__ __launch_bounds__(NT) void decode_generic_kernel(const DecodeParams p
 // rows of this query are read (the same row arithmetic as the split
 // kernels), in split order, so the result is deterministic.  One wave per
 // query row; each lane owns 4 consecutive latent columns per 256-column block.
-// For up to CMB_FAST splits and d_c <= 512 every partial load of a lane is
-// issued before the first one is used.
 constexpr int CMB_ROWS = 4;   // query rows (waves) per workgroup
-constexpr int CMB_FAST = 16;  // splits merged with all loads in flight
 
 __global__ __launch_bounds__(64 * CMB_ROWS) void combine_kernel(const DecodeParams p) {
   const int TH = p.T * p.H;
@@ -171,31 +168,27 @@ __global__ __launch_bounds__(64 * CMB_ROWS) void combine_kernel(const DecodePara
   for (int s = 0; s < ns; ++s) den += exp2f((lse_b[(size_t)s * TH] - M) * kLog2e);
   const float inv = 1.0f / den;
 
-  if ((p.d_c & 255) == 0 && p.d_c <= 512 && ns <= CMB_FAST) {
-    const int nblk = p.d_c >> 8;  // 1 or 2 blocks of 256 columns
-    f32x4 v[CMB_FAST][2];
+  if ((p.d_c & 3) == 0) {
+    for (int d = 4 * lane; d < p.d_c; d += 256) {
+      f32x4 a = {0.f, 0.f, 0.f, 0.f};
+      int s = 0;
+      for (; s + 4 <= ns; s += 4) {  // four splits' loads in flight at a time
+        f32x4 v[4];
+        float w[4];
 #pragma unroll
-    for (int s = 0; s < CMB_FAST; ++s) {
-      if (s < ns) {
+        for (int k = 0; k < 4; ++k) {
+          v[k] = *reinterpret_cast<const f32x4*>(po_b + (size_t)(s + k) * sstride + d);
+          w[k] = exp2f((lse_b[(size_t)(s + k) * TH] - M) * kLog2e);
+        }
 #pragma unroll
-        for (int k = 0; k < 2; ++k)
-          if (k < nblk)
-            v[s][k] = *reinterpret_cast<const f32x4*>(po_b + (size_t)s * sstride + 256 * k + 4 * lane);
+        for (int k = 0; k < 4; ++k) a += w[k] * v[k];
       }
-    }
-    f32x4 a[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
-#pragma unroll
-    for (int s = 0; s < CMB_FAST; ++s) {
-      if (s < ns) {
-        const float w = exp2f((lse_b[(size_t)s * TH] - M) * kLog2e);
-#pragma unroll
-        for (int k = 0; k < 2; ++k)
-          if (k < nblk) a[k] += w * v[s][k];
+      for (; s < ns; ++s) {
+        const f32x4 v = *reinterpret_cast<const f32x4*>(po_b + (size_t)s * sstride + d);
+        a += exp2f((lse_b[(size_t)s * TH] - M) * kLog2e) * v;
       }
+      *reinterpret_cast<f32x4*>(out + d) = a * inv;
     }
-#pragma unroll
-    for (int k = 0; k < 2; ++k)
-      if (k < nblk) *reinterpret_cast<f32x4*>(out + 256 * k + 4 * lane) = a[k] * inv;
   } else {
     for (int d = lane; d < p.d_c; d += 64) {
       float a = 0.0f;
