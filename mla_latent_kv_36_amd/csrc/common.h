@@ -45,9 +45,18 @@ template <> struct Elem<uint16_t> {
 // Reductions across lane l and lane l ^ 32 (or l ^ 16) on the VALU with the
 // gfx950 lane-swap instructions: each lane gets back {x[l], x[l ^ 32]} (resp.
 // {x[l], x[l ^ 16]}), so a symmetric operation of the pair is the reduction.
+// Maximum of two floats as one v_max_f32.  fmaxf on values that arrive as
+// bit patterns (the lane swaps below) makes the compiler quieten possible
+// signalling NaNs first (two extra instructions); the reductions here only
+// see scores, -inf or quiet NaN, for which the plain instruction is exact.
+__device__ __forceinline__ float vmax(float a, float b) {
+  float r;
+  asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+  return r;
+}
 __device__ __forceinline__ float xor32_max(float x) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  return vmax(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 __device__ __forceinline__ float xor32_sum(float x) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
@@ -55,7 +64,7 @@ __device__ __forceinline__ float xor32_sum(float x) {
 }
 __device__ __forceinline__ float xor16_max(float x) {
   const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  return vmax(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 __device__ __forceinline__ float xor16_sum(float x) {
   const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);

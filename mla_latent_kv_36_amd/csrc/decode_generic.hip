@@ -139,6 +139,8 @@ __global__ __launch_bounds__(NT) void decode_generic_kernel(const DecodeParams p
 // rows of this query are read (the same row arithmetic as the split
 // kernels), in split order, so the result is deterministic.  One wave per
 // query row; each lane owns 4 consecutive latent columns per 256-column block.
+// The merge streams the partials once, so the loads of a row are issued
+// together, as many as fit, rather than one split at a time.
 constexpr int CMB_ROWS = 4;   // query rows (waves) per workgroup
 
 __global__ __launch_bounds__(64 * CMB_ROWS) void combine_kernel(const DecodeParams p) {
@@ -150,8 +152,63 @@ __global__ __launch_bounds__(64 * CMB_ROWS) void combine_kernel(const DecodePara
   const int b = (int)(row / TH);
   const int rr = (int)(row - (long long)b * TH);
   const int t = rr / p.H;
+  if (p.num_splits <= 8 && p.d_c == 512) {
+    // The common shape in one memory round trip: the sequence length, every
+    // split's log-sum-exp (lane s) and every split's partial row (8 columns
+    // per lane) are read before any of them is used.  Splits that hold no row
+    // of this query were never written; they are left out by selection, not
+    // by a zero weight, since their memory may hold anything.
+    const int S = p.num_splits;
+    const float* lse_b = p.part_lse + (size_t)b * S * TH + rr;
+    const float* po_b = p.part_o + ((size_t)b * S * TH + rr) * 512 + 4 * lane;
+    const size_t sstride = (size_t)TH * 512;
+    const int len = p.seq_lens[b];
+    const float lse_l = lse_b[(size_t)min(lane, S - 1) * TH];
+    f32x4 v0[8], v1[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const float* src = po_b + (size_t)min(k, S - 1) * sstride;
+      v0[k] = *reinterpret_cast<const f32x4*>(src);
+      v1[k] = *reinterpret_cast<const f32x4*>(src + 256);
+    }
+    // every value above is consumed here, so all 18 loads are issued before
+    // the first wait (the compiler would otherwise interleave waits and loads)
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("" ::"v"(len), "v"(lse_l));
+#pragma unroll
+    for (int k = 0; k < 8; ++k) asm volatile("" ::"v"(v0[k]), "v"(v1[k]));
+    const int n_valid = visible_rows(len, p.T, t, p.causal, p.cap);
+    const int ns = __builtin_amdgcn_readfirstlane(
+        min(S, (n_valid + p.chunk_rows - 1) / p.chunk_rows));
+    // no branches from here on: a branch would let the compiler move the
+    // loads above behind it, one dependent round trip at a time
+    float M = lane < ns ? lse_l : -INFINITY;
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
+    const float e = lane < ns ? exp2f((lse_l - M) * kLog2e) : 0.0f;
+    float den = e;
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) den += __shfl_xor(den, off);
+    f32x4 a0 = {0.f, 0.f, 0.f, 0.f}, a1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const float w = __shfl(e, k);
+      const f32x4 t0 = a0 + w * v0[k], t1 = a1 + w * v1[k];
+      a0 = k < ns ? t0 : a0;
+      a1 = k < ns ? t1 : a1;
+    }
+    // no visible row (ns == 0): o = 0, lse = -inf
+    const float inv = ns > 0 ? 1.0f / den : 0.0f;
+    float* out = p.o_lat + (size_t)row * 512 + 4 * lane;
+    *reinterpret_cast<f32x4*>(out) = a0 * inv;
+    *reinterpret_cast<f32x4*>(out + 256) = a1 * inv;
+    if (lane == 0 && p.lse != nullptr) p.lse[row] = ns > 0 ? M + logf(den) : -INFINITY;
+    return;
+  }
   const int n_valid = visible_rows(p.seq_lens[b], p.T, t, p.causal, p.cap);
-  const int ns = min(p.num_splits, (n_valid + p.chunk_rows - 1) / p.chunk_rows);
+  // one row per wave: the split count is the same in every lane
+  const int ns = __builtin_amdgcn_readfirstlane(
+      min(p.num_splits, (n_valid + p.chunk_rows - 1) / p.chunk_rows));
   float* out = p.o_lat + (size_t)row * p.d_c;
   const float* lse_b = p.part_lse + (size_t)b * p.num_splits * TH + rr;
   const float* po_b = p.part_o + ((size_t)b * p.num_splits * TH + rr) * p.d_c;
@@ -162,13 +219,53 @@ __global__ __launch_bounds__(64 * CMB_ROWS) void combine_kernel(const DecodePara
     if (lane == 0 && p.lse != nullptr) p.lse[row] = -INFINITY;
     return;
   }
+  // split s's log-sum-exp is read by lane s % 64 (all loads of a pass in
+  // flight at once), then reduced across the wave in a fixed order
   float M = -INFINITY;
-  for (int s = 0; s < ns; ++s) M = fmaxf(M, lse_b[(size_t)s * TH]);
+  for (int c = 0; c < ns; c += 64)
+    if (c + lane < ns) M = fmaxf(M, lse_b[(size_t)(c + lane) * TH]);
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
   float den = 0.0f;
-  for (int s = 0; s < ns; ++s) den += exp2f((lse_b[(size_t)s * TH] - M) * kLog2e);
+  for (int c = 0; c < ns; c += 64)
+    if (c + lane < ns) den += exp2f((lse_b[(size_t)(c + lane) * TH] - M) * kLog2e);
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) den += __shfl_xor(den, off);
   const float inv = 1.0f / den;
 
-  if ((p.d_c & 3) == 0) {
+  if ((p.d_c & 511) == 0) {
+    // 512 columns per pass, 8 per lane; the loads of up to 8 splits (16 x 16 B
+    // per lane) are all issued before the first is used, so that enough bytes
+    // are in flight to stream the partials at memory speed
+    for (int d0 = 0; d0 < p.d_c; d0 += 512) {
+      const int da = d0 + 4 * lane;
+      f32x4 a0 = {0.f, 0.f, 0.f, 0.f}, a1 = {0.f, 0.f, 0.f, 0.f};
+      for (int s0 = 0; s0 < ns; s0 += 8) {
+        // splits past the last one re-read the last one with weight 0, so
+        // that every load is unconditional
+        float w[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          const float e = exp2f((lse_b[(size_t)min(s0 + k, ns - 1) * TH] - M) * kLog2e);
+          w[k] = s0 + k < ns ? e : 0.0f;
+        }
+        f32x4 v0[8], v1[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          const float* src = po_b + (size_t)min(s0 + k, ns - 1) * sstride + da;
+          v0[k] = *reinterpret_cast<const f32x4*>(src);
+          v1[k] = *reinterpret_cast<const f32x4*>(src + 256);
+        }
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          a0 += w[k] * v0[k];
+          a1 += w[k] * v1[k];
+        }
+      }
+      *reinterpret_cast<f32x4*>(out + da) = a0 * inv;
+      *reinterpret_cast<f32x4*>(out + da + 256) = a1 * inv;
+    }
+  } else if ((p.d_c & 3) == 0) {
     for (int d = 4 * lane; d < p.d_c; d += 256) {
       f32x4 a = {0.f, 0.f, 0.f, 0.f};
       int s = 0;

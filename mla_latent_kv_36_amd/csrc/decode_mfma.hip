@@ -1,45 +1,47 @@
 // Split-KV latent-attention decode for the DeepSeek shape on CDNA4 (gfx950).
 //
 // One workgroup = 64 query rows (64 heads of one new token) x one contiguous
-// range of 64-token cache pages of one sequence.  The range is processed in
-// 32-token units (half pages, 36 KiB contiguous in HBM) through a software
-// pipeline in which three things overlap in every step j:
-//   * copies: unit j+3 is copied into LDS with 128-bit direct-to-LDS loads;
-//   * scores: unit j+1 is scored, S^T = K . Q^T on MFMA over all 576 columns --
-//     the content term (first 512) and the rotary term (last 64) are one dot
-//     product ("Attention, Part 2: MQA, GQA and MLA", the absorbed path adds the
-//     two terms before scaling) -- followed by the online softmax in the log2
-//     domain, which writes P (bf16) for the unit;
+// range of cache rows of one sequence.  The range is processed in 32-token
+// units (half pages, 36 KiB contiguous in HBM) through a software pipeline
+// with one workgroup barrier per step; in step j:
+//   * copies: unit j+4 is issued into LDS with 128-bit direct-to-LDS loads
+//     (latent columns only) and unit j+3 is waited for;
+//   * scores: unit j+2 is scored, S^T = K . Q^T on MFMA over all 576 columns
+//     -- the content term (first 512) and the rotary term (last 64) are one
+//     dot product ("Attention, Part 2: MQA, GQA and MLA", the absorbed path
+//     adds the two terms before scaling); the raw scores go to LDS;
+//   * softmax: unit j+1, online, in the log2 domain, writing P (bf16) and the
+//     rows' rescale factors;
 //   * values: O += P . V for unit j, V being the first 512 columns of the SAME
 //     LDS rows ("How DeepSeek Rewrote the Transformer", section "Absorbed
 //     projections", point 3), with O in registers for the whole range.
-// One workgroup barrier per step hands P of unit j+1 and the LDS slots over.
 // The range's result is written normalised with its log-sum-exp, as the final
 // output (one split) or as a partial for the log-sum-exp merge.
 //
-// Waves (8, two per SIMD) have fixed roles and separate loops that meet at the
-// same barriers:
-//   score waves 0..3: wave w owns query rows 16w..16w+15 outright: their
-//     absorbed queries sit in registers (72 VGPRs, the B operand of
-//     v_mfma_f32_16x16x32_bf16), the wave scores all 32 tokens of a unit and
-//     runs the softmax of its rows with no other wave involved;
-//   value waves 4..7: wave 4+v owns latent columns 128v..128v+127 of O for all
-//     64 rows (128 VGPRs, v_mfma_f32_32x32x16_bf16), issues the copies, and
-//     reads V with the transposing LDS read (ds_read_b64_tr_b16), 4 tokens x
-//     16 columns per 16-lane group.
+// Waves (8; wave w and wave w + 4 share a SIMD) have fixed roles and separate
+// loops that meet at the same barriers:
+//   score waves 0, 1: wave w holds the absorbed queries of rows 32w..32w+31 in
+//     registers (144 VGPRs, the B operand of v_mfma_f32_16x16x32_bf16), reads
+//     K fragments from LDS, and reads the unit's rotary key columns straight
+//     from memory into registers one unit ahead;
+//   copy waves 4, 5 (on the score waves' SIMDs): the copies;
+//   value waves 2, 3, 6, 7: wave v owns latent columns 128v..128v+127 of O for
+//     all 64 rows (128 VGPRs, v_mfma_f32_32x32x16_bf16), reads V with the
+//     transposing LDS read (ds_read_b64_tr_b16), and runs the softmax of rows
+//     16v..16v+15.  The two value waves of a SIMD take softmax and P.V in
+//     opposite orders, so that one's VALU work meets the other's MFMAs.
 // A row's reference maximum is only raised when a unit's maximum exceeds it by
 // more than 2^8, so the accumulator rescale is skipped on almost every unit;
 // probabilities then stay below 2^8, which bf16 and the fp32 sums carry with
 // unchanged relative precision.
 //
-// LDS: a ring of 4 latent slots (32 rows x 1 KiB: the c part of a unit), 3
-// rotary slots (32 rows x 128 B: the k^R part), P double-buffered by unit
-// parity, and the per-row rescale factors.  16-byte chunk c of latent row t
-// sits at chunk position c ^ (t & 15) of its row, and of rotary row t at
-// c ^ ((t >> 1) & 7).  With these placements the 128-bit score reads (16 rows
-// at one chunk) are free of bank conflicts, and so are the transposing reads
-// provided the 4 rows of each 16-lane group lie 4 tokens apart: the values
-// MFMA therefore walks each 16-token k-step in the order
+// LDS: a ring of 4 latent slots (32 rows x 1 KiB: the c part of a unit), raw
+// scores and P double-buffered by unit parity, and the per-row rescale
+// factors.  16-byte chunk c of latent row t sits at chunk position c ^ (t & 15)
+// of its row.  With this placement the 128-bit score reads (16 rows at one
+// chunk) are free of bank conflicts, and so are the transposing reads provided
+// the 4 rows of each 16-lane group lie 4 tokens apart: the values MFMA
+// therefore walks each 16-token k-step in the order
 // token(lhi, e) = 4*(e & 3) + 2*lhi + (e >> 2) for k-slot 8*lhi + e, and P is
 // written in that order (the sum over tokens does not depend on it).  Layouts
 // were chosen by measuring SQ_LDS_BANK_CONFLICT on gfx950.
@@ -61,27 +63,23 @@ constexpr int NT = 512;                     // threads per workgroup
 constexpr int ROW_BYTES = W * 2;            // 1152
 constexpr int TILE_BYTES = BS * ROW_BYTES;  // 73728 per page in HBM
 constexpr int LAT_SLOTS = 4;
-constexpr int ROT_SLOTS = 3;
 constexpr int P_LD = 40;                    // bf16 per row of a P tile (32 + pad)
+constexpr int S_LD = 36;                    // floats per row of a score tile (32 + pad)
 constexpr int QSTEPS = W / 32;              // 18 k-steps of 32 columns (score MFMA)
-constexpr int COPIES = 18;                  // direct-to-LDS copies per copy wave per unit
+constexpr int LSTEPS = DC / 32;             // 16 of them over the latent columns
+constexpr int COPIES = 16;                  // direct-to-LDS copies per copy wave per unit
 constexpr float kRescaleSlack = 8.0f;       // log2 units
 
-constexpr int S_LD = 36;                    // floats per row of the score tile (32 + pad)
-constexpr int A_SPLIT = 9;                  // score k-steps of unit j+2 run between M(j) and E(j)
-
 struct __align__(16) Smem {
-  uint8_t lat[LAT_SLOTS][UNIT * 1024];
-  uint8_t rot[ROT_SLOTS][UNIT * 128];
-  float s[ROWS * S_LD];        // raw scores of one unit, [row][token]
-  uint16_t p[ROWS * P_LD];     // probabilities of one unit (bf16), [row][k-slot]
-  float alpha[ROWS];           // per-row rescale factor of that unit
+  uint8_t lat[LAT_SLOTS][UNIT * 1024];  // latent columns of 4 units (32 rows x 1 KiB)
+  float s[2][ROWS * S_LD];     // raw scores by unit parity, [row][token]
+  uint16_t p[2][ROWS * P_LD];  // probabilities (bf16) by unit parity, [row][k-slot]
+  float alpha[2][ROWS];        // per-row rescale factor, by unit parity
   float lrow[ROWS];
-  int flag[2];                 // [copy wave]: some row of its 32 raised its max
+  int flag[2][4];              // [unit parity][row group]: some row of its 16 raised its max
 };
 
 __device__ __forceinline__ int lat_sw(int t) { return t & 15; }
-__device__ __forceinline__ int rot_sw(int t) { return (t >> 1) & 7; }
 
 // Token (within a 16-token k-step of P.V) held at P k-slot m, 0 <= m < 16.
 // The value waves' transposing reads take the 4 tokens of a slot quad 4
@@ -129,14 +127,21 @@ __device__ __forceinline__ void lds_barrier() {
 // the slot to the readers.  The copy has no result register; its address
 // operands are read at issue.  On gfx9 a copy that reads M0 needs one wait
 // state after M0 is written (the s_nop).
+// gbase and lds are the same in every lane; they are moved to scalar
+// registers explicitly so that the constraints hold whatever the compiler
+// concludes about their uniformity.
 __device__ __forceinline__ void copy16_to_lds(const uint8_t* gbase, uint32_t voff,
                                               uint32_t lds) {
+  const uint64_t g = (uint64_t)(uintptr_t)gbase;
+  const uint32_t glo = __builtin_amdgcn_readfirstlane((uint32_t)g);
+  const uint32_t ghi = __builtin_amdgcn_readfirstlane((uint32_t)(g >> 32));
+  const uint8_t* gs = (const uint8_t*)(uintptr_t)(((uint64_t)ghi << 32) | glo);
   asm volatile(
       "s_mov_b32 m0, %0\n\t"
       "s_nop 0\n\t"
       "global_load_lds_dwordx4 %1, %2"
       :
-      : "s"(lds), "v"(voff), "s"(gbase)
+      : "s"(__builtin_amdgcn_readfirstlane(lds)), "v"(voff), "s"(gs)
       : "memory");
 }
 
@@ -146,6 +151,75 @@ __device__ __forceinline__ void wait_vmcnt() {
   // vmcnt bits [3:0] and [15:14], expcnt [6:4], lgkmcnt [11:8].
   static_assert(N >= 0 && N < 64, "vmcnt");
   __builtin_amdgcn_s_waitcnt((N & 15) | (((N >> 4) & 3) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+// Online softmax of one 16-row group of a unit, in the log2 domain: raw
+// scores sm.s -> probabilities sm.p (bf16, in the k-slot order of P.V), the
+// rows' rescale factors and the group's rescale flag.  Lane l takes row
+// 16 grp + (l & 15) and P k-slots 8 g8 .. +7 (g8 = l >> 4: k-step g8 >> 1,
+// half g8 & 1); the other 24 scores of the row are in lanes l ^ 16, l ^ 32,
+// l ^ 48.  m_run is the row's reference maximum, l_run the sum in that
+// reference.
+__device__ __forceinline__ void softmax_unit(Smem& sm, int u, int valid, int grp, int lane,
+                                             float c_log2, float& m_run, float& l_run) {
+  // Scale and subtract stay separate operations, so the maximal score gives
+  // exactly exp2(0) = 1.
+#pragma clang fp contract(off)
+  const int i16 = lane & 15;
+  const int g8 = lane >> 4;
+  const int srow = 16 * grp + i16;
+  // k-slot 8h + e of k-step ks holds token 16ks + tok_of(8h + e): token pairs
+  // 16ks + 2h + 4q, +1 give slots e = q and e = q + 4
+  const float* srd = &sm.s[u & 1][srow * S_LD + 16 * (g8 >> 1) + 2 * (g8 & 1)];
+  float x[8];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const float2 pr = *reinterpret_cast<const float2*>(srd + 4 * q);
+    x[q] = pr.x * c_log2;
+    x[q + 4] = pr.y * c_log2;
+  }
+  if (valid < UNIT) {  // only the range's last unit can be partial
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+      if (16 * (g8 >> 1) + tok_of(8 * (g8 & 1) + e) >= valid) x[e] = -INFINITY;
+  }
+  float mx = vmax(vmax(vmax(x[0], x[1]), vmax(x[2], x[3])),
+                  vmax(vmax(x[4], x[5]), vmax(x[6], x[7])));
+  mx = xor32_max(xor16_max(mx));
+  const bool raise = mx > m_run + kRescaleSlack;  // always on the first unit
+  const float m_new = raise ? mx : m_run;
+  const float alpha = raise ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.0f;
+  m_run = m_new;
+  float ex[8];
+  u16x8 pb;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    ex[e] = __builtin_amdgcn_exp2f(x[e] - m_new);
+    pb[e] = f32_to_bf16(ex[e]);
+  }
+  float sum = ((ex[0] + ex[1]) + (ex[2] + ex[3])) + ((ex[4] + ex[5]) + (ex[6] + ex[7]));
+  *reinterpret_cast<u16x8*>(&sm.p[u & 1][srow * P_LD + 8 * g8]) = pb;
+  sum = xor32_sum(xor16_sum(sum));
+  l_run = l_run * alpha + sum;
+  if (g8 == 0) sm.alpha[u & 1][srow] = alpha;
+  const bool any_raise = __any(raise);
+  if (lane == 0) sm.flag[u & 1][grp] = any_raise ? 1 : 0;
+}
+
+// After the last unit: the group's row sums for the normalisation, and the
+// rows' log-sum-exp (natural log) to the output or to the split's partial.
+__device__ __forceinline__ void softmax_finish(Smem& sm, const DecodeParams& p, int grp, int lane,
+                                               float m_run, float l_run, bool direct, int b, int s,
+                                               int TH, int rb) {
+  if ((lane >> 4) != 0) return;
+  const int srow = 16 * grp + (lane & 15);
+  sm.lrow[srow] = l_run;
+  const float lse = (m_run + log2f(l_run)) * kLn2;
+  if (direct) {
+    if (p.lse != nullptr) p.lse[(size_t)b * TH + rb + srow] = lse;
+  } else {
+    p.part_lse[((size_t)b * p.num_splits + s) * TH + rb + srow] = lse;
+  }
 }
 
 __global__ __launch_bounds__(NT, 1) void decode_mfma_kernel(const DecodeParams p) {
@@ -185,7 +259,10 @@ __global__ __launch_bounds__(NT, 1) void decode_mfma_kernel(const DecodeParams p
   const int TH = p.T * p.H;
   const int rb = g * ROWS;  // first query row (t*H + h) of the group
   const int t = rb / p.H;
-  const int n_valid = visible_rows(p.seq_lens[b], p.T, t, p.causal, p.cap);
+  // the same for the whole workgroup: kept in scalar registers, so that the
+  // range bounds, loop counts and page addresses below are scalar as well
+  const int n_valid =
+      __builtin_amdgcn_readfirstlane(visible_rows(p.seq_lens[b], p.T, t, p.causal, p.cap));
   // this range: cache rows tok0 .. tok_end-1 (tok0 is a multiple of UNIT)
   const int tok0 = s * p.chunk_rows;
   const int tok_end = min(tok0 + p.chunk_rows, n_valid);
@@ -203,17 +280,18 @@ __global__ __launch_bounds__(NT, 1) void decode_mfma_kernel(const DecodeParams p
   const int U = (tok_end - tok0 + UNIT - 1) / UNIT;
   auto unit_valid = [&](int u) { return min(UNIT, tok_end - tok0 - u * UNIT); };
 
-  // Two barriers per unit.  Barrier schedule, the same for every wave: B0,
-  // then M(j) and E(j) for j = -1 .. U-1, then F.
-  //   E(j-1) .. M(j): score waves finish the scores of unit j+1 and store them
-  //     raw (fp32) in sm.s; value waves read P(j) and V(j) into registers and
-  //     start O += P(j) V(j); copy waves issue the copies of unit j+3 and
-  //     wait for unit j+2.
-  //   M(j) .. E(j): copy waves turn sm.s into P(j+1) (softmax, 32 rows each),
-  //     on the same SIMDs where the score waves start on unit j+2, so that
-  //     VALU and MFMA work overlap there; value waves finish O += P(j) V(j).
-  // Each of sm.s, sm.p and sm.alpha is written in one phase and read in the
-  // other, so one buffer of each suffices.
+  // One barrier per unit.  Barrier schedule, the same for every wave: B0, then
+  // E(j) for j = -2 .. U-1, then F.  In step j (between E(j-1) and E(j)):
+  //   score waves: raw scores of unit j+2 (fp32) into sm.s[(j+2) & 1];
+  //   value waves: softmax of unit j+1 for their 16 rows (sm.s -> sm.p) and
+  //                O += P(j) V(j), in the order of the wave, and V(j+1) into
+  //                registers after the MFMAs;
+  //   copy waves:  copies of unit j+4 issued, unit j+3 waited for, the stale
+  //                tail of the range's last unit zeroed.
+  // Latent slot u & 3 is read in step u-2 (K) and u-1 (V into registers), so
+  // the 4 slots hold units j+1 .. j+4 and keep two units of copies in flight.
+  // The rotary key columns (64 per row) are not staged: the score waves read
+  // them from memory into registers one unit ahead.
   if (wave < 2) {
     // =============================== score waves ===============================
     // Wave w owns query rows 32w .. 32w+31 as two 16-row tiles rt.  S^T = K . Q^T
@@ -235,40 +313,73 @@ __global__ __launch_bounds__(NT, 1) void decode_mfma_kernel(const DecodeParams p
       for (int kk = 0; kk < QSTEPS; ++kk)
         qf[rt][kk] = *reinterpret_cast<const bf16x8*>(q + 32 * kk);
     }
-    // K fragment offsets: latent chunk c = 4kk + g4 of token n16 sits at chunk
-    // position c ^ lat_sw(n16) (only the low 4 bits of c take part), rotary
-    // chunk c = 4(kk - 16) + g4 at c ^ rot_sw(n16); token tile ti adds 16 KiB
-    // (latent) or 2 KiB (rotary).
+    // latent chunk c = 4kk + g4 of token n16 sits at chunk position
+    // c ^ lat_sw(n16) (only the low 4 bits of c take part); token tile ti adds
+    // 16 KiB
     int loff[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) loff[j] = n16 * 1024 + (((4 * j + g4) ^ lat_sw(n16)) << 4);
-    int roff[2];
-#pragma unroll
-    for (int j = 0; j < 2; ++j) roff[j] = n16 * 128 + (((4 * j + g4) ^ rot_sw(n16)) << 4);
+    const int32_t __attribute__((address_space(4)))* ctable =
+        (const int32_t __attribute__((address_space(4)))*)(p.block_table + (size_t)b * p.max_blocks);
+    const uint16_t* pool = static_cast<const uint16_t*>(p.pool);
 
-    f32x4 acc[2][2];  // [rt][ti], carried from the first k-steps to the rest
-    auto kfrag = [&](int u, int kk, int ti) {
-      const uint8_t* a = kk < 16 ? sm.lat[u & 3] + loff[kk & 3] + ti * 16 * 1024 + ((kk >> 2) << 8)
-                                 : sm.rot[u % 3] + roff[kk - 16] + ti * 16 * 128;
-      return *reinterpret_cast<const bf16x8*>(a);
+    // Page-table entry of unit u (clamped to the range's last unit), read one
+    // unit before its rotary keys so that the scalar load is not waited for.
+    auto page_raw = [&](int u) { return ctable[(tok0 + min(u, U - 1) * UNIT) / BS]; };
+    // rotary columns 512 + 32(kk-16) + 8*g4 .. +7 of token 16ti + n16 of unit
+    // u (page-table entry raw), from memory (a unit lies within one page), as
+    // kr[kk - 16][ti]
+    auto load_kr = [&](int u, int raw, bf16x8 (&kr)[2][2]) {
+      const int tok = tok0 + u * UNIT;
+      const int blk = clamp_block(raw, p.num_blocks);
+      const uint16_t* rrow = pool + ((size_t)blk * BS + tok % BS + n16) * W + DC + 8 * g4;
+#pragma unroll
+      for (int k2 = 0; k2 < 2; ++k2)
+#pragma unroll
+        for (int ti = 0; ti < 2; ++ti)
+          kr[k2][ti] = *reinterpret_cast<const bf16x8*>(rrow + ti * 16 * W + 32 * k2);
     };
-    // k-steps [KB, KE) of unit u, fragments read KDEPTH k-steps ahead
-    auto steps = [&](int u, auto kb_tag, auto ke_tag) {
-      constexpr int KB = decltype(kb_tag)::value, KE = decltype(ke_tag)::value;
+
+    // scores of unit u with its rotary keys in kr; the next unit's rotary keys
+    // are read into krn first
+    int raw_next;  // page-table entry of unit u + 1 in scores(u)
+    auto scores = [&](int u, const bf16x8 (&kr)[2][2], bf16x8 (&krn)[2][2])
+                      __attribute__((always_inline)) {
+      if (u + 1 < U) {
+        load_kr(u + 1, raw_next, krn);
+        raw_next = page_raw(u + 2);
+      }
+      const uint8_t* lat = sm.lat[u & 3];
+      auto kfrag = [&](int kk, int ti) {
+        return *reinterpret_cast<const bf16x8*>(lat + loff[kk & 3] + ti * 16 * 1024 + ((kk >> 2) << 8));
+      };
+      f32x4 acc[2][2];  // [rt][ti]
+#pragma unroll
+      for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+        for (int ti = 0; ti < 2; ++ti)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) acc[rt][ti][i] = 0.0f;
       constexpr int KDEPTH = 4;
       bf16x8 kf[KDEPTH][2];
 #pragma unroll
-      for (int kk = KB; kk < KB + KDEPTH && kk < KE; ++kk) {
-        kf[kk % KDEPTH][0] = kfrag(u, kk, 0);
-        kf[kk % KDEPTH][1] = kfrag(u, kk, 1);
+      for (int kk = 0; kk < KDEPTH; ++kk) {
+        kf[kk][0] = kfrag(kk, 0);
+        kf[kk][1] = kfrag(kk, 1);
       }
 #pragma unroll
-      for (int kk = KB; kk < KE; ++kk) {
-        const bf16x8 k0 = kf[kk % KDEPTH][0];
-        const bf16x8 k1 = kf[kk % KDEPTH][1];
-        if (kk + KDEPTH < KE) {
-          kf[kk % KDEPTH][0] = kfrag(u, kk + KDEPTH, 0);
-          kf[kk % KDEPTH][1] = kfrag(u, kk + KDEPTH, 1);
+      for (int kk = 0; kk < QSTEPS; ++kk) {
+        bf16x8 k0, k1;
+        if (kk < LSTEPS) {
+          k0 = kf[kk % KDEPTH][0];
+          k1 = kf[kk % KDEPTH][1];
+          if (kk + KDEPTH < LSTEPS) {
+            kf[kk % KDEPTH][0] = kfrag(kk + KDEPTH, 0);
+            kf[kk % KDEPTH][1] = kfrag(kk + KDEPTH, 1);
+          }
+        } else {
+          k0 = kr[kk - LSTEPS][0];
+          k1 = kr[kk - LSTEPS][1];
         }
         acc[0][0] = mfma16(k0, qf[0][kk], acc[0][0]);
         acc[1][0] = mfma16(k0, qf[1][kk], acc[1][0]);
@@ -276,67 +387,49 @@ __global__ __launch_bounds__(NT, 1) void decode_mfma_kernel(const DecodeParams p
         acc[1][1] = mfma16(k1, qf[1][kk], acc[1][1]);
         __builtin_amdgcn_sched_barrier(0);
       }
-    };
-    using K0 = std::integral_constant<int, 0>;
-    using KA = std::integral_constant<int, A_SPLIT>;
-    using KN = std::integral_constant<int, QSTEPS>;
-    auto first_steps = [&](int u) {
+      float* sdst = sm.s[u & 1];
 #pragma unroll
       for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
         for (int ti = 0; ti < 2; ++ti)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) acc[rt][ti][i] = 0.0f;
-      steps(u, K0{}, KA{});
-    };
-    auto finish_and_store = [&](int u) {
-      steps(u, KA{}, KN{});
-#pragma unroll
-      for (int rt = 0; rt < 2; ++rt)
-#pragma unroll
-        for (int ti = 0; ti < 2; ++ti)
-          *reinterpret_cast<f32x4*>(&sm.s[(32 * wave + 16 * rt + n16) * S_LD + 16 * ti + 4 * g4]) =
+          *reinterpret_cast<f32x4*>(&sdst[(32 * wave + 16 * rt + n16) * S_LD + 16 * ti + 4 * g4]) =
               acc[rt][ti];
     };
 
+    // rotary keys double-buffered by unit parity
+    bf16x8 kra[2][2], krb[2][2];
+    load_kr(0, page_raw(0), kra);
+    raw_next = page_raw(1);
     lds_barrier();                         // B0: unit 0 landed
-    first_steps(0);
-    for (int j = -1; j < U; ++j) {
-      if (j + 1 < U) finish_and_store(j + 1);
-      lds_barrier();                       // M(j)
-      if (j + 2 < U) first_steps(j + 2);
+    // j even: unit j+2 is even, its keys in kra, the next unit's into krb
+    for (int j = -2; j < U; j += 2) {
+      if (j + 2 < U) scores(j + 2, kra, krb);
       lds_barrier();                       // E(j)
+      if (j + 1 < U) {
+        if (j + 3 < U) scores(j + 3, krb, kra);
+        lds_barrier();                     // E(j+1)
+      }
     }
     lds_barrier();                         // F
   } else if (wave >= 4 && wave < 6) {
-    // ============================ copy / softmax waves ===========================
-    // Copy wave c fills latent rows t = c + 2i (i < 16) and the rotary rows
-    // 16c .. 16c+15 of a unit: 18 direct-to-LDS copies of 1 KiB.  Lane l
-    // fetches the chunk that belongs at LDS chunk position l of its row
-    // (latent), or at slot l & 7 of row 8q + (l >> 3) (rotary).  It also runs
-    // the softmax of query rows 32c .. 32c+31.
+    // =============================== copy waves ================================
+    // Copy wave c fills latent rows t = c + 2i (i < 16) of a unit: 16
+    // direct-to-LDS copies of 1 KiB.  Lane l fetches the 16-byte chunk that
+    // belongs at LDS chunk position l of its row.
     const int c = wave - 4;
-    const int32_t* table = p.block_table + (size_t)b * p.max_blocks;
     // Page ids are read through the constant address space: the index is
     // uniform, so this is a scalar load (lgkmcnt), and the wait for it does not
     // drain the copies in flight (vmcnt).
     const int32_t __attribute__((address_space(4)))* ctable =
-        (const int32_t __attribute__((address_space(4)))*)table;
+        (const int32_t __attribute__((address_space(4)))*)(p.block_table + (size_t)b * p.max_blocks);
     const uint8_t* pool = static_cast<const uint8_t*>(p.pool);
     int cl[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) cl[i] = (lane ^ lat_sw(c + 2 * i)) << 4;
-    int cr[2];
-#pragma unroll
-    for (int e = 0; e < 2; ++e) {
-      const int row = 8 * (2 * c + e) + (lane >> 3);
-      cr[e] = row * ROW_BYTES + 1024 + (((lane & 7) ^ rot_sw(row)) << 4);
-    }
     // Page-table entry of unit u (clamped to the range's last unit, so the
     // read stays inside the range's pages); read one step ahead in the loop.
     auto page_raw = [&](int u) { return ctable[(tok0 + min(u, U - 1) * UNIT) / BS]; };
     const uint32_t lat_base = (uint32_t)(uintptr_t)&sm.lat[0][0];
-    const uint32_t rot_base = (uint32_t)(uintptr_t)&sm.rot[0][0];
     auto issue = [&](int u, int raw) {
       const int blk = clamp_block(raw, p.num_blocks);
       const uint8_t* src = pool + (size_t)blk * TILE_BYTES + ((tok0 + u * UNIT) % BS) * ROW_BYTES;
@@ -346,10 +439,6 @@ __global__ __launch_bounds__(NT, 1) void decode_mfma_kernel(const DecodeParams p
         const int row = c + 2 * i;
         copy16_to_lds(src + row * ROW_BYTES, (uint32_t)cl[i & 7], lat + row * 1024);
       }
-#pragma unroll
-      for (int e = 0; e < 2; ++e)
-        copy16_to_lds(src, (uint32_t)cr[e],
-                      rot_base + (u % 3) * (UNIT * 128) + (2 * c + e) * 1024);
     };
     // Rows past the visible length of the range's last unit are zeroed once
     // it has landed and before V is read from it: stale contents (possibly
@@ -362,104 +451,42 @@ __global__ __launch_bounds__(NT, 1) void decode_mfma_kernel(const DecodeParams p
       const u32x4 z = {0u, 0u, 0u, 0u};
       u32x4* dl = reinterpret_cast<u32x4*>(sm.lat[u & 3]);
       for (int q = valid * 64 + zt; q < UNIT * 64; q += 128) dl[q] = z;
-      u32x4* dr = reinterpret_cast<u32x4*>(sm.rot[u % 3]);
-      for (int q = valid * 8 + zt; q < UNIT * 8; q += 128) dr[q] = z;
-    };
-
-    // softmax lanes: query row 32c + (l & 31), P k-slots 8h + e (+16ks),
-    // h = l >> 5, e < 8, ks < 2: 16 scores per lane, the other 16 of the row
-    // in lane l ^ 32
-    const int srow = 32 * c + l32;
-    float m_run = -INFINITY;  // reference max (log2 units) of row srow
-    float l_run = 0.0f;       // running sum in that reference
-    const float c_log2 = p.scale_log2;
-    auto softmax = [&](int u) {
-      // Scale and subtract stay separate operations, so the maximal score
-      // gives exactly exp2(0) = 1.
-#pragma clang fp contract(off)
-      float x[2][8];
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        // slot 8h + e of k-step ks holds token 16ks + tok_of(8h + e): token
-        // pairs 16ks + 2h + 4q, +1 give slots e = q and e = q + 4
-        const float* srd = &sm.s[srow * S_LD + 16 * ks + 2 * lhi];
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const float2 pr = *reinterpret_cast<const float2*>(srd + 4 * q);
-          x[ks][q] = pr.x * c_log2;
-          x[ks][q + 4] = pr.y * c_log2;
-        }
-      }
-      const int valid = unit_valid(u);
-      if (valid < UNIT) {  // only the range's last unit can be partial
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-          for (int e = 0; e < 8; ++e)
-            if (16 * ks + tok_of(8 * lhi + e) >= valid) x[ks][e] = -INFINITY;
-      }
-      float mx = -INFINITY;
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) mx = fmaxf(mx, x[ks][e]);
-      mx = xor32_max(mx);
-      const bool raise = mx > m_run + kRescaleSlack;  // always on the first unit
-      const float m_new = raise ? mx : m_run;
-      const float alpha = raise ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.0f;
-      m_run = m_new;
-      float sum = 0.0f;
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        u16x8 pb;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float ex = __builtin_amdgcn_exp2f(x[ks][e] - m_new);
-          sum += ex;
-          pb[e] = f32_to_bf16(ex);
-        }
-        *reinterpret_cast<u16x8*>(&sm.p[srow * P_LD + 16 * ks + 8 * lhi]) = pb;
-      }
-      sum = xor32_sum(sum);
-      l_run = l_run * alpha + sum;
-      if (lhi == 0) sm.alpha[srow] = alpha;
-      const bool any_raise = __any(raise);
-      if (lane == 0) sm.flag[c] = any_raise ? 1 : 0;
     };
 
     issue(0, page_raw(0));
     if (U > 1) issue(1, page_raw(1));
     if (U > 2) issue(2, page_raw(2));
-    int raw_next = page_raw(3);
-    if (U > 2) wait_vmcnt<2 * COPIES>(); else if (U > 1) wait_vmcnt<COPIES>(); else wait_vmcnt<0>();
-    lds_barrier();                         // B0: unit 0 landed
-    zero_tail(0);
-    for (int j = -1; j < U; ++j) {
-      if (j >= 0 && j + 3 < U) {
-        issue(j + 3, raw_next);
-        raw_next = page_raw(j + 4);
+    if (U > 3) issue(3, page_raw(3));
+    int raw_next = page_raw(4);
+    // unit 0 lands before B0 (its scores run in step -2); units 1..3 may
+    // still be in flight
+    if (U > 3) wait_vmcnt<3 * COPIES>();
+    else if (U > 2) wait_vmcnt<2 * COPIES>();
+    else if (U > 1) wait_vmcnt<COPIES>();
+    else wait_vmcnt<0>();
+    lds_barrier();                         // B0
+    for (int j = -2; j < U; ++j) {
+      if (j >= 0 && j + 4 < U) {
+        issue(j + 4, raw_next);
+        raw_next = page_raw(j + 5);
       }
-      if (j + 2 < U) {  // unit j+2 landed: only unit j+3 may still be in flight
-        if (j + 3 < U) wait_vmcnt<COPIES>(); else wait_vmcnt<0>();
+      if (j + 2 >= 0 && j + 2 < U) zero_tail(j + 2);  // landed by E(j-1) (B0 for unit 0)
+      // unit j+3 lands before E(j): the units issued after it may stay in
+      // flight -- units 2 and 3 in step -2, unit j+4 from step -1 on
+      if (j + 3 < U) {
+        if (j == -2) {
+          if (U > 3) wait_vmcnt<2 * COPIES>(); else if (U > 2) wait_vmcnt<COPIES>(); else wait_vmcnt<0>();
+        } else {
+          if (j + 4 < U) wait_vmcnt<COPIES>(); else wait_vmcnt<0>();
+        }
       }
-      lds_barrier();                       // M(j)
-      if (j + 1 < U) softmax(j + 1);
-      if (j + 2 < U) zero_tail(j + 2);
       lds_barrier();                       // E(j)
-    }
-    if (lhi == 0) {
-      sm.lrow[srow] = l_run;
-      const float lse = (m_run + log2f(l_run)) * kLn2;
-      if (direct) {
-        if (p.lse != nullptr) p.lse[(size_t)b * TH + rb + srow] = lse;
-      } else {
-        p.part_lse[((size_t)b * S + s) * TH + rb + srow] = lse;
-      }
     }
     lds_barrier();                         // F
   } else {
     // =============================== value waves ===============================
-    // Value wave v owns latent columns 128v .. 128v+127 of O for all 64 rows.
+    // Value wave v owns latent columns 128v .. 128v+127 of O for all 64 rows,
+    // and the softmax of query rows 16v .. 16v+15.
     const int v = (wave & 1) + 2 * (wave >> 2);
     // Transposing-read offsets of this lane: in 16-lane group gq, lane i points
     // at token 4*(i >> 2) + 2*lhi + sel (+ 16*ks), columns 128v + 32dt + 16*gq
@@ -478,6 +505,8 @@ __global__ __launch_bounds__(NT, 1) void decode_mfma_kernel(const DecodeParams p
       }
     const int poff = l32 * P_LD + 8 * lhi;  // bf16 elements
 
+    float m_run = -INFINITY, l_run = 0.0f;
+
     f32x16 o[2][4];
 #pragma unroll
     for (int rt = 0; rt < 2; ++rt)
@@ -486,16 +515,11 @@ __global__ __launch_bounds__(NT, 1) void decode_mfma_kernel(const DecodeParams p
 #pragma unroll
         for (int r = 0; r < 16; ++r) o[rt][dt][r] = 0.0f;
 
-    bf16x8 pf[2][2], vf[2][4];
-    // P(j), the rescale flags and V(j) into registers, rescale O if a row of
-    // unit j raised its reference max, and the MFMAs of k-step 0.
-    auto pv_first = [&](int j) {
-      const uint8_t* lat = sm.lat[j & 3];
-      const int2 fl = *reinterpret_cast<const int2*>(sm.flag);
+    bf16x8 vf[2][4];  // V of the unit whose P.V runs next
+    auto load_v = [&](int u) {
+      const uint8_t* lat = sm.lat[u & 3];
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        pf[ks][0] = *reinterpret_cast<const bf16x8*>(sm.p + poff + 16 * ks);
-        pf[ks][1] = *reinterpret_cast<const bf16x8*>(sm.p + 32 * P_LD + poff + 16 * ks);
+      for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
         for (int dt = 0; dt < 4; ++dt) {
           const s16x4 v0 = lds_tr16(lat + voff[dt][0] + 16 * ks * 1024);
@@ -503,13 +527,29 @@ __global__ __launch_bounds__(NT, 1) void decode_mfma_kernel(const DecodeParams p
           const short vv[8] = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
           vf[ks][dt] = __builtin_bit_cast(bf16x8, vv);
         }
+    };
+    // P(u) and the rescale flags into registers (issued before the softmax of
+    // the next unit so that their latency is hidden), then O = alpha(u) O +
+    // P(u) V(u)
+    bf16x8 pf[2][2];
+    int4 fl;
+    auto read_p = [&](int u) {
+      const uint16_t* pp = sm.p[u & 1];
+      fl = *reinterpret_cast<const int4*>(sm.flag[u & 1]);
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        pf[ks][0] = *reinterpret_cast<const bf16x8*>(pp + poff + 16 * ks);
+        pf[ks][1] = *reinterpret_cast<const bf16x8*>(pp + 32 * P_LD + poff + 16 * ks);
       }
-      if (fl.x | fl.y) {
+    };
+    auto pv = [&](int u) {
+      if (fl.x | fl.y | fl.z | fl.w) {
 #pragma unroll
         for (int rt = 0; rt < 2; ++rt) {
 #pragma unroll
           for (int r4 = 0; r4 < 4; ++r4) {
-            const float4 al = *reinterpret_cast<const float4*>(&sm.alpha[32 * rt + 8 * r4 + 4 * lhi]);
+            const float4 al =
+                *reinterpret_cast<const float4*>(&sm.alpha[u & 1][32 * rt + 8 * r4 + 4 * lhi]);
 #pragma unroll
             for (int dt = 0; dt < 4; ++dt) {
               o[rt][dt][4 * r4 + 0] *= al.x;
@@ -521,27 +561,42 @@ __global__ __launch_bounds__(NT, 1) void decode_mfma_kernel(const DecodeParams p
         }
       }
 #pragma unroll
-      for (int dt = 0; dt < 4; ++dt) {
-        o[0][dt] = mfma32(pf[0][0], vf[0][dt], o[0][dt]);
-        o[1][dt] = mfma32(pf[0][1], vf[0][dt], o[1][dt]);
-      }
-    };
-    auto pv_second = [&]() {
+      for (int ks = 0; ks < 2; ++ks) {
 #pragma unroll
-      for (int dt = 0; dt < 4; ++dt) {
-        o[0][dt] = mfma32(pf[1][0], vf[1][dt], o[0][dt]);
-        o[1][dt] = mfma32(pf[1][1], vf[1][dt], o[1][dt]);
+        for (int dt = 0; dt < 4; ++dt) {
+          o[0][dt] = mfma32(pf[ks][0], vf[ks][dt], o[0][dt]);
+          o[1][dt] = mfma32(pf[ks][1], vf[ks][dt], o[1][dt]);
+        }
       }
     };
 
-    lds_barrier();                         // B0
-    for (int j = -1; j < U; ++j) {
-      if (j >= 0) pv_first(j);
-      lds_barrier();                       // M(j)
-      if (j >= 0) pv_second();
+    // Step j.  The softmax of unit j+1 and P(j) V(j) are independent; the two
+    // value waves of a SIMD (v and v + 2) run them in opposite orders, so
+    // that one wave's softmax (VALU) overlaps the other's MFMAs instead of
+    // both waves contending for the same unit at the same time.  V(j+1)
+    // replaces V(j) in registers right after the MFMAs that read V(j).
+    auto step = [&](int j, auto pv_first) __attribute__((always_inline)) {
+      const bool next = j + 1 >= 0 && j + 1 < U;
+      if (j >= 0) read_p(j);
+      if (pv_first) {
+        if (j >= 0) pv(j);
+        if (next) load_v(j + 1);
+        if (next) softmax_unit(sm, j + 1, unit_valid(j + 1), v, lane, p.scale_log2, m_run, l_run);
+      } else {
+        if (next) softmax_unit(sm, j + 1, unit_valid(j + 1), v, lane, p.scale_log2, m_run, l_run);
+        if (j >= 0) pv(j);
+        if (next) load_v(j + 1);
+      }
       lds_barrier();                       // E(j)
+    };
+    lds_barrier();                         // B0
+    if (v >= 2) {
+      for (int j = -2; j < U; ++j) step(j, std::true_type{});
+    } else {
+      for (int j = -2; j < U; ++j) step(j, std::false_type{});
     }
 
+    softmax_finish(sm, p, v, lane, m_run, l_run, direct, b, s, TH, rb);
     lds_barrier();                         // F
     float* dst = direct ? p.o_lat + ((size_t)b * TH + rb) * DC
                         : p.part_o + (((size_t)b * S + s) * TH + rb) * DC;
