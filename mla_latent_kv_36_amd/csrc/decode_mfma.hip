@@ -75,7 +75,7 @@ struct __align__(16) Smem {
   float s[2][ROWS * S_LD];     // raw scores by unit parity, [row][token]
   uint16_t p[2][ROWS * P_LD];  // probabilities (bf16) by unit parity, [row][k-slot]
   float alpha[2][ROWS];        // per-row rescale factor, by unit parity
-  float lrow[ROWS];
+  float lrow[ROWS];            // 1 / (row sum), after the last unit
   int flag[2][4];              // [unit parity][row group]: some row of its 16 raised its max
 };
 
@@ -206,14 +206,15 @@ __device__ __forceinline__ void softmax_unit(Smem& sm, int u, int valid, int grp
   if (lane == 0) sm.flag[u & 1][grp] = any_raise ? 1 : 0;
 }
 
-// After the last unit: the group's row sums for the normalisation, and the
-// rows' log-sum-exp (natural log) to the output or to the split's partial.
+// After the last unit: the reciprocals of the group's row sums for the
+// normalisation, and the rows' log-sum-exp (natural log) to the output or to
+// the split's partial.
 __device__ __forceinline__ void softmax_finish(Smem& sm, const DecodeParams& p, int grp, int lane,
                                                float m_run, float l_run, bool direct, int b, int s,
                                                int TH, int rb) {
   if ((lane >> 4) != 0) return;
   const int srow = 16 * grp + (lane & 15);
-  sm.lrow[srow] = l_run;
+  sm.lrow[srow] = 1.0f / l_run;
   const float lse = (m_run + log2f(l_run)) * kLn2;
   if (direct) {
     if (p.lse != nullptr) p.lse[(size_t)b * TH + rb + srow] = lse;
@@ -345,10 +346,6 @@ __global__ __launch_bounds__(NT, 1) void decode_mfma_kernel(const DecodeParams p
     int raw_next;  // page-table entry of unit u + 1 in scores(u)
     auto scores = [&](int u, const bf16x8 (&kr)[2][2], bf16x8 (&krn)[2][2])
                       __attribute__((always_inline)) {
-      if (u + 1 < U) {
-        load_kr(u + 1, raw_next, krn);
-        raw_next = page_raw(u + 2);
-      }
       const uint8_t* lat = sm.lat[u & 3];
       auto kfrag = [&](int kk, int ti) {
         return *reinterpret_cast<const bf16x8*>(lat + loff[kk & 3] + ti * 16 * 1024 + ((kk >> 2) << 8));
@@ -367,8 +364,16 @@ __global__ __launch_bounds__(NT, 1) void decode_mfma_kernel(const DecodeParams p
         kf[kk][0] = kfrag(kk, 0);
         kf[kk][1] = kfrag(kk, 1);
       }
+      // the two rotary k-steps (keys already in registers) run first, while
+      // the first latent fragments are still on their way from LDS; the next
+      // unit's rotary keys are requested right after
 #pragma unroll
-      for (int kk = 0; kk < QSTEPS; ++kk) {
+      for (int i = 0; i < QSTEPS; ++i) {
+        const int kk = i < QSTEPS - LSTEPS ? LSTEPS + i : i - (QSTEPS - LSTEPS);
+        if (i == QSTEPS - LSTEPS && u + 1 < U) {
+          load_kr(u + 1, raw_next, krn);
+          raw_next = page_raw(u + 2);
+        }
         bf16x8 k0, k1;
         if (kk < LSTEPS) {
           k0 = kf[kk % KDEPTH][0];
@@ -605,7 +610,7 @@ __global__ __launch_bounds__(NT, 1) void decode_mfma_kernel(const DecodeParams p
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int row = 32 * rt + 8 * (r >> 2) + 4 * lhi + (r & 3);
-        const float inv = 1.0f / sm.lrow[row];
+        const float inv = sm.lrow[row];
 #pragma unroll
         for (int dt = 0; dt < 4; ++dt)
           dst[(size_t)row * DC + 128 * v + 32 * dt + l32] = o[rt][dt][r] * inv;
