@@ -35,6 +35,9 @@ REDUCED = {
     "long": LONG.scaled(B=2, N=1500),
     "v2_multi": V2_MULTI.scaled(B=3, N=300),
     "bf16_h16": V3.scaled(B=2, H=16, N=200),        # bf16 through the generic kernel
+    # 16 heads x 4 causal tokens: 64 rows per token set, but each query token
+    # has its own causal limit, so this must not take the 64-row MFMA path
+    "bf16_h16_t4": V3.scaled(B=2, T=4, H=16, N=200),
 }
 
 
