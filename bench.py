@@ -219,9 +219,18 @@ def main() -> int:
     W = w.d_c + w.d_r
     elem = 2 if w.dtype == "bf16" else 4
     cache_bytes = total_tokens * W * elem                       # per decode launch
-    pairs = sum(int(n) * w.T for n in bt.seq_lens)               # (query, cached row) pairs
+    # (query, cached row) pairs: with the causal mask query t of a sequence of
+    # n rows (after the append) sees n - T + t + 1 of them
+    if w.causal:
+        pairs = sum(int(n) * w.T - w.T * (w.T - 1) // 2 for n in bt.seq_lens)
+    else:
+        pairs = sum(int(n) * w.T for n in bt.seq_lens)
     decode_flops = pairs * w.H * (2 * W + 2 * w.d_c)
-    achieved = cache_bytes / (ms_decode * 1e-3) / 1e9
+    gbps = cache_bytes / (ms_decode * 1e-3) / 1e9
+    tflops = decode_flops / (ms_decode * 1e-3) / 1e12
+    # the bound is the one the workload's arithmetic intensity puts it under
+    # (T = 1 decode sits below the ridge, many queries per row above it)
+    mfma_bound = decode_flops / cache_bytes > MFMA_BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBPS * 1e9)
     tokens = w.B * w.T
     traffic = measured_traffic(w.name, splits)
     line = {
@@ -243,8 +252,12 @@ def main() -> int:
                    "block_size": w.block_size, "num_splits": splits,
                    "rotated_copies": args.rotate, "timing": "HIP graph replay"},
         "roofline": {"kernel": "mla_decode launch = decode_mfma_kernel + combine_kernel",
-                     "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS,
-                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
+                     "bound": "mfma" if mfma_bound else "hbm",
+                     "achieved": tflops if mfma_bound else gbps,
+                     "peak": MFMA_BF16_PEAK_TFLOPS if mfma_bound else HBM_PEAK_GBPS,
+                     "unit": "TFLOP/s" if mfma_bound else "GB/s",
+                     "frac": (tflops / MFMA_BF16_PEAK_TFLOPS) if mfma_bound
+                     else (gbps / HBM_PEAK_GBPS),
                      "traffic": traffic["hbm_bytes_per_launch"] if traffic else None,
                      "traffic_detail": ({k: traffic[k] for k in
                                          ("fetch_bytes_per_launch", "write_bytes_per_launch",
@@ -252,9 +265,9 @@ def main() -> int:
                                         if traffic else None),
                      "algorithmic_bytes_per_launch": cache_bytes,
                      "avg_launch_us": ms_decode * 1e3,
-                     "mfma_tflops": decode_flops / (ms_decode * 1e-3) / 1e12,
-                     "mfma_frac": decode_flops / (ms_decode * 1e-3) / 1e12
-                     / MFMA_BF16_PEAK_TFLOPS},
+                     "algorithmic_flops_per_launch": decode_flops,
+                     "cache_GBps": gbps, "hbm_frac": gbps / HBM_PEAK_GBPS,
+                     "mfma_tflops": tflops, "mfma_frac": tflops / MFMA_BF16_PEAK_TFLOPS},
         "latent_cache_GBps_step": cache_bytes / (ms_step * 1e-3) / 1e9,
         "decode_tokens_per_s": tokens / (ms_decode * 1e-3),
         "phases_us": {"absorb_q": ms_absorb * 1e3, "cache_append": ms_append * 1e3,

@@ -8,7 +8,7 @@ import torch
 
 import oracle
 from mla_latent_kv_36_amd import binding as mla
-from workloads import LONG, V2_MULTI, V3, VARLEN, make_inputs
+from workloads import LONG, PREFILL, V2_MULTI, V3, VARLEN, make_inputs
 from workloads.device import upload
 
 from gpu_util import (dev_bits, make_step, max_err_ratio, note, oracle_pool_after,
@@ -79,3 +79,12 @@ def test_long_context_full(num_splits):
 def test_v2_multi_token_full():
     """32 sequences x (8,192 + 4) rows, 4 causal queries each: four sequences."""
     _check_step(V2_MULTI, seqs=[0, 9, 22, 31])
+
+
+def test_prefill_chunk_full():
+    """4 sequences x (3,584 + 512) rows, 512 causal queries each (a prefill
+    chunk through the absorbed path): every sequence, six heads chosen up front,
+    all 512 queries."""
+    heads = [0, 31, 64, 77, 100, 127]
+    _check_step(PREFILL, seqs=range(PREFILL.B), heads=heads)
+

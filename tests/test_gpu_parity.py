@@ -19,7 +19,7 @@ import torch
 
 import oracle
 from mla_latent_kv_36_amd import binding as mla
-from workloads import LONG, TINY, V2_MULTI, V3, VARLEN, make_inputs
+from workloads import LONG, PREFILL, TINY, V2_MULTI, V3, VARLEN, make_inputs
 from workloads.device import to_dev, torch_dtype, upload
 
 from gpu_util import (cfg_of, dev_bits, make_step, max_err_ratio, note, oracle_decode,
@@ -38,6 +38,8 @@ REDUCED = {
     # 16 heads x 4 causal tokens: 64 rows per token set, but each query token
     # has its own causal limit, so this must not take the 64-row MFMA path
     "bf16_h16_t4": V3.scaled(B=2, T=4, H=16, N=200),
+    # a prefill chunk: 64 causal queries per sequence over a ragged cache
+    "prefill": PREFILL.scaled(B=2, T=64, N=200),
 }
 
 

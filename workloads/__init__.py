@@ -1,6 +1,6 @@
 """Seeded synthetic decode workloads (shapes and random inputs only)."""
-from .configs import ALL, BY_NAME, LONG, TINY, V2_MULTI, V3, VARLEN, Workload
+from .configs import ALL, BY_NAME, EXTRA, LONG, PREFILL, TINY, V2_MULTI, V3, VARLEN, Workload
 from .inputs import Batch, bf16_bits, bf16_round, make_inputs
 
-__all__ = ["ALL", "BY_NAME", "LONG", "TINY", "V2_MULTI", "V3", "VARLEN", "Workload",
+__all__ = ["ALL", "BY_NAME", "EXTRA", "LONG", "PREFILL", "TINY", "V2_MULTI", "V3", "VARLEN", "Workload",
            "Batch", "bf16_bits", "bf16_round", "make_inputs"]

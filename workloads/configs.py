@@ -75,4 +75,13 @@ V2_MULTI = Workload(name="v2_multi_token", seed=5, B=32, T=4, H=128, d_c=512, d_
                     d_n=40, d_v=40, N=8192, dtype="bf16")
 
 ALL = (TINY, V3, VARLEN, LONG, V2_MULTI)
-BY_NAME = {w.name: w for w in ALL}
+
+# Beyond the five decode configs: a chunk of prefill -- 512 new tokens per
+# sequence attend causally to 3,584 cached rows and to each other, through the
+# same absorbed path (the pages' absorbed code runs exactly this with T > 1).
+# No page gives a prefill shape; V3 widths, 4 sequences, 4,096 rows after.
+PREFILL = Workload(name="prefill_chunk", seed=6, B=4, T=512, H=128, d_c=512, d_r=64,
+                   d_n=128, d_v=128, N=3584, dtype="bf16")
+EXTRA = (PREFILL,)
+
+BY_NAME = {w.name: w for w in ALL + EXTRA}
