@@ -329,6 +329,34 @@ def rope_ref(x: np.ndarray, pos: np.ndarray, base: float = 10000.0) -> np.ndarra
     return out
 
 
+def kv_produce_ref(hidden: np.ndarray, w_dkv: np.ndarray, w_kr: np.ndarray,
+                   pos: np.ndarray, base: float = 10000.0, dtype=F64) -> np.ndarray:
+    """The cached row of each new token, from its hidden vector h (width d):
+    the latent c = W^DKV h ("Multi-head latent attention (MLA)", section 2: the
+    down-projection is the only thing cached) and the decoupled rotary key
+    k^R = RoPE(W^KR h) at the token's position (same page, section 3: the key
+    has its own projection and is rotated directly; "Attention, Part 2",
+    section "The MLA equations" and its inference code, which computes the two
+    and nothing else for the cache).  The latent is never rotated.
+    hidden [n, d], w_dkv [d_c, d], w_kr [d_r, d], pos [n] -> [n, d_c + d_r]."""
+    h = np.asarray(hidden, dtype)
+    c = h @ np.asarray(w_dkv, dtype).T
+    kr = h @ np.asarray(w_kr, dtype).T
+    return np.concatenate([c, rope_ref(kr, pos, base)], axis=-1)
+
+
+def produce_append_ref(pool, block_table, seq_lens_before, hidden, w_dkv, w_kr,
+                       block_size: int, base: float = 10000.0) -> np.ndarray:
+    """The producer step of a batch: token i of sequence b (hidden [B, T, d])
+    sits at position seq_lens_before[b] + i; its row is produced and appended
+    there.  Returns the pool after (float64)."""
+    B, T, _ = hidden.shape
+    rows = np.stack([kv_produce_ref(hidden[b], w_dkv, w_kr,
+                                    int(seq_lens_before[b]) + np.arange(T), base)
+                     for b in range(B)])
+    return append_ref(pool, block_table, seq_lens_before, rows, block_size)
+
+
 def naive_rope_on_rebuilt_keys_ref(q_nope, w_uk, w_uv, rows, d_c: int, scale: float,
                                    q_pos: np.ndarray, k_pos: Optional[np.ndarray] = None,
                                    base: float = 10000.0):

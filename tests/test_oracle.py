@@ -321,3 +321,80 @@ def test_rope_rotation_properties():
     d1 = oracle.rope_ref(np.stack([a, b]), np.array([3, 1]))
     d2 = oracle.rope_ref(np.stack([a, b]), np.array([9, 7]))
     assert math.isclose(d1[0] @ d1[1], d2[0] @ d2[1], rel_tol=1e-12, abs_tol=1e-12)
+
+
+# ------------------------------------------------------------------ producer step
+# The producer of a cached row (c = W^DKV h, k^R = RoPE(W^KR h) at the token's
+# position).  Each check takes the functions under test, so the planted
+# mistakes in test_oracle_mutants.py run through the same pins.
+
+def producer_one_hot_pin(produce) -> bool:
+    """h = e_j: the latent is column j of W^DKV (a transposed weight would read
+    a row) and at position 0 (no rotation) the rotary key is column j of W^KR
+    ("Multi-head latent attention (MLA)", sections 2 and 3)."""
+    rng = np.random.default_rng(21)
+    d, d_c, d_r = 12, 6, 4
+    w_dkv, w_kr = rng.standard_normal((d_c, d)), rng.standard_normal((d_r, d))
+    for j in (0, 5, 11):
+        h = np.zeros((1, d))
+        h[0, j] = 1.0
+        row = produce(h, w_dkv, w_kr, np.array([0]))
+        if not (np.array_equal(row[0, :d_c], w_dkv[:, j]) and np.array_equal(row[0, d_c:], w_kr[:, j])):
+            return False
+    return True
+
+
+def producer_position_pin(produce) -> bool:
+    """Only k^R carries position: the latent of one hidden vector is the same
+    at every position, and its rotary key keeps its norm ("Attention, Part 2",
+    section "Why position needs its own key": the latent is never rotated)."""
+    rng = np.random.default_rng(22)
+    d, d_c, d_r = 10, 6, 8
+    w_dkv, w_kr = rng.standard_normal((d_c, d)), rng.standard_normal((d_r, d))
+    h = np.repeat(rng.standard_normal((1, d)), 5, axis=0)
+    rows = produce(h, w_dkv, w_kr, np.array([0, 1, 7, 100, 4095]))
+    same_c = all(np.array_equal(rows[i, :d_c], rows[0, :d_c]) for i in range(5))
+    norms = np.linalg.norm(rows[:, d_c:], axis=1)
+    return same_c and bool(np.allclose(norms, norms[0], rtol=1e-13, atol=0))
+
+
+def rope_angle_pin(rope) -> bool:
+    """The reading for the angles (the pages leave the base open): consecutive
+    pairs (x[2i], x[2i+1]) at position m turn by m * base^(-2i/d), base 10000.
+    With d = 4, pair 0 turns 1 rad per position and pair 1 0.01 rad."""
+    x = np.array([[1.0, 0.0, 0.0, 0.0], [0.0, 0.0, 1.0, 0.0], [0.0, 1.0, 0.0, 0.0]])
+    y = rope(x, np.array([1, 100, 2]))
+    c1, s1, c2, s2 = math.cos(1.0), math.sin(1.0), math.cos(2.0), math.sin(2.0)
+    want = np.array([[c1, s1, 0.0, 0.0], [0.0, 0.0, c1, s1], [-s2, c2, 0.0, 0.0]])
+    return bool(np.allclose(y, want, rtol=0, atol=1e-12))
+
+
+def test_producer_one_hot_reads_weight_columns():
+    assert producer_one_hot_pin(oracle.kv_produce_ref)
+
+
+def test_producer_latent_is_never_rotated():
+    assert producer_position_pin(oracle.kv_produce_ref)
+
+
+def test_rope_angles_closed_form():
+    assert rope_angle_pin(oracle.rope_ref)
+
+
+def test_produced_cache_attends_like_rebuilt_keys():
+    """End to end: rows made by the producer, attended through the absorbed
+    path, equal the naive path that rebuilds every head's key [W^UK c ; k^R]
+    and value W^UV c from the same rows (page 1, Exercise 3 at full size)."""
+    rng = np.random.default_rng(23)
+    T, H, d, d_n, d_v, d_c, d_r, N = 3, 4, 24, 8, 8, 16, 8, 20
+    w_dkv = rng.standard_normal((d_c, d)) / math.sqrt(d)
+    w_kr = rng.standard_normal((d_r, d)) / math.sqrt(d)
+    rows = oracle.kv_produce_ref(rng.standard_normal((N, d)), w_dkv, w_kr, np.arange(N))
+    q_nope, q_rope = rng.standard_normal((T, H, d_n)), rng.standard_normal((T, H, d_r))
+    w_uk = rng.standard_normal((H, d_n, d_c)) / math.sqrt(d_c)
+    w_uv = rng.standard_normal((H, d_v, d_c)) / math.sqrt(d_c)
+    scale = 1 / math.sqrt(d_n + d_r)
+    o_lat, _ = oracle.attend_ref(oracle.absorb_q_ref(q_nope, q_rope, w_uk), rows, d_c, scale, True)
+    got = oracle.out_proj_ref(o_lat, w_uv)
+    want = oracle.naive_ref(q_nope, q_rope, w_uk, w_uv, rows, d_c, scale, True)
+    assert _close(got, want, 1e-12)

@@ -101,3 +101,60 @@ def test_attend_mutant_rejected(case, bug):
 def test_absorb_mutant_rejected(case, bug):
     w, bt, rows = case
     assert not _absorb_pin(w, bt, rows, lambda qn, qr, wk: _absorb_variant(qn, qr, wk, bug))
+
+
+# ------------------------------------------------------------------ producer step
+
+def _rope_variant(x, pos, bug, base=10000.0):
+    x = np.asarray(x, np.float64)
+    d = x.shape[-1]
+    k = np.arange(0, d, 2, dtype=np.float64)
+    if bug == "angle_exponent_shifted":
+        k = k + 2
+    theta = base ** (-k / d)
+    ang = np.asarray(pos, np.float64)[:, None] * theta[None, :]
+    c, s = np.cos(ang), np.sin(ang)
+    if bug == "half_split_pairs":     # pairs (x[i], x[i + d/2]) instead of (x[2i], x[2i+1])
+        x1, x2 = x[..., : d // 2], x[..., d // 2:]
+        out = np.empty_like(x)
+        out[..., : d // 2] = x1 * c - x2 * s
+        out[..., d // 2:] = x1 * s + x2 * c
+        return out
+    sgn = -1.0 if bug == "rotation_sign" else 1.0
+    x1, x2 = x[..., 0::2], x[..., 1::2]
+    out = np.empty_like(x)
+    out[..., 0::2] = x1 * c - sgn * x2 * s
+    out[..., 1::2] = sgn * x1 * s + x2 * c
+    return out
+
+
+def _produce_variant(bug):
+    def produce(h, w_dkv, w_kr, pos):
+        h = np.asarray(h, np.float64)
+        if bug == "transposed_down_projection":
+            w = np.asarray(w_dkv, np.float64)
+            c = h @ w.reshape(w.shape[1], w.shape[0])
+        else:
+            c = h @ np.asarray(w_dkv, np.float64).T
+        kr = h @ np.asarray(w_kr, np.float64).T
+        if bug == "latent_rotated":
+            c = oracle.rope_ref(c, pos)
+        return np.concatenate([c, _rope_variant(kr, pos, bug)], axis=-1)
+    return produce
+
+
+@pytest.mark.parametrize("bug", ["transposed_down_projection", "latent_rotated",
+                                 "half_split_pairs", "angle_exponent_shifted", "rotation_sign"])
+def test_producer_pins_reject_planted_bug(bug):
+    from test_oracle import producer_one_hot_pin, producer_position_pin, rope_angle_pin
+    produce = _produce_variant(bug)
+    rope = lambda x, pos: _rope_variant(x, pos, bug)
+    assert not (producer_one_hot_pin(produce) and producer_position_pin(produce)
+                and rope_angle_pin(rope))
+
+
+def test_producer_pins_accept_the_unmutated_variant():
+    from test_oracle import producer_one_hot_pin, producer_position_pin, rope_angle_pin
+    produce = _produce_variant("none")
+    rope = lambda x, pos: _rope_variant(x, pos, "none")
+    assert producer_one_hot_pin(produce) and producer_position_pin(produce) and rope_angle_pin(rope)

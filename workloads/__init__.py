@@ -1,6 +1,7 @@
 """Seeded synthetic decode workloads (shapes and random inputs only)."""
 from .configs import ALL, BY_NAME, EXTRA, LONG, PREFILL, TINY, V2_MULTI, V3, VARLEN, Workload
-from .inputs import Batch, bf16_bits, bf16_round, make_inputs
+from .inputs import Batch, ProducerInputs, bf16_bits, bf16_round, make_inputs, make_producer_inputs
 
 __all__ = ["ALL", "BY_NAME", "EXTRA", "LONG", "PREFILL", "TINY", "V2_MULTI", "V3", "VARLEN", "Workload",
-           "Batch", "bf16_bits", "bf16_round", "make_inputs"]
+           "Batch", "ProducerInputs", "bf16_bits", "bf16_round", "make_inputs",
+           "make_producer_inputs"]

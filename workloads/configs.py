@@ -42,6 +42,7 @@ class Workload:
     var_len: bool = False  # per-sequence N drawn uniformly from [1, N]
     outlier_frac: float = 0.0   # fraction of cached rows scaled by outlier_scale
     outlier_scale: float = 1.0
+    d_model: int = 0       # model width d, for the producer step (0: no source gives it)
 
     @property
     def W(self) -> int:
@@ -71,8 +72,10 @@ VARLEN = Workload(name="varlen_serving", seed=3, B=64, T=1, H=128, d_c=512, d_r=
 LONG = Workload(name="long_128k", seed=4, B=4, T=1, H=128, d_c=512, d_r=64, d_n=128,
                 d_v=128, N=131072, dtype="bf16", outlier_frac=0.01, outlier_scale=8.0)
 # 5: V2-scale heads, 4 new tokens per sequence with a causal mask among them
+# (model width d = 5120 from the V2-scale configuration of "Multi-head latent
+# attention (MLA)", section 1)
 V2_MULTI = Workload(name="v2_multi_token", seed=5, B=32, T=4, H=128, d_c=512, d_r=64,
-                    d_n=40, d_v=40, N=8192, dtype="bf16")
+                    d_n=40, d_v=40, N=8192, dtype="bf16", d_model=5120)
 
 ALL = (TINY, V3, VARLEN, LONG, V2_MULTI)
 

@@ -157,3 +157,32 @@ def make_inputs(w: Workload, seed: int | None = None, *, with_rows: bool = True)
     return Batch(workload=w, lengths=lengths, seq_lens=seq_lens, rows=rows,
                  new_rows=new_rows, q_nope=q_nope, q_rope=q_rope, w_uk=w_uk, w_uv=w_uv,
                  q_abs=q_abs, pool=pool, block_table=table, poison_block=poison)
+
+
+@dataclass
+class ProducerInputs:
+    """Inputs of the producer step of one batch: the new tokens' hidden vectors
+    and the two down-projections.  Positions come from the batch's lengths."""
+    hidden: np.ndarray   # [B, T, d]
+    w_dkv: np.ndarray    # [d_c, d]
+    w_kr: np.ndarray     # [d_r, d]
+
+
+def make_producer_inputs(w: Workload, seed: int | None = None) -> ProducerInputs:
+    """Draws for the producer step, from their own ``default_rng`` stream
+    (seed 1000 + the workload's seed by default, so the decode inputs of
+    ``make_inputs`` are unchanged).  Order: hidden ``[B, T, d]`` ~ N(0, 1);
+    ``W^DKV [d_c, d]`` and ``W^KR [d_r, d]`` ~ N(0, 1) times 1/sqrt(d)
+    (standard deviation 1/sqrt(fan-in), the rule used for W^UK and W^UV).
+    Rounded to bf16 like the rest when the workload is bf16."""
+    if w.d_model <= 0:
+        raise ValueError(f"workload {w.name} has no model width for the producer step")
+    rng = np.random.default_rng(1000 + w.seed if seed is None else seed)
+    rnd = bf16_round if w.dtype == "bf16" else (lambda a: a.astype(np.float32))
+    d = w.d_model
+    hidden = rnd(rng.standard_normal((w.B, w.T, d), dtype=np.float32))
+    s = np.float32(1.0 / np.sqrt(d))
+    w_dkv = rnd(rng.standard_normal((w.d_c, d), dtype=np.float32) * s)
+    w_kr = rnd(rng.standard_normal((w.d_r, d), dtype=np.float32) * s)
+    return ProducerInputs(hidden=hidden, w_dkv=w_dkv, w_kr=w_kr)
+
