@@ -111,6 +111,56 @@ def cpu_baseline(w, budget_s: float) -> dict:
             "host_cpus": os.cpu_count(), "cpu_model": _cpu_model()}
 
 
+def producer_phase(w, bt, steps, torch, mla) -> dict:
+    """mla_kv_produce for the step's new tokens (W^DKV / W^KR down-projection,
+    RoPE on k^R, written into the cache), replayed over enough copies of the
+    hidden vectors and weights (>= 512 MiB in all) that the 256 MB MALL cannot
+    serve them: the weights are the bytes that bound this call."""
+    from workloads import make_producer_inputs
+    from workloads.device import to_dev
+    pi = make_producer_inputs(w)
+    cfg = mla.make_config(w.H, w.d_c, w.d_r, w.d_n, w.d_v, w.block_size, 0.0, w.dtype)
+    dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    elem = 2 if w.dtype == "bf16" else 4
+    M, N, d = w.B * w.T, w.d_c + w.d_r, w.d_model
+    read_bytes = (N * d + M * d) * elem
+    copies = max(8, -(-(512 << 20) // read_bytes))
+    base = [to_dev(a, dt, "cuda") for a in (pi.hidden, pi.w_dkv, pi.w_kr)]
+    sets = [base] + [[t.clone() for t in base] for _ in range(copies - 1)]
+    nbytes = mla.mla_kv_produce_workspace_size(cfg, M, d)
+    ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device="cuda")
+    lengths = torch.from_numpy(bt.lengths.astype("int32")).cuda()
+    cap = int(bt.seq_lens.max())
+
+    def call(k):
+        h, wd, wk = sets[k]
+        st = steps[k % len(steps)]
+        mla.mla_kv_produce(cfg, h, wd, wk, st.pool, st.block_table, lengths, cap, ws)
+
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for k in range(copies):
+            call(k)
+    stream = torch.cuda.current_stream()
+    for _ in range(2):
+        g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    reps = 5
+    e0.record(stream)
+    for _ in range(reps):
+        g.replay()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / (reps * copies)
+    algo = read_bytes + M * N * elem
+    return {"call": "mla_kv_produce", "kernels": "kv_proj_mfma_kernel + kv_rope_append_kernel",
+            "d_model": d, "tokens": M, "us": us, "bound": "hbm",
+            "algorithmic_bytes": algo, "GBps": algo / (us * 1e-6) / 1e9,
+            "frac": algo / (us * 1e-6) / 1e9 / HBM_PEAK_GBPS,
+            "k_split_workspace_bytes": nbytes, "rotated_copies": copies}
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -273,6 +323,8 @@ def main() -> int:
         "phases_us": {"absorb_q": ms_absorb * 1e3, "cache_append": ms_append * 1e3,
                       "decode": ms_decode * 1e3, "out_proj": ms_out * 1e3},
     }
+    if w.d_model > 0:
+        line["producer"] = producer_phase(w, bt, steps, torch, mla)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
     else:

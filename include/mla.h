@@ -8,6 +8,10 @@
  *                     softmax, and sum the cached latents (split-KV + merge)
  *   mla_out_proj      up-project the latent output once per head through W^UV
  *
+ * and, on the input side, mla_kv_produce (the cached row made from the token's
+ * hidden vector, with RoPE on k^R, written into the cache in place of
+ * mla_cache_append) and mla_rope (the same rotation for the query's rotary part).
+ *
  * The method is the inference path of "Attention, Part 2: MQA, GQA and MLA",
  * section "The trick that makes it fast: never rebuild at all": only the latent c
  * (width d_c) and the decoupled rotary key k^R (width d_rope) are cached per token
@@ -176,6 +180,54 @@ mla_status mla_decode(const mla_config* cfg, const void* q_abs, const void* pool
  */
 mla_status mla_out_proj(const mla_config* cfg, const float* o_lat, const void* w_uv,
                         void* out, int32_t M, void* stream);
+
+/*
+ * mla_kv_produce -- the producer step before the cache: each new token's row is
+ * made from its hidden vector h and written into the paged cache, replacing
+ * mla_cache_append when the rows are not already at hand.
+ *
+ *   c   = W^DKV h                 ("Multi-head latent attention (MLA)", section 2)
+ *   k^R = RoPE(W^KR h, p)         (same page, section 3; "Attention, Part 2",
+ *                                  section "The MLA equations" and its code)
+ *   pool[block_table[b, p / bs], p % bs, :] = [c | k^R],  p = seq_lens[b] + i
+ *
+ * RoPE turns each consecutive pair (x[2i], x[2i+1]) of k^R by the angle
+ * p * rope_base^(-2i/d_rope) ("Attention, Part 2", section "Why position needs
+ * its own key", one pair turned by m*theta; the angle rule is RoFormer's).  The
+ * latent is never rotated.  rope_base 0 selects 10000; otherwise it must be a
+ * finite value > 1.
+ *
+ * hidden [B, T_new, d_model], w_dkv [d_c, d_model], w_kr [d_rope, d_model]
+ * (cfg->dtype; the weights of linear layers d_model -> d_c and d_model -> d_rope),
+ * pool / block_table / seq_lens / max_seq_len_host as for mla_cache_append
+ * (seq_lens BEFORE the append, not modified; rows whose page or page id is out
+ * of range are skipped on the device).  d_c and d_rope must be even.  Products
+ * accumulate in fp32 and are rounded once to cfg->dtype.  workspace (device, fp32
+ * partial sums) must hold mla_kv_produce_workspace_size(cfg, B * T_new, d_model)
+ * bytes (MLA_ERR_WORKSPACE otherwise); its contents on entry do not matter.
+ * B * T_new == 0 launches nothing.
+ */
+size_t mla_kv_produce_workspace_size(const mla_config* cfg, int32_t M, int32_t d_model);
+mla_status mla_kv_produce(const mla_config* cfg, const void* hidden, int32_t d_model,
+                          const void* w_dkv, const void* w_kr, float rope_base, void* pool,
+                          int32_t num_blocks, const int32_t* block_table, int32_t max_blocks,
+                          const int32_t* seq_lens, int32_t B, int32_t T_new,
+                          int32_t max_seq_len_host, void* workspace, size_t workspace_bytes,
+                          void* stream);
+
+/*
+ * mla_rope -- the rotation of the query's decoupled rotary part, in place: for
+ * m < M and h < heads, x[m, h, 2i .. 2i+1] is turned by positions[m] *
+ * rope_base^(-2i/d_rope), the same rotation mla_kv_produce applies to k^R (the
+ * score's positional term pairs the rotated query with the rotated key:
+ * "Attention, Part 2", section "Why position needs its own key").  Apply it to
+ * q_rope before mla_absorb_q.  x [M, heads, d_rope] (device, cfg->dtype),
+ * positions [M] (device int32; for decode, token i of sequence b is at
+ * seq_lens_before[b] + i).  rope_base as for mla_kv_produce; d_rope must be
+ * even.  M, heads or d_rope == 0 launches nothing.
+ */
+mla_status mla_rope(const mla_config* cfg, void* x, int32_t heads, const int32_t* positions,
+                    int32_t M, float rope_base, void* stream);
 
 /*
  * Debug and test helpers.

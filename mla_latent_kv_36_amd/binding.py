@@ -56,6 +56,10 @@ _SIGNATURES = {
     "mla_out_proj": (_I, [_CFG, _P, _P, _P, _I, _P]),
     "mla_gather_rows": (_I, [_CFG, _P, _I, _P, _I, _P, _I, _I, _P, _P]),
     "mla_validate_block_table": (_I, [_P, _I, _I, _P, _I, _I, _P, _P]),
+    "mla_kv_produce_workspace_size": (ctypes.c_size_t, [_CFG, _I, _I]),
+    "mla_kv_produce": (_I, [_CFG, _P, _I, _P, _P, ctypes.c_float, _P, _I, _P, _I, _P, _I, _I,
+                            _I, _P, ctypes.c_size_t, _P]),
+    "mla_rope": (_I, [_CFG, _P, _I, _P, _I, ctypes.c_float, _P]),
 }
 
 
@@ -198,3 +202,42 @@ def mla_validate_block_table(block_table: torch.Tensor, seq_lens: torch.Tensor,
     _check(load().mla_validate_block_table(_ptr(block_table), block_table.shape[0],
                                            block_table.shape[1], _ptr(seq_lens), block_size,
                                            num_blocks, _ptr(err_flag), _stream(stream)))
+
+
+def mla_kv_produce_workspace_size(cfg: MlaConfig, M: int, d_model: int) -> int:
+    n = int(load().mla_kv_produce_workspace_size(ctypes.byref(cfg), M, d_model))
+    if n == ctypes.c_size_t(-1).value:
+        raise RuntimeError("mla_kv_produce_workspace_size: invalid arguments")
+    return n
+
+
+def mla_kv_produce(cfg: MlaConfig, hidden: torch.Tensor, w_dkv: torch.Tensor,
+                   w_kr: Optional[torch.Tensor], pool: torch.Tensor, block_table: torch.Tensor,
+                   seq_lens: torch.Tensor, max_seq_len_host: int, workspace: torch.Tensor,
+                   rope_base: float = 0.0, stream=None) -> None:
+    """Rows [W^DKV h | RoPE(W^KR h)] of hidden [B, T_new, d_model] written after
+    each sequence's seq_lens[b] rows.  workspace: a device byte tensor of at
+    least mla_kv_produce_workspace_size(cfg, B * T_new, d_model) bytes."""
+    dt = _TORCH_DTYPE[cfg.dtype]
+    _dev(hidden, dt, "hidden"), _dev(w_dkv, dt, "w_dkv"), _dev(pool, dt, "pool")
+    if w_kr is not None:
+        _dev(w_kr, dt, "w_kr")
+    _dev(block_table, torch.int32, "block_table"), _dev(seq_lens, torch.int32, "seq_lens")
+    B, T_new, d_model = hidden.shape
+    _check(load().mla_kv_produce(ctypes.byref(cfg), _ptr(hidden), d_model, _ptr(w_dkv),
+                                 _ptr(w_kr), float(rope_base), _ptr(pool), pool.shape[0],
+                                 _ptr(block_table), block_table.shape[1], _ptr(seq_lens), B,
+                                 T_new, int(max_seq_len_host), _ptr(workspace),
+                                 workspace.numel() * workspace.element_size(), _stream(stream)))
+
+
+def mla_rope(cfg: MlaConfig, x: torch.Tensor, positions: torch.Tensor, rope_base: float = 0.0,
+             stream=None) -> None:
+    """In place: x [M, heads, d_rope], pair i of row m turned by
+    positions[m] * base^(-2i/d_rope)."""
+    dt = _TORCH_DTYPE[cfg.dtype]
+    _dev(x, dt, "x"), _dev(positions, torch.int32, "positions")
+    M, heads = x.shape[0], x.shape[1]
+    _check(load().mla_rope(ctypes.byref(cfg), _ptr(x), heads, _ptr(positions), M,
+                           float(rope_base), _stream(stream)))
+

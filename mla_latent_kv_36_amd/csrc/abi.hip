@@ -114,7 +114,7 @@ const char* mla_status_string(int32_t status) {
   }
 }
 
-int32_t mla_abi_version(void) { return 1; }
+int32_t mla_abi_version(void) { return 2; }
 
 mla_status mla_absorb_q(const mla_config* cfg, const void* q_nope, const void* q_rope,
                         const void* w_uk, void* q_abs, int32_t M, void* stream) {
@@ -280,3 +280,76 @@ mla_status mla_validate_block_table(const int32_t* block_table, int32_t B, int32
 }
 
 }  // extern "C"
+
+namespace {
+constexpr float kDefaultRopeBase = 10000.0f;
+// The producer's k split aims at half the compute units: a longer k range per
+// workgroup, but half the partial sums to write and add (measured faster at
+// the V2-scale width than one workgroup per compute unit).
+constexpr int kProduceWorkgroups = kCUs / 2;
+
+// 0 selects the default base; anything else must be a finite value > 1
+bool rope_base_of(float in, float* out) {
+  if (in == 0.0f) {
+    *out = kDefaultRopeBase;
+    return true;
+  }
+  if (!(in > 1.0f) || !isfinite(in)) return false;
+  *out = in;
+  return true;
+}
+}  // namespace
+
+extern "C" size_t mla_kv_produce_workspace_size(const mla_config* cfg, int32_t M,
+                                                int32_t d_model) {
+  if (check_cfg(cfg) != MLA_OK || M < 0 || d_model <= 0) return (size_t)-1;
+  if (M == 0) return 0;
+  const int ks = mla::kv_produce_ksplit(cfg->dtype, M, d_model, cfg->d_c, cfg->d_rope, kProduceWorkgroups);
+  return round256((size_t)ks * M * (cfg->d_c + cfg->d_rope) * sizeof(float));
+}
+
+extern "C" mla_status mla_kv_produce(const mla_config* cfg, const void* hidden, int32_t d_model,
+                                     const void* w_dkv, const void* w_kr, float rope_base,
+                                     void* pool, int32_t num_blocks, const int32_t* block_table,
+                                     int32_t max_blocks, const int32_t* seq_lens, int32_t B,
+                                     int32_t T_new, int32_t max_seq_len_host, void* workspace,
+                                     size_t workspace_bytes, void* stream) {
+  mla_status st = check_cfg(cfg);
+  if (st != MLA_OK) return st;
+  float base;
+  if (B < 0 || T_new < 0 || d_model <= 0 || num_blocks <= 0 || max_blocks <= 0 ||
+      max_seq_len_host < 0 || (cfg->d_c & 1) || (cfg->d_rope & 1) || !rope_base_of(rope_base, &base))
+    return MLA_ERR_DIM;
+  if ((int64_t)max_seq_len_host > (int64_t)max_blocks * cfg->block_size) return MLA_ERR_CAPACITY;
+  if ((int64_t)B * T_new > 0x7fffffffLL) return MLA_ERR_DIM;
+  const int M = B * T_new;
+  if (M == 0) return MLA_OK;
+  if (hidden == nullptr || w_dkv == nullptr || (cfg->d_rope > 0 && w_kr == nullptr) ||
+      pool == nullptr || block_table == nullptr || seq_lens == nullptr)
+    return MLA_ERR_NULL;
+  if (!aligned16(hidden) || !aligned16(w_dkv) || (w_kr != nullptr && !aligned16(w_kr)) ||
+      !aligned16(pool) || !aligned16(block_table) || !aligned16(seq_lens) ||
+      (workspace != nullptr && !aligned16(workspace)))
+    return MLA_ERR_ALIGN;
+  const size_t need = mla_kv_produce_workspace_size(cfg, M, d_model);
+  if (workspace == nullptr || workspace_bytes < need) return MLA_ERR_WORKSPACE;
+  const int ks = mla::kv_produce_ksplit(cfg->dtype, M, d_model, cfg->d_c, cfg->d_rope, kProduceWorkgroups);
+  return hip_status(mla::launch_kv_produce(
+      cfg->dtype, hidden, d_model, w_dkv, w_kr, base, static_cast<float*>(workspace), ks, pool,
+      num_blocks, block_table, max_blocks, seq_lens, B, T_new, cfg->block_size, cfg->d_c,
+      cfg->d_rope, static_cast<hipStream_t>(stream)));
+}
+
+extern "C" mla_status mla_rope(const mla_config* cfg, void* x, int32_t heads,
+                               const int32_t* positions, int32_t M, float rope_base,
+                               void* stream) {
+  mla_status st = check_cfg(cfg);
+  if (st != MLA_OK) return st;
+  float base;
+  if (M < 0 || heads < 0 || (cfg->d_rope & 1) || !rope_base_of(rope_base, &base)) return MLA_ERR_DIM;
+  if (M == 0 || heads == 0 || cfg->d_rope == 0) return MLA_OK;
+  if (x == nullptr || positions == nullptr) return MLA_ERR_NULL;
+  if (!aligned16(x) || !aligned16(positions)) return MLA_ERR_ALIGN;
+  return hip_status(mla::launch_rope(cfg->dtype, x, positions, M, heads, cfg->d_rope, base,
+                                     static_cast<hipStream_t>(stream)));
+}

@@ -26,8 +26,8 @@ struct DecodeParams {
   float scale_log2;           // softmax scale * log2(e)
 };
 
-// The MFMA kernel covers bf16, d_c = 512, d_rope = 64, 64-token pages and
-// T*H a multiple of 64.
+// The MFMA kernel covers bf16, d_c = 512, d_rope = 64, 64-token pages and H
+// a multiple of 64.
 bool decode_mfma_supported(int dtype, int d_c, int d_r, int block_size, int T, int H);
 hipError_t launch_decode_mfma(const DecodeParams& p, hipStream_t stream);
 hipError_t launch_decode_generic(const DecodeParams& p, int dtype, hipStream_t stream);
@@ -45,6 +45,18 @@ hipError_t launch_append(void* pool, int num_blocks, const int32_t* block_table,
 hipError_t launch_gather(const void* pool, int num_blocks, const int32_t* block_table,
                          int max_blocks, const int32_t* seq_lens, int B, int cap,
                          int block_size, int row_bytes, void* dense, hipStream_t stream);
+// Producer step: cached rows [W^DKV h | RoPE(W^KR h)] into the pool.  `part`
+// holds ksplit * M * (d_c + d_r) fp32 partial sums; ksplit comes from
+// kv_produce_ksplit (1 for the generic kernel).
+bool kv_proj_mfma_supported(int dtype, int d_model);
+int kv_produce_ksplit(int dtype, int M, int d_model, int d_c, int d_r, int cus);
+hipError_t launch_kv_produce(int dtype, const void* hidden, int d_model, const void* w_dkv,
+                             const void* w_kr, float rope_base, float* part, int ksplit,
+                             void* pool, int num_blocks, const int32_t* block_table,
+                             int max_blocks, const int32_t* seq_lens, int B, int T_new,
+                             int block_size, int d_c, int d_r, hipStream_t stream);
+hipError_t launch_rope(int dtype, void* x, const int32_t* positions, int M, int heads, int d_r,
+                       float rope_base, hipStream_t stream);
 hipError_t launch_validate(const int32_t* block_table, int B, int max_blocks,
                            const int32_t* seq_lens, int block_size, int num_blocks,
                            int32_t* err_flag, hipStream_t stream);

@@ -52,7 +52,7 @@ def test_status_strings(lib):
         s = mla.mla_status_string(code)
         assert s.startswith("MLA_")
     assert "unknown" in mla.mla_status_string(99)
-    assert mla.mla_abi_version() == 1
+    assert mla.mla_abi_version() == 2
 
 
 def _decode(lib, cfg, q=FAKE, pool=FAKE, nb=10, bt=FAKE, mb=4, sl=FAKE, cap=256, B=2, T=1,
@@ -140,6 +140,44 @@ def test_absorb_and_out_proj_validation(lib):
     assert lib.mla_out_proj(ctypes.byref(v3_cfg(d_v=0)), FAKE, FAKE, FAKE, 4, None) == DIM
     assert lib.mla_out_proj(c, FAKE, FAKE, FAKE_MIS, 4, None) == ALIGN
     assert lib.mla_out_proj(c, FAKE, FAKE, FAKE, 0, None) == OK
+
+
+def test_producer_and_rope_validation(lib):
+    cfg = v3_cfg()
+    c = ctypes.byref(cfg)
+    f = lib.mla_kv_produce
+    ws = lib.mla_kv_produce_workspace_size
+    # workspace: the library's k split x M x (d_c + d_rope) fp32, 256-byte rounded
+    need = ws(c, 4, 5120)
+    assert need > 0 and need % 256 == 0 and need >= 4 * 576 * 4
+    assert ws(c, 0, 5120) == 0
+    assert ws(c, 4, 0) == ctypes.c_size_t(-1).value
+    # fp32 configs take the generic kernel: one partial slot
+    f32 = ctypes.byref(v3_cfg(dtype=0))
+    assert ws(f32, 4, 5120) == -(-(4 * 576 * 4) // 256) * 256
+    args = lambda **k: [k.get("cfg", c), k.get("hidden", FAKE), k.get("d", 5120),
+                        k.get("w_dkv", FAKE), k.get("w_kr", FAKE), k.get("base", 0.0),
+                        k.get("pool", FAKE), 10, FAKE, 4, FAKE, k.get("B", 2), k.get("T", 2),
+                        k.get("cap", 10), k.get("ws", FAKE), k.get("wsb", need), None]
+    assert f(*args(cap=4 * 64 + 1)) == CAP
+    assert f(*args(hidden=None)) == NULL
+    assert f(*args(w_kr=None)) == NULL                       # d_rope > 0 needs W^KR
+    assert f(*args(pool=FAKE_MIS)) == ALIGN
+    assert f(*args(d=0)) == DIM
+    assert f(*args(base=-1.0)) == DIM
+    assert f(*args(base=1.0)) == DIM
+    assert f(*args(base=float("inf"))) == DIM
+    assert f(*args(cfg=ctypes.byref(v3_cfg(d_rope=63)))) == DIM   # odd rotary width
+    assert f(*args(ws=None)) == WS
+    assert f(*args(wsb=need - 1)) == WS
+    assert f(*args(T=0)) == OK                                  # no new tokens
+    r = lib.mla_rope
+    assert r(c, None, 128, FAKE, 4, 0.0, None) == NULL
+    assert r(c, FAKE, 128, FAKE_MIS, 4, 0.0, None) == ALIGN
+    assert r(c, FAKE, 128, FAKE, 4, -2.0, None) == DIM
+    assert r(c, FAKE, -1, FAKE, 4, 0.0, None) == DIM
+    assert r(c, FAKE, 128, FAKE, 0, 0.0, None) == OK
+    assert r(ctypes.byref(v3_cfg(d_rope=0)), FAKE, 128, FAKE, 4, 0.0, None) == OK
 
 
 def test_debug_helpers_validation(lib):

@@ -1,0 +1,143 @@
+"""GPU parity of the producer step (mla_kv_produce) and the query rotation
+(mla_rope) through the C ABI, against the fp64 oracle on the same seeded
+inputs.
+
+* produced rows [W^DKV h | RoPE(W^KR h)] in their page slots: per element within
+  bf16 rounding (2^-8 relative) plus an fp32-accumulation floor, or 1e-5
+  relative for fp32 caches; every other pool slot bit-for-bit unchanged
+  (poison included);
+* the k split of the MFMA kernel sums in a fixed order: reruns are bit-exact;
+* rotation at positions up to 131,071, where an fp32 angle would be off.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from mla_latent_kv_36_amd import binding as mla
+from workloads import TINY, V2_MULTI, make_inputs, make_producer_inputs
+from workloads.device import to_dev, upload
+
+from gpu_util import cfg_of, dev_bits, note, pool_bits
+
+pytestmark = pytest.mark.gpu
+TDT = {"bf16": torch.bfloat16, "f32": torch.float32}
+
+CASES = {
+    # MFMA kernel: bf16, d = 5120 (the V2-scale width), ragged lengths and pages
+    "v2_reduced": V2_MULTI.scaled(B=3, N=300),
+    # more tokens than one 64-row tile, T = 1
+    "v2_many_tokens": V2_MULTI.scaled(B=70, T=1, N=100),
+    # generic kernel: a width that is not a multiple of 32
+    "bf16_odd_width": V2_MULTI.scaled(B=2, N=90, d_model=200),
+    # fp32 cache: the generic kernel
+    "tiny_f32": TINY.scaled(B=2, T=3, d_model=96),
+}
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    mla.load()
+
+
+def _run_produce(w, bt, pi, dev):
+    cfg = cfg_of(w)
+    dt = TDT[w.dtype]
+    hidden = to_dev(pi.hidden, dt, "cuda")
+    w_dkv, w_kr = to_dev(pi.w_dkv, dt, "cuda"), to_dev(pi.w_kr, dt, "cuda")
+    M = w.B * w.T
+    nbytes = mla.mla_kv_produce_workspace_size(cfg, M, w.d_model)
+    ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device="cuda")
+    lengths = torch.from_numpy(bt.lengths.astype(np.int32)).cuda()
+    mla.mla_kv_produce(cfg, hidden, w_dkv, w_kr, dev["pool"], dev["block_table"], lengths,
+                       int(bt.seq_lens.max()), ws)
+    torch.cuda.synchronize()
+
+
+def _check_rows(w, bt, pi, pool_dev):
+    ref = oracle.produce_append_ref(bt.pool.astype(np.float64), bt.block_table, bt.lengths,
+                                    pi.hidden, pi.w_dkv, pi.w_kr, w.block_size)
+    got_bits = dev_bits(pool_dev)
+    ref_bits = pool_bits(bt.pool, w.dtype)
+    written = np.zeros(bt.pool.shape[:2], dtype=bool)
+    for b in range(w.B):
+        for i in range(w.T):
+            p = int(bt.lengths[b]) + i
+            written[bt.block_table[b, p // w.block_size], p % w.block_size] = True
+    # untouched slots: bit for bit
+    assert np.array_equal(got_bits[~written], ref_bits[~written])
+    got = pool_dev.float().cpu().numpy()[written]
+    want = ref[written]
+    mx = float(np.max(np.abs(want)))
+    if w.dtype == "bf16":
+        bound = 2.0 ** -8 * np.abs(want) + 1e-4 * mx
+    else:
+        bound = 1e-5 * np.abs(want) + 1e-6 * mx
+    err = np.abs(got - want)
+    assert np.all(err <= bound), float(np.max(err / np.maximum(bound, 1e-30)))
+
+
+@pytest.mark.parametrize("name", list(CASES))
+def test_kv_produce_matches_oracle(name):
+    w = CASES[name]
+    bt = make_inputs(w)
+    pi = make_producer_inputs(w)
+    note(f"kv_produce {name} M={w.B * w.T} d={w.d_model}")
+    dev = upload(bt)
+    _run_produce(w, bt, pi, dev)
+    _check_rows(w, bt, pi, dev["pool"])
+
+
+def test_kv_produce_full_size_v2():
+    """The V2-scale producer step at full size: 32 sequences x 4 new tokens,
+    d = 5120, on 8,192-row caches; every produced row checked."""
+    w = V2_MULTI
+    bt = make_inputs(w)
+    pi = make_producer_inputs(w)
+    note("kv_produce v2 full size")
+    dev = upload(bt)
+    _run_produce(w, bt, pi, dev)
+    _check_rows(w, bt, pi, dev["pool"])
+
+
+def test_kv_produce_rerun_bit_exact():
+    """The k-split partial sums are added in split order: two runs into fresh
+    copies of the pool give identical bits."""
+    w = CASES["v2_many_tokens"]
+    bt = make_inputs(w)
+    pi = make_producer_inputs(w)
+    note("kv_produce rerun")
+    d1, d2 = upload(bt), upload(bt)
+    _run_produce(w, bt, pi, d1)
+    _run_produce(w, bt, pi, d2)
+    assert np.array_equal(dev_bits(d1["pool"]), dev_bits(d2["pool"]))
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_rope_matches_oracle(dtype):
+    w = V2_MULTI.scaled(dtype=dtype)
+    cfg = cfg_of(w)
+    rng = np.random.default_rng(31)
+    M, H = 37, 128
+    x = rng.standard_normal((M, H, w.d_r)).astype(np.float32)
+    if dtype == "bf16":
+        from workloads import bf16_round
+        x = bf16_round(x)
+    pos = np.concatenate([[0, 1, 2, 4095, 4096, 65535, 131071],
+                          rng.integers(0, 131072, M - 7)]).astype(np.int32)
+    note(f"rope {dtype}")
+    xd = to_dev(x, TDT[dtype], "cuda")
+    mla.mla_rope(cfg, xd, torch.from_numpy(pos).cuda())
+    torch.cuda.synchronize()
+    got = xd.float().cpu().numpy()
+    want = oracle.rope_ref(x.astype(np.float64).transpose(1, 0, 2), pos).transpose(1, 0, 2)
+    if dtype == "bf16":
+        bound = 2.0 ** -8 * np.abs(want) + 1e-6
+    else:
+        # fp32 rotation of inputs up to ~5 in size: a few ulp of the two products
+        bound = 1e-6 * np.abs(want) + 1e-6
+    assert np.all(np.abs(got - want) <= bound)
+    # position 0 leaves the row bit for bit
+    assert np.array_equal(got[0], x[0])
