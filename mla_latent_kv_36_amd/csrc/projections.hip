@@ -158,25 +158,44 @@ __global__ __launch_bounds__(PJ_NT) void absorb_q_mfma_kernel(
 
   // B fragments (query rows) of the first tile are requested before the
   // weight, so both loads are in flight together.
+  // The loads are unconditional, on a clamped row and offset, and what lies
+  // outside is replaced by zeros afterwards: conditional loads would each be
+  // waited for before the next is issued.
   auto load_q = [&](int m0, bf16x8* bq) {
     const int m = m0 + i16;
-    const uint16_t* qrow = q_nope + ((size_t)m * H + h) * d_n;
+    const uint16_t* qrow = q_nope + ((size_t)min(m, mend - 1) * H + h) * d_n;
+    bf16x8 raw[AB_KS];
+#pragma unroll
+    for (int ks = 0; ks < AB_KS; ++ks) raw[ks] = load_bf16x8(qrow + min(32 * ks + 8 * g, d_n - 8));
 #pragma unroll
     for (int ks = 0; ks < AB_KS; ++ks) {
-      bq[ks] = bf16x8{};
-      const int d = 32 * ks + 8 * g;
-      if (ks < nks && m < mend && d < d_n) bq[ks] = load_bf16x8(qrow + d);
+      const bool in = ks < nks && m < mend && 32 * ks + 8 * g < d_n;
+      bq[ks] = in ? raw[ks] : bf16x8{};
     }
   };
   bf16x8 bq[AB_KS];
   load_q(mbeg, bq);
 
+  // the weight slice: every piece is loaded (clamped, unconditional) before
+  // the first is stored, so staging costs one memory latency
   const uint16_t* wsrc = w_uk + (size_t)h * d_n * d_c + cb * AB_CT;
-  for (int i = tid; i < nks * 32 * (AB_CT / 8); i += PJ_NT) {
+  constexpr int ST = AB_KS * 32 * (AB_CT / 8) / PJ_NT;  // pieces per thread, at most
+  const int pieces = nks * 32 * (AB_CT / 8);
+  u32x4 sv[ST];
+#pragma unroll
+  for (int u = 0; u < ST; ++u) {
+    const int i = tid + u * PJ_NT;
     const int d = i / (AB_CT / 8), ch = i % (AB_CT / 8);
-    u32x4 v = {0u, 0u, 0u, 0u};
-    if (d < d_n) v = *reinterpret_cast<const u32x4*>(wsrc + (size_t)d * d_c + ch * 8);
-    *reinterpret_cast<u32x4*>(wl + d * AB_LD + ch * 16) = v;
+    sv[u] = *reinterpret_cast<const u32x4*>(wsrc + (size_t)min(d, d_n - 1) * d_c + ch * 8);
+  }
+#pragma unroll
+  for (int u = 0; u < ST; ++u) {
+    const int i = tid + u * PJ_NT;
+    const int d = i / (AB_CT / 8), ch = i % (AB_CT / 8);
+    if (i < pieces) {
+      const u32x4 z = {0u, 0u, 0u, 0u};
+      *reinterpret_cast<u32x4*>(wl + d * AB_LD + ch * 16) = d < d_n ? sv[u] : z;
+    }
   }
   __syncthreads();
 
@@ -246,23 +265,38 @@ __global__ __launch_bounds__(PJ_NT) void out_proj_mfma_kernel(
   const int nks = d_c >> 5;
   const int vrow = vb * OP_VT + 16 * wave + i16;  // A row of this lane
 
+  // W^UV fragments: unconditional loads on a clamped row and k-step, zeros
+  // selected afterwards (conditional loads would be waited for one by one)
   bf16x8 a[OP_KS];
-  const uint16_t* wrow = w_uv + ((size_t)h * d_v + vrow) * d_c + 8 * g;
+  const uint16_t* wrow = w_uv + ((size_t)h * d_v + min(vrow, d_v - 1)) * d_c + 8 * g;
 #pragma unroll
-  for (int ks = 0; ks < OP_KS; ++ks) {
-    a[ks] = bf16x8{};
-    if (ks < nks && vrow < d_v) a[ks] = load_bf16x8(wrow + 32 * ks);
-  }
+  for (int ks = 0; ks < OP_KS; ++ks) a[ks] = load_bf16x8(wrow + 32 * min(ks, nks - 1));
+#pragma unroll
+  for (int ks = 0; ks < OP_KS; ++ks)
+    if (!(ks < nks && vrow < d_v)) a[ks] = bf16x8{};
 
   const int v0 = vb * OP_VT + 16 * wave + 4 * g;  // this lane's 4 output columns
   const int q4 = d_c >> 2;                        // float4 chunks per row
   for (int m0 = mbeg; m0 < mend; m0 += 16) {
-    // stage rows m0 .. m0+15 (zeros past mend) as bf16 hi / lo
-    for (int i = tid; i < 16 * q4; i += PJ_NT) {
+    // stage rows m0 .. m0+15 (zeros past mend) as bf16 hi / lo; a thread's
+    // loads (up to OP_ST, on clamped rows) are all issued before the first
+    // is used
+    constexpr int OP_ST = 16 * (32 * OP_KS / 4) / PJ_NT;
+    f32x4 xs[OP_ST];
+#pragma unroll
+    for (int u = 0; u < OP_ST; ++u) {
+      const int i = min(tid + u * PJ_NT, 16 * q4 - 1);
       const int r = i / q4, c4 = i - r * q4;
-      f32x4 x = {0.f, 0.f, 0.f, 0.f};
-      if (m0 + r < mend)
-        x = *reinterpret_cast<const f32x4*>(o_lat + ((size_t)(m0 + r) * H + h) * d_c + 4 * c4);
+      xs[u] = *reinterpret_cast<const f32x4*>(
+          o_lat + ((size_t)min(m0 + r, mend - 1) * H + h) * d_c + 4 * c4);
+    }
+#pragma unroll
+    for (int u = 0; u < OP_ST; ++u) {
+      const int i = tid + u * PJ_NT;
+      if (i >= 16 * q4) continue;
+      const int r = i / q4, c4 = i - r * q4;
+      f32x4 x = xs[u];
+      if (m0 + r >= mend) x = f32x4{0.f, 0.f, 0.f, 0.f};
       u16x4 hb, lb;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
