@@ -458,32 +458,24 @@ __global__ __launch_bounds__(NT, 1) void decode_mfma_kernel(const DecodeParams p
       for (int q = valid * 64 + zt; q < UNIT * 64; q += 128) dl[q] = z;
     };
 
+    // Only units 0 and 1 are requested before the first barrier: every
+    // workgroup starts at once, and unit 0 (scored in step -2) lands sooner
+    // when it does not queue behind units 2 and 3 of the whole chip.  Unit u
+    // is then issued in step u - 4, units 2 and 3 in steps -2 and -1.
     issue(0, page_raw(0));
     if (U > 1) issue(1, page_raw(1));
-    if (U > 2) issue(2, page_raw(2));
-    if (U > 3) issue(3, page_raw(3));
-    int raw_next = page_raw(4);
-    // unit 0 lands before B0 (its scores run in step -2); units 1..3 may
-    // still be in flight
-    if (U > 3) wait_vmcnt<3 * COPIES>();
-    else if (U > 2) wait_vmcnt<2 * COPIES>();
-    else if (U > 1) wait_vmcnt<COPIES>();
-    else wait_vmcnt<0>();
+    int raw_next = page_raw(2);
+    if (U > 1) wait_vmcnt<COPIES>(); else wait_vmcnt<0>();  // unit 0 landed
     lds_barrier();                         // B0
     for (int j = -2; j < U; ++j) {
-      if (j >= 0 && j + 4 < U) {
+      if (j + 4 < U) {
         issue(j + 4, raw_next);
         raw_next = page_raw(j + 5);
       }
       if (j + 2 >= 0 && j + 2 < U) zero_tail(j + 2);  // landed by E(j-1) (B0 for unit 0)
-      // unit j+3 lands before E(j): the units issued after it may stay in
-      // flight -- units 2 and 3 in step -2, unit j+4 from step -1 on
+      // unit j+3 lands before E(j); only unit j+4 may stay in flight
       if (j + 3 < U) {
-        if (j == -2) {
-          if (U > 3) wait_vmcnt<2 * COPIES>(); else if (U > 2) wait_vmcnt<COPIES>(); else wait_vmcnt<0>();
-        } else {
-          if (j + 4 < U) wait_vmcnt<COPIES>(); else wait_vmcnt<0>();
-        }
+        if (j + 4 < U) wait_vmcnt<COPIES>(); else wait_vmcnt<0>();
       }
       lds_barrier();                       // E(j)
     }
