@@ -111,6 +111,9 @@ __device__ __forceinline__ s16x4 lds_tr16(const uint8_t* p) {
 // each wave waits only for its own LDS reads and writes (lgkmcnt(0)); copies
 // are waited for explicitly (vmcnt) before the barrier that publishes them.
 // The signal fences keep the compiler from moving memory accesses across.
+// Makes a uniform value live in a scalar register at this point (no code).
+__device__ __forceinline__ void pin_sgpr(int x) { asm volatile("" ::"s"(x)); }
+
 __device__ __forceinline__ void lds_barrier() {
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
   __builtin_amdgcn_s_waitcnt((0x7 << 4) | 0xF | (3 << 14));  // lgkmcnt(0)
@@ -370,10 +373,7 @@ __global__ __launch_bounds__(NT, 1) void decode_mfma_kernel(const DecodeParams p
 #pragma unroll
       for (int i = 0; i < QSTEPS; ++i) {
         const int kk = i < QSTEPS - LSTEPS ? LSTEPS + i : i - (QSTEPS - LSTEPS);
-        if (i == QSTEPS - LSTEPS && u + 1 < U) {
-          load_kr(u + 1, raw_next, krn);
-          raw_next = page_raw(u + 2);
-        }
+        if (i == QSTEPS - LSTEPS && u + 1 < U) load_kr(u + 1, raw_next, krn);
         bf16x8 k0, k1;
         if (kk < LSTEPS) {
           k0 = kf[kk % KDEPTH][0];
@@ -392,6 +392,12 @@ __global__ __launch_bounds__(NT, 1) void decode_mfma_kernel(const DecodeParams p
         acc[1][1] = mfma16(k1, qf[1][kk], acc[1][1]);
         __builtin_amdgcn_sched_barrier(0);
       }
+      // The page-table entry of unit u + 2 is requested only now: a scalar
+      // load in flight would turn every LDS wait of the loop above into a
+      // wait for all of them.  The barrier after this unit waits for it
+      // anyway, and pin_sgpr after that barrier keeps the compiler from
+      // sinking the load back into the next unit's loop.
+      raw_next = page_raw(u + 2);
       float* sdst = sm.s[u & 1];
 #pragma unroll
       for (int rt = 0; rt < 2; ++rt)
@@ -410,9 +416,11 @@ __global__ __launch_bounds__(NT, 1) void decode_mfma_kernel(const DecodeParams p
     for (int j = -2; j < U; j += 2) {
       if (j + 2 < U) scores(j + 2, kra, krb);
       lds_barrier();                       // E(j)
+      pin_sgpr(raw_next);
       if (j + 1 < U) {
         if (j + 3 < U) scores(j + 3, krb, kra);
         lds_barrier();                     // E(j+1)
+        pin_sgpr(raw_next);
       }
     }
     lds_barrier();                         // F
