@@ -199,9 +199,11 @@ __global__ __launch_bounds__(64 * CMB_ROWS) void combine_kernel(const DecodePara
     }
     // no visible row (ns == 0): o = 0, lse = -inf
     const float inv = ns > 0 ? 1.0f / den : 0.0f;
+    // streaming stores: o_lat is read by the next kernel (no L2 lines left
+    // dirty for the end-of-launch write-back)
     float* out = p.o_lat + (size_t)row * 512 + 4 * lane;
-    *reinterpret_cast<f32x4*>(out) = a0 * inv;
-    *reinterpret_cast<f32x4*>(out + 256) = a1 * inv;
+    __builtin_nontemporal_store(a0 * inv, reinterpret_cast<f32x4*>(out));
+    __builtin_nontemporal_store(a1 * inv, reinterpret_cast<f32x4*>(out + 256));
     if (lane == 0 && p.lse != nullptr) p.lse[row] = ns > 0 ? M + logf(den) : -INFINITY;
     return;
   }

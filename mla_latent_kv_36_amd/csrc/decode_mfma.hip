@@ -605,6 +605,9 @@ __global__ __launch_bounds__(NT, 1) void decode_mfma_kernel(const DecodeParams p
     lds_barrier();                         // F
     float* dst = direct ? p.o_lat + ((size_t)b * TH + rb) * DC
                         : p.part_o + (((size_t)b * S + s) * TH + rb) * DC;
+    // Streaming (non-temporal) stores: the rows are read by the next kernel,
+    // not by this one, and lines left dirty in L2 would all be written back
+    // at the end of the launch, which delays the next kernel's start.
 #pragma unroll
     for (int rt = 0; rt < 2; ++rt) {
 #pragma unroll
@@ -613,7 +616,8 @@ __global__ __launch_bounds__(NT, 1) void decode_mfma_kernel(const DecodeParams p
         const float inv = sm.lrow[row];
 #pragma unroll
         for (int dt = 0; dt < 4; ++dt)
-          dst[(size_t)row * DC + 128 * v + 32 * dt + l32] = o[rt][dt][r] * inv;
+          __builtin_nontemporal_store(o[rt][dt][r] * inv,
+                                      &dst[(size_t)row * DC + 128 * v + 32 * dt + l32]);
       }
     }
   }
