@@ -521,6 +521,16 @@ __global__ __launch_bounds__(NT, 1) void decode_mfma_kernel(const DecodeParams p
         for (int r = 0; r < 16; ++r) o[rt][dt][r] = 0.0f;
 
     bf16x8 vf[2][4];  // V of the unit whose P.V runs next
+    // the 16-token half ks of V(u) into vf[ks]
+    auto load_v_half = [&](int u, int ks) __attribute__((always_inline)) {
+      const uint8_t* lat = sm.lat[u & 3];
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt) {
+        const s16x4 v0 = lds_tr16(lat + voff[dt][0] + 16 * ks * 1024);
+        const s16x4 v1 = lds_tr16(lat + voff[dt][1] + 16 * ks * 1024);
+        vf[ks][dt] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
+      }
+    };
     auto load_v = [&](int u) {
       const uint8_t* lat = sm.lat[u & 3];
 #pragma unroll
@@ -529,8 +539,8 @@ __global__ __launch_bounds__(NT, 1) void decode_mfma_kernel(const DecodeParams p
         for (int dt = 0; dt < 4; ++dt) {
           const s16x4 v0 = lds_tr16(lat + voff[dt][0] + 16 * ks * 1024);
           const s16x4 v1 = lds_tr16(lat + voff[dt][1] + 16 * ks * 1024);
-          const short vv[8] = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
-          vf[ks][dt] = __builtin_bit_cast(bf16x8, vv);
+          // a plain concatenation: no instruction reads the loaded registers
+          vf[ks][dt] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
         }
     };
     // P(u) and the rescale flags into registers (issued before the softmax of
@@ -547,7 +557,10 @@ __global__ __launch_bounds__(NT, 1) void decode_mfma_kernel(const DecodeParams p
         pf[ks][1] = *reinterpret_cast<const bf16x8*>(pp + 32 * P_LD + poff + 16 * ks);
       }
     };
-    auto pv = [&](int u) {
+    // P(u) V(u); with `nxt` >= 0, the first half of V(nxt) replaces the first
+    // half of V(u) in registers as soon as the MFMAs that read it are issued,
+    // so that those reads complete under the second half's MFMAs.
+    auto pv = [&](int u, int nxt) __attribute__((always_inline)) {
       if (fl.x | fl.y | fl.z | fl.w) {
 #pragma unroll
         for (int rt = 0; rt < 2; ++rt) {
@@ -572,7 +585,18 @@ __global__ __launch_bounds__(NT, 1) void decode_mfma_kernel(const DecodeParams p
           o[0][dt] = mfma32(pf[ks][0], vf[ks][dt], o[0][dt]);
           o[1][dt] = mfma32(pf[ks][1], vf[ks][dt], o[1][dt]);
         }
+        if (ks == 0) {
+          __builtin_amdgcn_sched_barrier(0);
+          // P has arrived (the MFMAs above read it); with nothing older in
+          // flight, the MFMAs below wait for none of the V reads.  The wait
+          // is unconditional so that both paths reach the MFMAs in the same
+          // state.
+          __builtin_amdgcn_s_waitcnt((0x7 << 4) | 0xF | (3 << 14));  // lgkmcnt(0)
+          if (nxt >= 0) load_v_half(nxt, 0);
+          __builtin_amdgcn_sched_barrier(0);
+        }
       }
+      if (nxt >= 0) load_v_half(nxt, 1);
     };
 
     // Step j.  The softmax of unit j+1 and P(j) V(j) are independent; the two
@@ -584,13 +608,13 @@ __global__ __launch_bounds__(NT, 1) void decode_mfma_kernel(const DecodeParams p
       const bool next = j + 1 >= 0 && j + 1 < U;
       if (j >= 0) read_p(j);
       if (pv_first) {
-        if (j >= 0) pv(j);
-        if (next) load_v(j + 1);
+        if (j >= 0) pv(j, next ? j + 1 : -1);
+        else if (next) load_v(j + 1);
         if (next) softmax_unit(sm, j + 1, unit_valid(j + 1), v, lane, p.scale_log2, m_run, l_run);
       } else {
         if (next) softmax_unit(sm, j + 1, unit_valid(j + 1), v, lane, p.scale_log2, m_run, l_run);
-        if (j >= 0) pv(j);
-        if (next) load_v(j + 1);
+        if (j >= 0) pv(j, next ? j + 1 : -1);
+        else if (next) load_v(j + 1);
       }
       lds_barrier();                       // E(j)
     };
