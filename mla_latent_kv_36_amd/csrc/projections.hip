@@ -209,8 +209,8 @@ __global__ __launch_bounds__(PJ_NT) void absorb_q_mfma_kernel(
         const int d = 32 * ks + 8 * g + (i16 >> 2);
         const s16x4 v0 = lds_tr16(wl + d * AB_LD + 2 * col);
         const s16x4 v1 = lds_tr16(wl + (d + 4) * AB_LD + 2 * col);
-        const short vv[8] = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
-        a[ct][ks] = __builtin_bit_cast(bf16x8, vv);
+        // a plain concatenation: no instruction reads the loaded registers
+        a[ct][ks] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
       }
     }
 
