@@ -118,16 +118,27 @@ mla_status mla_cache_append(const mla_config* cfg, void* pool, int32_t num_block
                             int32_t T_new, int32_t max_seq_len_host, void* stream);
 
 /*
- * Split-KV planning for mla_decode.  The cached rows of each sequence are cut
- * into `num_splits` contiguous page ranges of equal page count (the last may be
- * shorter or empty); each range is attended on its own and the partial results
- * are merged by log-sum-exp.  mla_decode_num_splits returns the number the
- * library would choose (>= 1) for this batch; total_tokens_host is the sum of the
- * sequence lengths if the caller knows it, else 0.
+ * Split-KV planning for mla_decode.  Each range of cache rows is attended on
+ * its own and the partial results are merged by log-sum-exp.  Two plans:
+ *  - plain (num_splits > 0, or the library's choice for equal lengths): the
+ *    rows of every sequence are cut at the same points into `num_splits`
+ *    contiguous ranges of equal size (the last may be shorter or empty);
+ *  - balanced (the library's choice for the bf16 kernel with d_c = 512,
+ *    d_rope = 64, 64-row pages, H a multiple of 64, when the lengths may
+ *    differ: total_tokens_host is 0 or below B x max_seq_len_host): K work
+ *    items per 64-row query group (one per compute unit over the grid), and
+ *    each sequence gets splits in proportion to its length, chosen on the
+ *    device from seq_lens so that no item holds more than the smallest
+ *    bound on 32-row units the K items allow (at least 8 units).
+ * mla_decode_num_splits returns what the library would choose for this batch:
+ * the split count of a plain plan (>= 1) or K for a balanced one;
+ * total_tokens_host is the sum of the sequence lengths if the caller knows it,
+ * else 0.
  *
  * mla_decode_workspace_size returns the device workspace mla_decode needs for a
- * given num_splits (0 = the library's choice, as above); 0 bytes when no merge
- * is needed.  Returns (size_t)-1 for an invalid config.
+ * given num_splits (0 = the library's choice, as above) and the same
+ * total_tokens_host; 0 bytes when no merge is needed.  Returns (size_t)-1 for
+ * an invalid config.
  */
 int32_t mla_decode_num_splits(const mla_config* cfg, int32_t B, int32_t T,
                               int32_t max_seq_len_host, int64_t total_tokens_host);

@@ -44,8 +44,9 @@ bool use_mfma(const mla_config* c, int T) {
 // pipeline unit for the MFMA kernel, a page for the generic one).  Shorter
 // sequences use the leading ranges only.
 struct Plan {
-  int splits;
-  int chunk;  // rows per split
+  int splits;     // splits per sequence; a balanced plan: work items K per 64-row group
+  int chunk;      // rows per split (plain plan)
+  bool balanced;  // split sizes chosen per sequence on the device
 };
 
 int granule(const mla_config* c, int T) { return use_mfma(c, T) ? 32 : c->block_size; }
@@ -73,25 +74,45 @@ int heuristic_splits(const mla_config* c, int B, int T, int gran_max, int64_t to
   return (int)(s < 1 ? 1 : s);
 }
 
+// The library's choice for the MFMA kernel when the lengths may differ (their
+// total is unknown or below B x the longest): a balanced plan with one work
+// item per compute unit, kCUs / G per 64-row group, when that is more than
+// one per sequence.  Each sequence then gets a number of splits in proportion
+// to its length, so that no work item holds much more than the average.
 Plan make_plan(const mla_config* c, int B, int T, int max_seq_len, int64_t total_tokens,
                int num_splits) {
   const int g = granule(c, T);
   const int gran_max = max_seq_len > 0 ? (max_seq_len + g - 1) / g : 0;
+  if (num_splits == 0 && use_mfma(c, T) && gran_max > 1 && B > 0) {
+    const bool equal = total_tokens > 0 && total_tokens >= (int64_t)B * max_seq_len;
+    const int64_t groups = (int64_t)T * c->n_heads / 64;
+    const int64_t K = kCUs / groups;
+    if (!equal && K > B) return Plan{(int)K, 0, true};
+  }
   int want = num_splits > 0 ? num_splits : heuristic_splits(c, B, T, gran_max, total_tokens);
   if (want > gran_max) want = gran_max;
   if (want < 1) want = 1;
   const int chunk = gran_max > 0 ? (gran_max + want - 1) / want : 1;
   const int splits = gran_max > 0 ? (gran_max + chunk - 1) / chunk : 1;
-  return Plan{splits, chunk * g};
+  return Plan{splits, chunk * g, false};
 }
 
 size_t round256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-size_t partial_bytes(const mla_config* c, int B, int T, int splits, size_t* lse_offset) {
-  const size_t rows = (size_t)B * splits * T * c->n_heads;
+// Workspace of a split plan: partial outputs (fp32, d_c per row) and partial
+// log-sum-exps (fp32) for B x S x T*H rows (plain plan) or K x T*H rows (a
+// balanced plan, whose partials are indexed by work item), then, for a
+// balanced plan, the per-sequence table of 4 int32 the merge reads; each
+// region rounded up to 256 bytes.
+size_t partial_bytes(const mla_config* c, int B, int T, const Plan& pl, size_t* lse_offset,
+                     size_t* plan_offset) {
+  const size_t rows =
+      (pl.balanced ? (size_t)pl.splits : (size_t)B * pl.splits) * T * c->n_heads;
   const size_t o_bytes = round256(rows * c->d_c * sizeof(float));
+  const size_t lse_bytes = round256(rows * sizeof(float));
   if (lse_offset) *lse_offset = o_bytes;
-  return o_bytes + round256(rows * sizeof(float));
+  if (plan_offset) *plan_offset = o_bytes + lse_bytes;
+  return o_bytes + lse_bytes + (pl.balanced ? round256((size_t)B * 4 * sizeof(int32_t)) : 0);
 }
 
 mla_status hip_status(hipError_t e) { return e == hipSuccess ? MLA_OK : MLA_ERR_HIP; }
@@ -168,7 +189,7 @@ size_t mla_decode_workspace_size(const mla_config* cfg, int32_t B, int32_t T,
     return (size_t)-1;
   const Plan pl = make_plan(cfg, B, T, max_seq_len_host, total_tokens_host, num_splits);
   if (pl.splits <= 1) return 0;
-  return partial_bytes(cfg, B, T, pl.splits, nullptr);
+  return partial_bytes(cfg, B, T, pl, nullptr, nullptr);
 }
 
 mla_status mla_decode(const mla_config* cfg, const void* q_abs, const void* pool,
@@ -195,7 +216,8 @@ mla_status mla_decode(const mla_config* cfg, const void* q_abs, const void* pool
 
   const Plan pl = make_plan(cfg, B, T, max_seq_len_host, total_tokens_host, num_splits);
   size_t lse_off = 0;
-  const size_t need = pl.splits > 1 ? partial_bytes(cfg, B, T, pl.splits, &lse_off) : 0;
+  size_t plan_off = 0;
+  const size_t need = pl.splits > 1 ? partial_bytes(cfg, B, T, pl, &lse_off, &plan_off) : 0;
   if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return MLA_ERR_WORKSPACE;
 
   mla::DecodeParams p{};
@@ -221,6 +243,8 @@ mla_status mla_decode(const mla_config* cfg, const void* q_abs, const void* pool
   p.num_splits = pl.splits;
   p.chunk_rows = pl.chunk;
   p.scale_log2 = softmax_scale(cfg) * 1.4426950408889634f;
+  p.plan = pl.balanced ? reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + plan_off)
+                       : nullptr;
 
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e = use_mfma(cfg, T) ? mla::launch_decode_mfma(p, s)

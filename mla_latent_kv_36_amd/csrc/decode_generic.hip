@@ -152,15 +152,34 @@ __global__ __launch_bounds__(64 * CMB_ROWS) void combine_kernel(const DecodePara
   const int b = (int)(row / TH);
   const int rr = (int)(row - (long long)b * TH);
   const int t = rr / p.H;
-  if (p.num_splits <= 8 && p.d_c == 512) {
+  // this sequence's splits: the first one's partial index, their count and
+  // the cache rows per split (a balanced plan: from the table the decode
+  // kernel wrote; the plain plan: the same for every sequence)
+  int P0, S, chunk;
+  if (p.plan != nullptr) {
+    const int4 e = *reinterpret_cast<const int4*>(p.plan + 4 * (size_t)b);
+    P0 = __builtin_amdgcn_readfirstlane(e.x);
+    S = __builtin_amdgcn_readfirstlane(e.y);
+    chunk = __builtin_amdgcn_readfirstlane(e.z) * 32;
+    if (S == 0) {  // no visible row in the sequence: o = 0, lse = -inf
+      float* out = p.o_lat + (size_t)row * p.d_c;
+      for (int d = lane; d < p.d_c; d += 64) out[d] = 0.0f;
+      if (lane == 0 && p.lse != nullptr) p.lse[row] = -INFINITY;
+      return;
+    }
+  } else {
+    P0 = b * p.num_splits;
+    S = p.num_splits;
+    chunk = p.chunk_rows;
+  }
+  if (S <= 8 && p.d_c == 512) {
     // The common shape in one memory round trip: the sequence length, every
     // split's log-sum-exp (lane s) and every split's partial row (8 columns
     // per lane) are read before any of them is used.  Splits that hold no row
     // of this query were never written; they are left out by selection, not
     // by a zero weight, since their memory may hold anything.
-    const int S = p.num_splits;
-    const float* lse_b = p.part_lse + (size_t)b * S * TH + rr;
-    const float* po_b = p.part_o + ((size_t)b * S * TH + rr) * 512 + 4 * lane;
+    const float* lse_b = p.part_lse + (size_t)P0 * TH + rr;
+    const float* po_b = p.part_o + ((size_t)P0 * TH + rr) * 512 + 4 * lane;
     const size_t sstride = (size_t)TH * 512;
     const int len = p.seq_lens[b];
     const float lse_l = lse_b[(size_t)min(lane, S - 1) * TH];
@@ -178,8 +197,7 @@ __global__ __launch_bounds__(64 * CMB_ROWS) void combine_kernel(const DecodePara
 #pragma unroll
     for (int k = 0; k < 8; ++k) asm volatile("" ::"v"(v0[k]), "v"(v1[k]));
     const int n_valid = visible_rows(len, p.T, t, p.causal, p.cap);
-    const int ns = __builtin_amdgcn_readfirstlane(
-        min(S, (n_valid + p.chunk_rows - 1) / p.chunk_rows));
+    const int ns = __builtin_amdgcn_readfirstlane(min(S, (n_valid + chunk - 1) / chunk));
     // no branches from here on: a branch would let the compiler move the
     // loads above behind it, one dependent round trip at a time
     float M = lane < ns ? lse_l : -INFINITY;
@@ -209,11 +227,10 @@ __global__ __launch_bounds__(64 * CMB_ROWS) void combine_kernel(const DecodePara
   }
   const int n_valid = visible_rows(p.seq_lens[b], p.T, t, p.causal, p.cap);
   // one row per wave: the split count is the same in every lane
-  const int ns = __builtin_amdgcn_readfirstlane(
-      min(p.num_splits, (n_valid + p.chunk_rows - 1) / p.chunk_rows));
+  const int ns = __builtin_amdgcn_readfirstlane(min(S, (n_valid + chunk - 1) / chunk));
   float* out = p.o_lat + (size_t)row * p.d_c;
-  const float* lse_b = p.part_lse + (size_t)b * p.num_splits * TH + rr;
-  const float* po_b = p.part_o + ((size_t)b * p.num_splits * TH + rr) * p.d_c;
+  const float* lse_b = p.part_lse + (size_t)P0 * TH + rr;
+  const float* po_b = p.part_o + ((size_t)P0 * TH + rr) * p.d_c;
   const size_t sstride = (size_t)TH * p.d_c;  // floats between splits of one row
 
   if (ns <= 0) {

@@ -77,6 +77,7 @@ struct __align__(16) Smem {
   float alpha[2][ROWS];        // per-row rescale factor, by unit parity
   float lrow[ROWS];            // 1 / (row sum), after the last unit
   int flag[2][4];              // [unit parity][row group]: some row of its 16 raised its max
+  int item[8];                 // this workgroup's work item under a balanced plan
 };
 
 __device__ __forceinline__ int lat_sw(int t) { return t & 15; }
@@ -213,8 +214,8 @@ __device__ __forceinline__ void softmax_unit(Smem& sm, int u, int valid, int grp
 // normalisation, and the rows' log-sum-exp (natural log) to the output or to
 // the split's partial.
 __device__ __forceinline__ void softmax_finish(Smem& sm, const DecodeParams& p, int grp, int lane,
-                                               float m_run, float l_run, bool direct, int b, int s,
-                                               int TH, int rb) {
+                                               float m_run, float l_run, bool direct, int b,
+                                               int pidx, int TH, int rb) {
   if ((lane >> 4) != 0) return;
   const int srow = 16 * grp + (lane & 15);
   sm.lrow[srow] = 1.0f / l_run;
@@ -222,8 +223,93 @@ __device__ __forceinline__ void softmax_finish(Smem& sm, const DecodeParams& p, 
   if (direct) {
     if (p.lse != nullptr) p.lse[(size_t)b * TH + rb + srow] = lse;
   } else {
-    p.part_lse[((size_t)b * p.num_splits + s) * TH + rb + srow] = lse;
+    p.part_lse[(size_t)pidx * TH + rb + srow] = lse;
   }
+}
+
+// Balanced split plan for a batch of sequences of different lengths, with K
+// work items per 64-row group.  Sequence b has U_b = ceil(n_b / 32) units (n_b
+// = the rows its last new token sees) and gets S_b = ceil(U_b / C) splits of
+// ch_b = ceil(U_b / S_b) units each (the last may be shorter), where C is the
+// smallest count >= kMinUnits for which sum_b S_b <= K; the splits of the
+// sequences are numbered in order, P_b being the first of sequence b.  Work
+// item k is split k - P_b of the sequence with P_b <= k < P_b + S_b, or no
+// work past the last.  Computed by one wave (64 lanes, sequences
+// lane + 64c); with `table`, every sequence's (P_b, S_b, ch_b) is written
+// there for the merge.  Returns {b, s, S_b, ch_b, P_b}, b = -1 for no work.
+constexpr int kMinUnits = 8;
+struct PlanItem {
+  int b, s, S_b, ch_b, P_b;
+};
+__device__ __forceinline__ PlanItem balanced_item(const DecodeParams& p, int k, int lane,
+                                                  int32_t* table) {
+  const int B = p.B;
+  const int K = p.num_splits;
+  auto units = [&](int b) {
+    if (b >= B) return 0;
+    const int n = visible_rows(p.seq_lens[b], p.T, p.T - 1, p.causal, p.cap);
+    return (n + UNIT - 1) / UNIT;
+  };
+  auto wave_sum = [](int x) {
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) x += __shfl_xor(x, off);
+    return x;
+  };
+  auto wave_max = [](int x) {
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) x = max(x, __shfl_xor(x, off));
+    return x;
+  };
+  // the splits sequence b gets for a bound of C units per split
+  auto splits_of = [](int U, int C) { return U == 0 ? 0 : (U + C - 1) / C; };
+  long long total = 0;
+  int umax = 0;
+  for (int c0 = 0; c0 < B; c0 += 64) {
+    const int U = units(c0 + lane);
+    total += wave_sum(U);
+    umax = max(umax, wave_max(U));
+  }
+  // smallest feasible C in [lo, hi]; hi = max units is feasible (one split per
+  // nonempty sequence, and K >= B)
+  int lo = (int)max((long long)kMinUnits, (total + K - 1) / K);
+  int hi = max(lo, umax);
+  while (lo < hi) {
+    const int mid = lo + (hi - lo) / 2;
+    int cnt = 0;
+    for (int c0 = 0; c0 < B; c0 += 64) cnt += wave_sum(splits_of(units(c0 + lane), mid));
+    if (cnt <= K) hi = mid; else lo = mid + 1;
+  }
+  const int C = lo;
+  PlanItem it{-1, 0, 0, 0, 0};
+  int base = 0;  // splits of the sequences before this chunk
+  for (int c0 = 0; c0 < B; c0 += 64) {
+    const int U = units(c0 + lane);
+    const int S_b = splits_of(U, C);
+    const int ch_b = S_b > 0 ? (U + S_b - 1) / S_b : 0;
+    int incl = S_b;  // inclusive prefix sum over the lanes
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int y = __shfl_up(incl, off);
+      if (lane >= off) incl += y;
+    }
+    const int P_b = base + incl - S_b;
+    if (table != nullptr && c0 + lane < B) {
+      table[4 * (c0 + lane) + 0] = P_b;
+      table[4 * (c0 + lane) + 1] = S_b;
+      table[4 * (c0 + lane) + 2] = ch_b;
+    }
+    const unsigned long long hit = __ballot(S_b > 0 && P_b <= k && k < P_b + S_b);
+    if (hit != 0) {
+      const int l = __builtin_ctzll(hit);
+      it.b = c0 + l;
+      it.s = k - __shfl(P_b, l);
+      it.S_b = __shfl(S_b, l);
+      it.ch_b = __shfl(ch_b, l);
+      it.P_b = __shfl(P_b, l);
+    }
+    base += __shfl(incl, 63);
+  }
+  return it;
 }
 
 __global__ __launch_bounds__(NT, 1) void decode_mfma_kernel(const DecodeParams p) {
@@ -257,8 +343,32 @@ __global__ __launch_bounds__(NT, 1) void decode_mfma_kernel(const DecodeParams p
     g = i % G;
     pair = i / G;
   }
-  const int s = pair % S;
-  const int b = pair / S;
+  // (sequence b, split s) of this workgroup, its partial's index and the cache
+  // rows per split: the plain plan cuts every sequence at the same rows; a
+  // balanced plan is computed here, by wave 0, from the sequence lengths
+  int b, s, pidx, chunk_rows;
+  if (p.plan == nullptr) {
+    s = pair % S;
+    b = pair / S;
+    pidx = pair;
+    chunk_rows = p.chunk_rows;
+  } else {
+    if (wave == 0) {
+      const PlanItem it = balanced_item(p, pair, lane, g == 0 && pair == 0 ? p.plan : nullptr);
+      if (lane == 0) {
+        sm.item[0] = it.b;
+        sm.item[1] = it.s;
+        sm.item[2] = it.P_b + it.s;
+        sm.item[3] = it.ch_b * UNIT;
+      }
+    }
+    __syncthreads();
+    b = __builtin_amdgcn_readfirstlane(sm.item[0]);
+    if (b < 0) return;  // no work item: the whole workgroup
+    s = __builtin_amdgcn_readfirstlane(sm.item[1]);
+    pidx = __builtin_amdgcn_readfirstlane(sm.item[2]);
+    chunk_rows = __builtin_amdgcn_readfirstlane(sm.item[3]);
+  }
 
   const int TH = p.T * p.H;
   const int rb = g * ROWS;  // first query row (t*H + h) of the group
@@ -268,9 +378,10 @@ __global__ __launch_bounds__(NT, 1) void decode_mfma_kernel(const DecodeParams p
   const int n_valid =
       __builtin_amdgcn_readfirstlane(visible_rows(p.seq_lens[b], p.T, t, p.causal, p.cap));
   // this range: cache rows tok0 .. tok_end-1 (tok0 is a multiple of UNIT)
-  const int tok0 = s * p.chunk_rows;
-  const int tok_end = min(tok0 + p.chunk_rows, n_valid);
-  const bool direct = (S == 1);
+  const int tok0 = s * chunk_rows;
+  const int tok_end = min(tok0 + chunk_rows, n_valid);
+  // one split and the plain plan: the final output directly
+  const bool direct = S == 1 && p.plan == nullptr;
 
   if (tok0 >= tok_end) {
     if (direct) {  // no visible row: o = 0, lse = -inf
@@ -625,10 +736,10 @@ __global__ __launch_bounds__(NT, 1) void decode_mfma_kernel(const DecodeParams p
       for (int j = -2; j < U; ++j) step(j, std::false_type{});
     }
 
-    softmax_finish(sm, p, v, lane, m_run, l_run, direct, b, s, TH, rb);
+    softmax_finish(sm, p, v, lane, m_run, l_run, direct, b, pidx, TH, rb);
     lds_barrier();                         // F
     float* dst = direct ? p.o_lat + ((size_t)b * TH + rb) * DC
-                        : p.part_o + (((size_t)b * S + s) * TH + rb) * DC;
+                        : p.part_o + ((size_t)pidx * TH + rb) * DC;
     // Streaming (non-temporal) stores: the rows are read by the next kernel,
     // not by this one, and lines left dirty in L2 would all be written back
     // at the end of the launch, which delays the next kernel's start.
@@ -658,7 +769,9 @@ bool decode_mfma_supported(int dtype, int d_c, int d_r, int block_size, int T, i
 
 hipError_t launch_decode_mfma(const DecodeParams& p, hipStream_t stream) {
   const int G = (p.T * p.H) / ROWS;
-  const long long grid = (long long)p.B * p.num_splits * G;
+  // plain plan: one workgroup per (sequence, split, group); balanced: per
+  // (work item, group)
+  const long long grid = (p.plan != nullptr ? 1LL : (long long)p.B) * p.num_splits * G;
   if (grid <= 0) return hipSuccess;
   if (grid > 0x7fffffffLL) return hipErrorInvalidValue;
   hipLaunchKernelGGL(decode_mfma_kernel, dim3((unsigned)grid), dim3(NT), 0, stream, p);

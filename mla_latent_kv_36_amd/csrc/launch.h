@@ -24,6 +24,12 @@ struct DecodeParams {
   int num_splits;             // S
   int chunk_rows;             // cache rows per split (a multiple of the kernel granule)
   float scale_log2;           // softmax scale * log2(e)
+  // Balanced plan (MFMA kernel only): when non-null, num_splits is the number
+  // K of work items per 64-row group, split sizes are chosen per sequence on
+  // the device, and plan[4b .. 4b+2] receives sequence b's first work item,
+  // split count and units per split for the merge.  Partials are then
+  // indexed by work item: part_o [K, T*H, d_c], part_lse [K, T*H].
+  int32_t* plan;
 };
 
 // The MFMA kernel covers bf16, d_c = 512, d_rope = 64, 64-token pages and H

@@ -103,11 +103,24 @@ def test_workspace_and_split_plan(lib):
         r256 = lambda x: -(-x // 256) * 256
         want = r256(rows * 512 * 4) + r256(rows * 4)
         assert mla.mla_decode_workspace_size(cfg, B, T, cap, 0, S) == want
-    # the library's own choice is a valid split count and sized consistently
-    s = mla.mla_decode_num_splits(cfg, 16, 1, 4097, 0)
+    # equal lengths (total = B x longest): the library's choice is a plain
+    # plan, a valid split count, sized like that count given explicitly
+    s = mla.mla_decode_num_splits(cfg, 16, 1, 4097, 16 * 4097)
     assert 1 <= s <= 129
-    assert mla.mla_decode_workspace_size(cfg, 16, 1, 4097, 0, 0) == \
-        mla.mla_decode_workspace_size(cfg, 16, 1, 4097, 0, s)
+    assert mla.mla_decode_workspace_size(cfg, 16, 1, 4097, 16 * 4097, 0) == \
+        mla.mla_decode_workspace_size(cfg, 16, 1, 4097, 16 * 4097, s)
+    # lengths that may differ (total unknown, or below B x longest): a balanced
+    # plan of 256 / G work items per 64-row group (G = T*H/64), partials indexed
+    # by work item, plus a 16-byte table entry per sequence
+    r256 = lambda x: -(-x // 256) * 256
+    for B, T, total in [(16, 1, 0), (64, 1, 64 * 1000), (8, 4, 0)]:
+        K = 256 // (T * 128 // 64)
+        assert mla.mla_decode_num_splits(cfg, B, T, 4097, total) == K
+        rows = K * T * 128
+        want = r256(rows * 512 * 4) + r256(rows * 4) + r256(B * 16)
+        assert mla.mla_decode_workspace_size(cfg, B, T, 4097, total, 0) == want
+    # no more work items than sequences: the plain plan
+    assert mla.mla_decode_num_splits(cfg, 200, 1, 4097, 0) <= 129
     # more splits than 32-row units collapse to one split per unit
     assert mla.mla_decode_workspace_size(cfg, 1, 1, 32, 0, 8) == 0
     with pytest.raises(RuntimeError):
