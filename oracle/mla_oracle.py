@@ -155,6 +155,47 @@ def out_proj_ref(o_lat: np.ndarray, w_uv: np.ndarray, dtype=F64) -> np.ndarray:
 
 
 # --------------------------------------------------------------------------
+# the output side: W^O over the heads, and W^UV folded into it
+# --------------------------------------------------------------------------
+
+def o_proj_ref(attn: np.ndarray, w_o: np.ndarray, dtype=F64) -> np.ndarray:
+    """y[m, :] = W^O x_m, where x_m lists the per-head outputs attn[m, h, :]
+    head after head ("Attention, Part 2: MQA, GQA and MLA", section "The trick
+    that makes it fast": its inference code reshapes the per-head outputs of a
+    token into one vector and applies the output projection W_o).
+    attn [M, H, d_v], w_o [d, H * d_v] (the weight of a linear layer
+    H * d_v -> d) -> y [M, d]."""
+    a = np.asarray(attn, dtype=dtype)
+    return a.reshape(a.shape[0], -1) @ np.asarray(w_o, dtype=dtype).T
+
+
+def fold_uv_o_ref(w_uv: np.ndarray, w_o: np.ndarray, dtype=F64) -> np.ndarray:
+    """The output-side absorption: W^UV and W^O merged into one matrix ("How
+    DeepSeek Rewrote the Transformer", section "Absorbed projections: the
+    mathematician's shortcut", point 2; "Multi-head latent attention (MLA)",
+    section 2: the up-projections fold into the output projection).  The block
+    of head h is W^O's block of head h times W^UV[h]:
+    W_fold[:, h*d_c + c] = sum_v W^O[:, h*d_v + v] W^UV[h, v, c].
+    w_uv [H, d_v, d_c], w_o [d, H * d_v] -> w_fold [d, H * d_c]."""
+    wv = np.asarray(w_uv, dtype=dtype)
+    H, d_v, d_c = wv.shape
+    wo = np.asarray(w_o, dtype=dtype)
+    d = wo.shape[0]
+    out = np.empty((d, H * d_c), dtype=dtype)
+    for h in range(H):
+        out[:, h * d_c:(h + 1) * d_c] = wo[:, h * d_v:(h + 1) * d_v] @ wv[h]
+    return out
+
+
+def o_proj_folded_ref(o_lat: np.ndarray, w_fold: np.ndarray, dtype=F64) -> np.ndarray:
+    """y[m, :] = W_fold z_m, where z_m lists the latent outputs o_lat[m, h, :]
+    head after head: the folded matrix applied straight to the latent-space
+    sums.  o_lat [M, H, d_c], w_fold [d, H * d_c] -> y [M, d]."""
+    z = np.asarray(o_lat, dtype=dtype)
+    return z.reshape(z.shape[0], -1) @ np.asarray(w_fold, dtype=dtype).T
+
+
+# --------------------------------------------------------------------------
 # split-KV: partial attention over a contiguous row range, merged by log-sum-exp
 # --------------------------------------------------------------------------
 

@@ -8,6 +8,8 @@ fix, never against the oracle itself.
 * pure-Python brute force on tiny inputs;
 * closed-form special cases, split and page-permutation invariance;
 * the negative RoPE experiment of page 3;
+* the output side: W^O against torch's linear layer on the concatenated heads,
+  the folded W^UV.W^O against one-hot weights and the full rebuild path;
 * planted mistakes in copies of the oracle are caught by these pins.
 """
 import json
@@ -398,3 +400,97 @@ def test_produced_cache_attends_like_rebuilt_keys():
     got = oracle.out_proj_ref(o_lat, w_uv)
     want = oracle.naive_ref(q_nope, q_rope, w_uk, w_uv, rows, d_c, scale, True)
     assert _close(got, want, 1e-12)
+
+
+# ------------------------------------------------------------------ output side
+# W^O over the heads concatenated head after head, and W^UV folded into W^O.
+# Each check takes the functions under test, so the planted mistakes in
+# test_oracle_mutants.py run through the same pins.
+
+def o_proj_linear_pin(o_proj) -> bool:
+    """The page-3 inference code ends with the output projection applied to the
+    per-head outputs of a token reshaped into one vector ("Attention, Part 2",
+    section "The trick that makes it fast").  The same two library steps in
+    torch (a reshape of [M, H, d_v], then F.linear with the [d, H*d_v]
+    weight), in float64, must give the oracle's result; d != H * d_v so a
+    transposed weight cannot fit."""
+    rng = np.random.default_rng(31)
+    M, H, d_v, d = 3, 5, 4, 7
+    attn, w_o = rng.standard_normal((M, H, d_v)), rng.standard_normal((d, H * d_v))
+    want = torch.nn.functional.linear(torch.from_numpy(attn).reshape(M, -1),
+                                      torch.from_numpy(w_o)).numpy()
+    try:
+        got = o_proj(attn, w_o)
+    except ValueError:
+        return False
+    return got.shape == want.shape and _close(got, want, 1e-13)
+
+
+def fold_one_hot_pin(fold) -> bool:
+    """W^O with a single 1 at (i, h*d_v + v) picks value row v of head h: the
+    folded block of head h in row i is W^UV[h, v, :] and every other entry is
+    0 (the merged matrix of "How DeepSeek Rewrote the Transformer", section
+    "Absorbed projections", point 2, by its definition)."""
+    rng = np.random.default_rng(32)
+    H, d_v, d_c, d = 3, 2, 5, 4
+    w_uv = rng.standard_normal((H, d_v, d_c))
+    for (i, h, v) in ((0, 0, 0), (3, 2, 1), (1, 1, 0)):
+        w_o = np.zeros((d, H * d_v))
+        w_o[i, h * d_v + v] = 1.0
+        want = np.zeros((d, H * d_c))
+        want[i, h * d_c:(h + 1) * d_c] = w_uv[h, v]
+        got = fold(w_uv, w_o)
+        if got.shape != want.shape or not np.array_equal(got, want):
+            return False
+    return True
+
+
+def fold_equals_full_path_pin(fold, o_proj_folded) -> bool:
+    """The output-side absorption changes no result: the full path (rebuild
+    every head's keys and values, attend, up-project per head, apply W^O)
+    equals attention in latent space followed by the folded matrix, to
+    rounding (same section, point 2; "Attention, Part 2", the proof that the
+    two paths agree).  The full path here is the naive path plus torch's
+    F.linear on the concatenated heads, so it shares nothing with the fold."""
+    rng = np.random.default_rng(33)
+    T, H, d, d_n, d_v, d_c, d_r, N = 3, 4, 9, 6, 5, 12, 4, 11
+    rows = rng.standard_normal((N, d_c + d_r))
+    q_nope, q_rope = rng.standard_normal((T, H, d_n)), rng.standard_normal((T, H, d_r))
+    w_uk = rng.standard_normal((H, d_n, d_c)) / math.sqrt(d_c)
+    w_uv = rng.standard_normal((H, d_v, d_c)) / math.sqrt(d_c)
+    w_o = rng.standard_normal((d, H * d_v)) / math.sqrt(H * d_v)
+    scale = 1 / math.sqrt(d_n + d_r)
+    o = oracle.naive_ref(q_nope, q_rope, w_uk, w_uv, rows, d_c, scale, True)
+    want = torch.nn.functional.linear(torch.from_numpy(o).reshape(T, -1),
+                                      torch.from_numpy(w_o)).numpy()
+    o_lat, _ = oracle.attend_ref(oracle.absorb_q_ref(q_nope, q_rope, w_uk), rows, d_c, scale, True)
+    try:
+        got = o_proj_folded(o_lat, fold(w_uv, w_o))
+    except ValueError:
+        return False
+    return got.shape == want.shape and _close(got, want, 1e-12)
+
+
+def test_o_proj_matches_the_pages_linear_layer():
+    assert o_proj_linear_pin(oracle.o_proj_ref)
+
+
+def test_fold_one_hot_picks_value_rows():
+    assert fold_one_hot_pin(oracle.fold_uv_o_ref)
+
+
+def test_folded_output_equals_full_path():
+    assert fold_equals_full_path_pin(oracle.fold_uv_o_ref, oracle.o_proj_folded_ref)
+
+
+def test_folded_and_unfolded_output_sides_agree_at_v2_width():
+    """At the V2-scale widths (H = 128, d_v = 40, d = 5120, with fewer rows of
+    W^O so that it stays quick) the two orders of the same products agree."""
+    rng = np.random.default_rng(34)
+    M, H, d_v, d_c, d = 2, 128, 40, 512, 48
+    o_lat = rng.standard_normal((M, H, d_c))
+    w_uv = rng.standard_normal((H, d_v, d_c)) / math.sqrt(d_c)
+    w_o = rng.standard_normal((d, H * d_v)) / math.sqrt(H * d_v)
+    y1 = oracle.o_proj_ref(oracle.out_proj_ref(o_lat, w_uv), w_o)
+    y2 = oracle.o_proj_folded_ref(o_lat, oracle.fold_uv_o_ref(w_uv, w_o))
+    assert _close(y1, y2, 1e-12)

@@ -158,3 +158,69 @@ def test_producer_pins_accept_the_unmutated_variant():
     produce = _produce_variant("none")
     rope = lambda x, pos: _rope_variant(x, pos, "none")
     assert producer_one_hot_pin(produce) and producer_position_pin(produce) and rope_angle_pin(rope)
+
+
+# ------------------------------------------------------------------ output side
+
+def _o_proj_variant(bug):
+    def o_proj(attn, w_o):
+        a = np.asarray(attn, np.float64)
+        M, H, d_v = a.shape
+        if bug == "value_major_concat":   # heads interleaved: x[v*H + h]
+            x = a.transpose(0, 2, 1).reshape(M, -1)
+        else:
+            x = a.reshape(M, -1)
+        w = np.asarray(w_o, np.float64)
+        if bug == "transposed_weight":    # W^O read as stored [H*d_v, d]
+            return x @ w.reshape(w.shape[1], w.shape[0])
+        return x @ w.T
+    return o_proj
+
+
+def _fold_variant(bug):
+    def fold(w_uv, w_o):
+        wv = np.asarray(w_uv, np.float64)
+        H, d_v, d_c = wv.shape
+        wo = np.asarray(w_o, np.float64)
+        d = wo.shape[0]
+        if bug == "heads_reversed":
+            wv = wv[::-1]
+        if bug == "value_major_blocks":   # W^O's columns read as v*H + h
+            wo = wo.reshape(d, d_v, H).transpose(0, 2, 1).reshape(d, H * d_v)
+        if bug == "uv_block_transposed":  # W^UV[h] read as if stored [d_c, d_v]
+            wv = wv.reshape(H, d_c, d_v).transpose(0, 2, 1)
+        out = np.empty((d, H * d_c))
+        for h in range(H):
+            out[:, h * d_c:(h + 1) * d_c] = wo[:, h * d_v:(h + 1) * d_v] @ wv[h]
+        return out
+    return fold
+
+
+def _o_proj_folded_variant(bug):
+    def folded(o_lat, w_fold):
+        z = np.asarray(o_lat, np.float64)
+        M, H, d_c = z.shape
+        x = z.transpose(0, 2, 1).reshape(M, -1) if bug == "latent_value_major" else z.reshape(M, -1)
+        return x @ np.asarray(w_fold, np.float64).T
+    return folded
+
+
+@pytest.mark.parametrize("bug", ["value_major_concat", "transposed_weight"])
+def test_o_proj_pin_rejects_planted_bug(bug):
+    from test_oracle import o_proj_linear_pin
+    assert not o_proj_linear_pin(_o_proj_variant(bug))
+
+
+@pytest.mark.parametrize("bug", ["heads_reversed", "value_major_blocks", "uv_block_transposed",
+                                 "latent_value_major"])
+def test_fold_pins_reject_planted_bug(bug):
+    from test_oracle import fold_equals_full_path_pin, fold_one_hot_pin
+    fold, folded = _fold_variant(bug), _o_proj_folded_variant(bug)
+    assert not (fold_one_hot_pin(fold) and fold_equals_full_path_pin(fold, folded))
+
+
+def test_output_side_pins_accept_the_unmutated_variants():
+    from test_oracle import fold_equals_full_path_pin, fold_one_hot_pin, o_proj_linear_pin
+    assert o_proj_linear_pin(_o_proj_variant("none"))
+    fold, folded = _fold_variant("none"), _o_proj_folded_variant("none")
+    assert fold_one_hot_pin(fold) and fold_equals_full_path_pin(fold, folded)
