@@ -161,6 +161,84 @@ def producer_phase(w, bt, steps, torch, mla) -> dict:
             "k_split_workspace_bytes": nbytes, "rotated_copies": copies}
 
 
+def output_side_phase(w, torch, mla) -> dict:
+    """The output side after the step's W^UV up-projection: mla_o_proj (W^O over
+    the concatenated heads) replayed over enough copies of W^O and the per-head
+    outputs (>= 512 MiB in all) that the 256 MB MALL cannot serve them; the
+    one-time fold of W^UV into W^O; and mla_o_proj_folded, the folded matrix
+    (671 MB at the V2-scale widths, larger than the MALL) on the fp32 latent
+    outputs."""
+    from workloads import make_output_inputs
+    from workloads.device import to_dev
+    oi = make_output_inputs(w)
+    cfg = mla.make_config(w.H, w.d_c, w.d_r, w.d_n, w.d_v, w.block_size, 0.0, w.dtype)
+    dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    elem = 2 if w.dtype == "bf16" else 4
+    M, d = w.B * w.T, w.d_model
+    K, Kf = w.H * w.d_v, w.H * w.d_c
+    stream = torch.cuda.current_stream()
+
+    def timed(fn, reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / reps
+
+    def graph_of(calls):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for c in calls:
+                c()
+        for _ in range(2):
+            g.replay()
+        torch.cuda.synchronize()
+        return g
+
+    # W^O, rotated over copies
+    wo_bytes = d * K * elem
+    copies = max(8, -(-(512 << 20) // wo_bytes))
+    base = [to_dev(oi.attn, dt, "cuda"), to_dev(oi.w_o, dt, "cuda")]
+    sets = [base] + [[t.clone() for t in base] for _ in range(copies - 1)]
+    y = torch.empty((M, d), dtype=dt, device="cuda")
+    n_ws = mla.mla_o_proj_workspace_size(cfg, M, d, False)
+    ws = torch.empty(max(n_ws, 256), dtype=torch.uint8, device="cuda")
+    g = graph_of([lambda a=a, wo=wo: mla.mla_o_proj(cfg, a, wo, y, ws) for a, wo in sets])
+    us = timed(g.replay, 5) / copies
+    algo = wo_bytes + M * K * elem + M * d * elem
+    out = {"o_proj": {"call": "mla_o_proj", "kernels": "wo_gemm_mfma_kernel + wo_finish_kernel",
+                      "tokens": M, "k": K, "d_model": d, "us": us, "bound": "hbm",
+                      "algorithmic_bytes": algo, "GBps": algo / (us * 1e-6) / 1e9,
+                      "frac": algo / (us * 1e-6) / 1e9 / HBM_PEAK_GBPS,
+                      "k_split_workspace_bytes": n_ws, "rotated_copies": copies}}
+    del sets, base
+    # the fold (once per model), then the folded product
+    w_uv = to_dev(oi.w_uv, dt, "cuda")
+    w_o = to_dev(oi.w_o, dt, "cuda")
+    wf = torch.empty((d, Kf), dtype=dt, device="cuda")
+    us_fold = timed(lambda: mla.mla_fold_uv_o(cfg, w_uv, w_o, wf), 3)
+    fold_bytes = (d * Kf + d * K + w.H * w.d_v * w.d_c) * elem
+    out["fold"] = {"call": "mla_fold_uv_o", "kernels": "fold_uv_o_kernel", "us": us_fold,
+                   "algorithmic_bytes": fold_bytes, "GBps": fold_bytes / (us_fold * 1e-6) / 1e9}
+    o_lat = torch.from_numpy(oi.o_lat).cuda()
+    n_wsf = mla.mla_o_proj_workspace_size(cfg, M, d, True)
+    wsf = torch.empty(max(n_wsf, 256), dtype=torch.uint8, device="cuda")
+    g2 = graph_of([lambda: mla.mla_o_proj_folded(cfg, o_lat, wf, y, wsf)])
+    us_f = timed(g2.replay, 5)
+    algo_f = d * Kf * elem + M * Kf * 4 + M * d * elem
+    out["o_proj_folded"] = {"call": "mla_o_proj_folded",
+                            "kernels": "wo_gemm_mfma_kernel + wo_finish_kernel",
+                            "us": us_f, "bound": "hbm", "algorithmic_bytes": algo_f,
+                            "GBps": algo_f / (us_f * 1e-6) / 1e9,
+                            "frac": algo_f / (us_f * 1e-6) / 1e9 / HBM_PEAK_GBPS,
+                            "k_split_workspace_bytes": n_wsf,
+                            "weight_bytes_vs_w_o": d * Kf / (d * K)}
+    del wf, g2
+    return out
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -325,6 +403,7 @@ def main() -> int:
     }
     if w.d_model > 0:
         line["producer"] = producer_phase(w, bt, steps, torch, mla)
+        line["output_side"] = output_side_phase(w, torch, mla)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
     else:

@@ -10,7 +10,9 @@
  *
  * and, on the input side, mla_kv_produce (the cached row made from the token's
  * hidden vector, with RoPE on k^R, written into the cache in place of
- * mla_cache_append) and mla_rope (the same rotation for the query's rotary part).
+ * mla_cache_append) and mla_rope (the same rotation for the query's rotary part);
+ * on the output side, mla_o_proj (the output projection W^O over the heads) and
+ * mla_fold_uv_o / mla_o_proj_folded (W^UV merged into W^O).
  *
  * The method is the inference path of "Attention, Part 2: MQA, GQA and MLA",
  * section "The trick that makes it fast: never rebuild at all": only the latent c
@@ -239,6 +241,53 @@ mla_status mla_kv_produce(const mla_config* cfg, const void* hidden, int32_t d_m
  */
 mla_status mla_rope(const mla_config* cfg, void* x, int32_t heads, const int32_t* positions,
                     int32_t M, float rope_base, void* stream);
+
+/*
+ * The output side, after mla_out_proj: the model's output projection W^O, and
+ * W^UV folded into it.
+ *
+ * mla_o_proj -- y[m, :] = W^O x_m, where x_m lists the per-head outputs
+ * attn[m, h, :] head after head ("Attention, Part 2", section "The trick that
+ * makes it fast": its inference code reshapes a token's heads into one vector
+ * and applies W_o).
+ *   attn [M, H, d_v] (cfg->dtype: mla_out_proj's output), w_o [d_model, H * d_v]
+ *   (cfg->dtype; the weight of a linear layer H * d_v -> d_model), y [M, d_model]
+ *   (cfg->dtype).
+ *
+ * mla_fold_uv_o -- the output-side absorption ("How DeepSeek Rewrote the
+ * Transformer", section "Absorbed projections: the mathematician's shortcut",
+ * point 2: W^UV and W^O merge into one matrix), a one-time weight preparation:
+ *   w_fold[i, h * d_c + c] = sum_v w_o[i, h * d_v + v] * w_uv[h, v, c]
+ *   w_uv [H, d_v, d_c], w_o [d_model, H * d_v], w_fold [d_model, H * d_c], all
+ *   cfg->dtype; fp32 accumulation, rounded once.  d_v must be <= 256.
+ *
+ * mla_o_proj_folded -- y[m, :] = w_fold z_m, where z_m lists the latent outputs
+ * o_lat[m, h, :] head after head: the same y as mla_out_proj followed by
+ * mla_o_proj, in one product.
+ *   o_lat [M, H, d_c] fp32 (mla_decode's output), w_fold as above, y [M, d_model]
+ *   (cfg->dtype).  The bf16 kernel rounds o_lat to bf16 as it reads it.  The
+ *   folded matrix holds d_c / d_v times the bytes of W^O (12.8x at the V2-scale
+ *   widths), and a decode step streams its weights, so the unfolded pair is
+ *   the faster route there; the folded one gives the same y.
+ *
+ * Both products accumulate in fp32 and round once.  When the k dimension is
+ * split over workgroups, the partial sums go to `workspace` (device) and are
+ * added in a fixed order (reruns are bit-exact): it must hold
+ * mla_o_proj_workspace_size(cfg, M, d_model, folded) bytes (0: none needed, NULL
+ * allowed), else MLA_ERR_WORKSPACE; its contents on entry do not matter.
+ * mla_o_proj_workspace_size returns (size_t)-1 for invalid arguments.  M == 0
+ * launches nothing.
+ */
+size_t mla_o_proj_workspace_size(const mla_config* cfg, int32_t M, int32_t d_model,
+                                 int32_t folded);
+mla_status mla_o_proj(const mla_config* cfg, const void* attn, const void* w_o, void* y,
+                      int32_t M, int32_t d_model, void* workspace, size_t workspace_bytes,
+                      void* stream);
+mla_status mla_fold_uv_o(const mla_config* cfg, const void* w_uv, const void* w_o,
+                         void* w_fold, int32_t d_model, void* stream);
+mla_status mla_o_proj_folded(const mla_config* cfg, const float* o_lat, const void* w_fold,
+                             void* y, int32_t M, int32_t d_model, void* workspace,
+                             size_t workspace_bytes, void* stream);
 
 /*
  * Debug and test helpers.

@@ -60,6 +60,10 @@ _SIGNATURES = {
     "mla_kv_produce": (_I, [_CFG, _P, _I, _P, _P, ctypes.c_float, _P, _I, _P, _I, _P, _I, _I,
                             _I, _P, ctypes.c_size_t, _P]),
     "mla_rope": (_I, [_CFG, _P, _I, _P, _I, ctypes.c_float, _P]),
+    "mla_o_proj_workspace_size": (ctypes.c_size_t, [_CFG, _I, _I, _I]),
+    "mla_o_proj": (_I, [_CFG, _P, _P, _P, _I, _I, _P, ctypes.c_size_t, _P]),
+    "mla_fold_uv_o": (_I, [_CFG, _P, _P, _P, _I, _P]),
+    "mla_o_proj_folded": (_I, [_CFG, _P, _P, _P, _I, _I, _P, ctypes.c_size_t, _P]),
 }
 
 
@@ -241,3 +245,63 @@ def mla_rope(cfg: MlaConfig, x: torch.Tensor, positions: torch.Tensor, rope_base
     _check(load().mla_rope(ctypes.byref(cfg), _ptr(x), heads, _ptr(positions), M,
                            float(rope_base), _stream(stream)))
 
+
+def mla_o_proj_workspace_size(cfg: MlaConfig, M: int, d_model: int, folded: bool = False) -> int:
+    n = int(load().mla_o_proj_workspace_size(ctypes.byref(cfg), M, d_model, 1 if folded else 0))
+    if n == ctypes.c_size_t(-1).value:
+        raise RuntimeError("mla_o_proj_workspace_size: invalid arguments")
+    return n
+
+
+def _sizes(**named) -> None:
+    for name, (t, n) in named.items():
+        if t.numel() != n:
+            raise ValueError(f"{name}: expected {n} elements, got {t.numel()}")
+
+
+def _ws(workspace: Optional[torch.Tensor]):
+    if workspace is None:
+        return None, 0
+    return workspace.data_ptr(), workspace.numel() * workspace.element_size()
+
+
+def mla_o_proj(cfg: MlaConfig, attn: torch.Tensor, w_o: torch.Tensor, y: torch.Tensor,
+               workspace: Optional[torch.Tensor] = None, stream=None) -> None:
+    """y[m] = W^O . attn[m] with the heads of attn [M, H, d_v] concatenated in
+    order; w_o [d_model, H * d_v], y [M, d_model]."""
+    dt = _TORCH_DTYPE[cfg.dtype]
+    _dev(attn, dt, "attn"), _dev(w_o, dt, "w_o"), _dev(y, dt, "y")
+    M, d = attn.shape[0], w_o.shape[0]
+    _sizes(attn=(attn, M * cfg.n_heads * cfg.d_v), w_o=(w_o, d * cfg.n_heads * cfg.d_v),
+           y=(y, M * d))
+    ws, nbytes = _ws(workspace)
+    _check(load().mla_o_proj(ctypes.byref(cfg), _ptr(attn), _ptr(w_o), _ptr(y), attn.shape[0],
+                             w_o.shape[0], ws, nbytes, _stream(stream)))
+
+
+def mla_fold_uv_o(cfg: MlaConfig, w_uv: torch.Tensor, w_o: torch.Tensor, w_fold: torch.Tensor,
+                  stream=None) -> None:
+    """w_fold[:, h*d_c:(h+1)*d_c] = W^O[:, h*d_v:(h+1)*d_v] . W^UV[h]."""
+    dt = _TORCH_DTYPE[cfg.dtype]
+    _dev(w_uv, dt, "w_uv"), _dev(w_o, dt, "w_o"), _dev(w_fold, dt, "w_fold")
+    H, d = cfg.n_heads, w_o.shape[0]
+    _sizes(w_uv=(w_uv, H * cfg.d_v * cfg.d_c), w_o=(w_o, d * H * cfg.d_v),
+           w_fold=(w_fold, d * H * cfg.d_c))
+    _check(load().mla_fold_uv_o(ctypes.byref(cfg), _ptr(w_uv), _ptr(w_o), _ptr(w_fold),
+                                w_o.shape[0], _stream(stream)))
+
+
+def mla_o_proj_folded(cfg: MlaConfig, o_lat: torch.Tensor, w_fold: torch.Tensor,
+                      y: torch.Tensor, workspace: Optional[torch.Tensor] = None,
+                      stream=None) -> None:
+    """y[m] = w_fold . o_lat[m] with the heads of o_lat [M, H, d_c] (f32)
+    concatenated in order; w_fold [d_model, H * d_c], y [M, d_model]."""
+    dt = _TORCH_DTYPE[cfg.dtype]
+    _dev(o_lat, torch.float32, "o_lat"), _dev(w_fold, dt, "w_fold"), _dev(y, dt, "y")
+    M, d = o_lat.shape[0], w_fold.shape[0]
+    _sizes(o_lat=(o_lat, M * cfg.n_heads * cfg.d_c), w_fold=(w_fold, d * cfg.n_heads * cfg.d_c),
+           y=(y, M * d))
+    ws, nbytes = _ws(workspace)
+    _check(load().mla_o_proj_folded(ctypes.byref(cfg), _ptr(o_lat), _ptr(w_fold), _ptr(y),
+                                    o_lat.shape[0], w_fold.shape[0], ws, nbytes,
+                                    _stream(stream)))

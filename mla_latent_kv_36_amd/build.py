@@ -18,7 +18,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libmla.so")
 SOURCES = ["abi.hip", "decode_mfma.hip", "decode_generic.hip", "projections.hip",
-           "cache_ops.hip", "producer.hip"]
+           "cache_ops.hip", "producer.hip", "output_side.hip"]
 ARCH = "gfx950"
 
 

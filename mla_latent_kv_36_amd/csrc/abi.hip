@@ -377,3 +377,81 @@ extern "C" mla_status mla_rope(const mla_config* cfg, void* x, int32_t heads,
   return hip_status(mla::launch_rope(cfg->dtype, x, positions, M, heads, cfg->d_rope, base,
                                      static_cast<hipStream_t>(stream)));
 }
+
+namespace {
+// The output-side product aims at two workgroups per compute unit (its
+// launch bounds allow two resident), splitting k when the tiles are fewer.
+constexpr int kOutputWorkgroups = 2 * kCUs;
+
+// k of the output-side product: H * d_v for W^O, H * d_c for the folded
+// matrix; 0 when it does not fit an int32.
+int64_t output_k(const mla_config* c, bool folded) {
+  const int64_t k = (int64_t)c->n_heads * (folded ? c->d_c : c->d_v);
+  return k > 0x7fffffffLL ? 0 : k;
+}
+
+size_t output_workspace(const mla_config* c, int M, int d_model, bool folded) {
+  const int64_t K = output_k(c, folded);
+  const int ks = mla::wo_gemm_ksplit(c->dtype, M, d_model, (int)K, kOutputWorkgroups);
+  return ks > 1 ? round256((size_t)ks * M * d_model * sizeof(float)) : 0;
+}
+
+mla_status output_args(const mla_config* cfg, int32_t M, int32_t d_model, bool folded) {
+  mla_status st = check_cfg(cfg);
+  if (st != MLA_OK) return st;
+  if (M < 0 || d_model <= 0 || (!folded && cfg->d_v <= 0) || output_k(cfg, folded) == 0)
+    return MLA_ERR_DIM;
+  return MLA_OK;
+}
+
+mla_status output_call(const mla_config* cfg, bool folded, const void* x, const void* w, void* y,
+                       int32_t M, int32_t d_model, void* workspace, size_t workspace_bytes,
+                       void* stream) {
+  mla_status st = output_args(cfg, M, d_model, folded);
+  if (st != MLA_OK) return st;
+  if (M == 0) return MLA_OK;
+  if (x == nullptr || w == nullptr || y == nullptr) return MLA_ERR_NULL;
+  if (!aligned16(x) || !aligned16(w) || !aligned16(y) ||
+      (workspace != nullptr && !aligned16(workspace)))
+    return MLA_ERR_ALIGN;
+  const int K = (int)output_k(cfg, folded);
+  const int ks = mla::wo_gemm_ksplit(cfg->dtype, M, d_model, K, kOutputWorkgroups);
+  if (ks > 1 && (workspace == nullptr || workspace_bytes < output_workspace(cfg, M, d_model, folded)))
+    return MLA_ERR_WORKSPACE;
+  // the latent outputs are fp32; so are the per-head outputs of an fp32 configuration
+  const bool x_f32 = folded || cfg->dtype == MLA_F32;
+  return hip_status(mla::launch_wo_gemm(cfg->dtype, x_f32, x, w, y, static_cast<float*>(workspace),
+                                        ks, M, d_model, K, static_cast<hipStream_t>(stream)));
+}
+}  // namespace
+
+extern "C" size_t mla_o_proj_workspace_size(const mla_config* cfg, int32_t M, int32_t d_model,
+                                            int32_t folded) {
+  if (output_args(cfg, M, d_model, folded != 0) != MLA_OK) return (size_t)-1;
+  return M == 0 ? 0 : output_workspace(cfg, M, d_model, folded != 0);
+}
+
+extern "C" mla_status mla_o_proj(const mla_config* cfg, const void* attn, const void* w_o,
+                                 void* y, int32_t M, int32_t d_model, void* workspace,
+                                 size_t workspace_bytes, void* stream) {
+  return output_call(cfg, false, attn, w_o, y, M, d_model, workspace, workspace_bytes, stream);
+}
+
+extern "C" mla_status mla_o_proj_folded(const mla_config* cfg, const float* o_lat,
+                                        const void* w_fold, void* y, int32_t M, int32_t d_model,
+                                        void* workspace, size_t workspace_bytes, void* stream) {
+  return output_call(cfg, true, o_lat, w_fold, y, M, d_model, workspace, workspace_bytes, stream);
+}
+
+extern "C" mla_status mla_fold_uv_o(const mla_config* cfg, const void* w_uv, const void* w_o,
+                                    void* w_fold, int32_t d_model, void* stream) {
+  mla_status st = output_args(cfg, 0, d_model, false);
+  if (st != MLA_OK) return st;
+  if (!mla::fold_uv_o_supported(cfg->d_v) || output_k(cfg, true) == 0 ||
+      (int64_t)(d_model + 15) / 16 > 65535)
+    return MLA_ERR_DIM;
+  if (w_uv == nullptr || w_o == nullptr || w_fold == nullptr) return MLA_ERR_NULL;
+  if (!aligned16(w_uv) || !aligned16(w_o) || !aligned16(w_fold)) return MLA_ERR_ALIGN;
+  return hip_status(mla::launch_fold_uv_o(cfg->dtype, w_uv, w_o, w_fold, cfg->n_heads, cfg->d_v,
+                                          cfg->d_c, d_model, static_cast<hipStream_t>(stream)));
+}

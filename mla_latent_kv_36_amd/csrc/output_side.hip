@@ -1,0 +1,325 @@
+// The output side of latent attention on CDNA4 (gfx950).
+//
+//   y = W^O x,  x = the per-head outputs of a token, head after head
+//       ("Attention, Part 2: MQA, GQA and MLA", section "The trick that makes
+//       it fast": the inference code reshapes the heads of a token into one
+//       vector and applies W_o);
+//   W_fold[:, h*d_c + c] = sum_v W^O[:, h*d_v + v] W^UV[h, v, c]
+//       (the output-side absorption: "How DeepSeek Rewrote the Transformer",
+//       section "Absorbed projections: the mathematician's shortcut", point
+//       2), and y = W_fold z with z the latent outputs of a token, head after
+//       head.
+//
+// Both projections are one product y[M, N] = X[M, K] . W[N, K]^T with both
+// operands contiguous along k: X the token rows (bf16 per-head outputs, or the
+// fp32 latent outputs for the folded matrix), W the weight (bf16).  At decode
+// batch sizes M is small and W is the bytes that bound the call (W^O is 52 MB
+// at the V2-scale width, the folded matrix 671 MB), so the kernel is a weight
+// stream on v_mfma_f32_16x16x32_bf16:
+//   * a workgroup owns 64 weight rows x 64 tokens over one k range, stages
+//     64 x 256 chunks of both operands in LDS, and issues the next chunk's
+//     loads before the current chunk's MFMAs;
+//   * the weight is the A operand and the tokens the B operand, so that a
+//     lane ends up with 4 consecutive outputs of one token (one 8-byte bf16
+//     store, or one 16-byte partial store);
+//   * tiles are numbered token tile fastest and placed XCD by XCD, so that
+//     the token tiles that read one weight slice run side by side on one XCD
+//     and share its L2;
+//   * the k dimension is split over workgroups when the tiles alone would
+//     leave compute units idle; the splits' fp32 partial sums are then added
+//     in split order by a second kernel (deterministic).
+// fp32 token rows are rounded to bf16 when staged (the product is bf16 x bf16
+// with fp32 accumulation either way).  fp32 weights and other shapes take a
+// one-thread-per-output kernel.  The fold is a one-time weight preparation and
+// runs on the VALU in fp32.
+#include "common.h"
+#include "launch.h"
+
+namespace mla {
+namespace {
+
+constexpr int WO_TM = 64;          // tokens per workgroup tile
+constexpr int WO_TN = 64;          // weight rows (outputs) per workgroup tile
+constexpr int WO_KC = 256;         // k per LDS chunk (8 MFMA k-steps)
+constexpr int WO_LD = WO_KC + 8;   // bf16 per LDS row: 528 B
+constexpr int WO_PIECES = WO_KC / 8;               // 16-byte bf16 pieces per row
+constexpr int WO_PER = WO_TM * WO_PIECES / 256;    // pieces per thread and operand
+
+typedef __attribute__((__vector_size__(4 * sizeof(uint16_t)))) uint16_t u16x4;
+
+__device__ __forceinline__ f32x4 mfma16(const bf16x8& a, const bf16x8& b, const f32x4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// 8 consecutive token-row elements as 8 bf16 (fp32 rows are rounded here)
+__device__ __forceinline__ uint4 load_piece(const uint16_t* p) {
+  return *reinterpret_cast<const uint4*>(p);
+}
+__device__ __forceinline__ uint4 load_piece(const float* p) {
+  const f32x4 a = *reinterpret_cast<const f32x4*>(p);
+  const f32x4 b = *reinterpret_cast<const f32x4*>(p + 4);
+  uint4 r;
+  r.x = (uint32_t)f32_to_bf16(a[0]) | ((uint32_t)f32_to_bf16(a[1]) << 16);
+  r.y = (uint32_t)f32_to_bf16(a[2]) | ((uint32_t)f32_to_bf16(a[3]) << 16);
+  r.z = (uint32_t)f32_to_bf16(b[0]) | ((uint32_t)f32_to_bf16(b[1]) << 16);
+  r.w = (uint32_t)f32_to_bf16(b[2]) | ((uint32_t)f32_to_bf16(b[3]) << 16);
+  return r;
+}
+
+// With y != nullptr (one k split): y[m, n] = sum_k x[m, k] w[n, k], rounded to
+// bf16.  Otherwise part[z, m, n] = the same sum over split z's k range.
+// Requires K % 32 == 0 and N % 4 == 0.
+template <typename XE>
+__global__ __launch_bounds__(256, 2) void wo_gemm_mfma_kernel(
+    const XE* __restrict__ x, const uint16_t* __restrict__ w, uint16_t* __restrict__ y,
+    float* __restrict__ part, int M, int N, int K, int steps_per_split) {
+  __shared__ __align__(16) uint16_t sx[WO_TM * WO_LD];
+  __shared__ __align__(16) uint16_t sw[WO_TN * WO_LD];
+  // Workgroup i runs on XCD i % 8.  XCD x takes a contiguous block of the
+  // tile numbers (ids past the last full set of 8 keep the plain order).
+  const int ntm = (M + WO_TM - 1) / WO_TM;
+  const int ntn = (N + WO_TN - 1) / WO_TN;
+  const int total = (int)gridDim.x;
+  const int full = total - total % 8;
+  const int i = blockIdx.x;
+  const int t = i < full ? (i % 8) * (full / 8) + i / 8 : i;
+  const int m0 = (t % ntm) * WO_TM;
+  const int n0 = ((t / ntm) % ntn) * WO_TN;
+  const int z = t / (ntm * ntn);
+  const int nk = K / 32;
+  const int s_begin = z * steps_per_split;
+  const int s_end = min(s_begin + steps_per_split, nk);
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+
+  f32x4 acc[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // A chunk: 64 rows x up to 256 k of both operands in 16-byte pieces, 32 per
+  // row (a wave covers two rows, 1 KB contiguous per operand).  Rows past M
+  // or N and k past the split are zero.
+  uint4 vx[WO_PER], vw[WO_PER];
+  auto load_chunk = [&](int sc) {
+    const int steps = min(WO_KC / 32, s_end - sc);
+    const int k0 = sc * 32;
+#pragma unroll
+    for (int u = 0; u < WO_PER; ++u) {
+      const int q = tid + 256 * u;
+      const int r = q / WO_PIECES, c = q % WO_PIECES;
+      const bool kin = c < steps * 4;
+      const int m = m0 + r, n = n0 + r;
+      vx[u] = uint4{0u, 0u, 0u, 0u};
+      vw[u] = uint4{0u, 0u, 0u, 0u};
+      if (kin && m < M) vx[u] = load_piece(x + (size_t)m * K + k0 + 8 * c);
+      if (kin && n < N) vw[u] = load_piece(w + (size_t)n * K + k0 + 8 * c);
+    }
+  };
+  if (s_begin < s_end) load_chunk(s_begin);
+  const int l16 = lane & 15;
+  const int kq = 8 * (lane >> 4);
+  for (int sc = s_begin; sc < s_end; sc += WO_KC / 32) {
+    const int steps = min(WO_KC / 32, s_end - sc);
+#pragma unroll
+    for (int u = 0; u < WO_PER; ++u) {
+      const int q = tid + 256 * u;
+      const int r = q / WO_PIECES, c = q % WO_PIECES;
+      *reinterpret_cast<uint4*>(&sx[r * WO_LD + 8 * c]) = vx[u];
+      *reinterpret_cast<uint4*>(&sw[r * WO_LD + 8 * c]) = vw[u];
+    }
+    __syncthreads();
+    if (sc + WO_KC / 32 < s_end) load_chunk(sc + WO_KC / 32);
+    // wave w: weight rows 16w + (l & 15) (A), tokens 16j + (l & 15) (B), k
+    // 32s + 8(l >> 4) .. +7
+    for (int s = 0; s < steps; ++s) {
+      const bf16x8 a =
+          *reinterpret_cast<const bf16x8*>(&sw[(16 * wave + l16) * WO_LD + 32 * s + kq]);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const bf16x8 b = *reinterpret_cast<const bf16x8*>(&sx[(16 * j + l16) * WO_LD + 32 * s + kq]);
+        acc[j] = mfma16(a, b, acc[j]);
+      }
+    }
+    __syncthreads();
+  }
+  // D: lane l holds token 16j + (l & 15), outputs 16w + 4(l >> 4) .. +3
+  const int n = n0 + 16 * wave + 4 * (lane >> 4);
+  if (n >= N) return;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int m = m0 + 16 * j + l16;
+    if (m >= M) continue;
+    if (y != nullptr) {
+      u16x4 h;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) h[e] = f32_to_bf16(acc[j][e]);
+      *reinterpret_cast<u16x4*>(y + (size_t)m * N + n) = h;
+    } else {
+      *reinterpret_cast<f32x4*>(part + ((size_t)z * M + m) * N + n) = acc[j];
+    }
+  }
+}
+
+// y[m, n .. n+3] = sum over splits z (in order) of part[z, m, n .. n+3],
+// rounded to bf16; one thread per 4 outputs.
+__global__ __launch_bounds__(256) void wo_finish_kernel(const float* __restrict__ part,
+                                                        uint16_t* __restrict__ y, int M, int N,
+                                                        int ksplit) {
+  const size_t q = (size_t)blockIdx.x * 256 + threadIdx.x;
+  const size_t total = (size_t)M * N / 4;
+  if (q >= total) return;
+  const size_t MN = (size_t)M * N;
+  f32x4 s = *reinterpret_cast<const f32x4*>(part + 4 * q);
+  for (int z = 1; z < ksplit; ++z) {
+    const f32x4 v = *reinterpret_cast<const f32x4*>(part + z * MN + 4 * q);
+    s[0] += v[0];
+    s[1] += v[1];
+    s[2] += v[2];
+    s[3] += v[3];
+  }
+  u16x4 h;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) h[e] = f32_to_bf16(s[e]);
+  *reinterpret_cast<u16x4*>(y + 4 * q) = h;
+}
+
+// Any element types and shape: one thread per output, the whole dot product
+// in fp32, rounded once.
+template <typename XE, typename WE>
+__global__ __launch_bounds__(256) void wo_gemm_generic_kernel(const XE* __restrict__ x,
+                                                              const WE* __restrict__ w,
+                                                              WE* __restrict__ y, int M, int N,
+                                                              int K) {
+  const int n = blockIdx.x * 256 + threadIdx.x;
+  if (n >= N) return;
+  const WE* wr = w + (size_t)n * K;
+  for (int m = blockIdx.y; m < M; m += gridDim.y) {
+    const XE* xr = x + (size_t)m * K;
+    float s = 0.0f;
+    for (int k = 0; k < K; ++k) s += Elem<XE>::load(xr, k) * Elem<WE>::load(wr, k);
+    Elem<WE>::store(y, (size_t)m * N + n, s);
+  }
+}
+
+constexpr int FOLD_R = 16;    // rows of W^O per workgroup
+constexpr int FOLD_VMAX = 256;
+
+// W_fold[i, h*d_c + c] = sum_v W^O[i, h*d_v + v] W^UV[h, v, c] in fp32, rounded
+// once.  Workgroup (c block, i block, h): thread c, rows i0 .. i0+15; the 16 x
+// d_v block of W^O is staged in LDS (d_v <= 256), W^UV[h, v, c] is read along
+// c (coalesced).
+template <typename E>
+__global__ __launch_bounds__(256) void fold_uv_o_kernel(const E* __restrict__ w_uv,
+                                                        const E* __restrict__ w_o,
+                                                        E* __restrict__ w_fold, int H, int d_v,
+                                                        int d_c, int d) {
+  __shared__ float so[FOLD_R * FOLD_VMAX];
+  const int c = blockIdx.x * 256 + threadIdx.x;
+  const int i0 = blockIdx.y * FOLD_R;
+  const int h = blockIdx.z;
+  const int rows = min(FOLD_R, d - i0);
+  for (int q = threadIdx.x; q < FOLD_R * d_v; q += 256) {
+    const int r = q / d_v, v = q - r * d_v;
+    so[r * FOLD_VMAX + v] =
+        r < rows ? Elem<E>::load(w_o, (size_t)(i0 + r) * H * d_v + (size_t)h * d_v + v) : 0.0f;
+  }
+  __syncthreads();
+  if (c >= d_c) return;
+  float acc[FOLD_R];
+#pragma unroll
+  for (int r = 0; r < FOLD_R; ++r) acc[r] = 0.0f;
+  const E* uv = w_uv + (size_t)h * d_v * d_c + c;
+  for (int v = 0; v < d_v; ++v) {
+    const float u = Elem<E>::load(uv, (size_t)v * d_c);
+#pragma unroll
+    for (int r = 0; r < FOLD_R; ++r) acc[r] += so[r * FOLD_VMAX + v] * u;
+  }
+  const size_t ld = (size_t)H * d_c;
+#pragma unroll
+  for (int r = 0; r < FOLD_R; ++r)
+    if (r < rows) Elem<E>::store(w_fold, (size_t)(i0 + r) * ld + (size_t)h * d_c + c, acc[r]);
+}
+
+}  // namespace
+
+bool wo_gemm_mfma_supported(int dtype, int N, int K) {
+  return dtype == 1 && K > 0 && K % 32 == 0 && N > 0 && N % 4 == 0;
+}
+
+int wo_gemm_ksplit(int dtype, int M, int N, int K, int target_workgroups) {
+  if (!wo_gemm_mfma_supported(dtype, N, K) || M <= 0) return 1;
+  const long long tiles = (long long)((N + WO_TN - 1) / WO_TN) * ((M + WO_TM - 1) / WO_TM);
+  const int nk = K / 32;
+  long long ks = (target_workgroups + tiles - 1) / tiles;
+  if (ks < 1) ks = 1;
+  if (ks > nk) ks = nk;
+  const int per = (int)((nk + ks - 1) / ks);
+  return (nk + per - 1) / per;
+}
+
+hipError_t launch_wo_gemm(int dtype, bool x_f32, const void* x, const void* w, void* y,
+                          float* part, int ksplit, int M, int N, int K, hipStream_t stream) {
+  if (M <= 0 || N <= 0) return hipSuccess;
+  if (wo_gemm_mfma_supported(dtype, N, K)) {
+    const int nk = K / 32;
+    const int per = (nk + ksplit - 1) / ksplit;
+    const long long tiles =
+        (long long)((N + WO_TN - 1) / WO_TN) * ((M + WO_TM - 1) / WO_TM) * ksplit;
+    if (tiles > 0x7fffffffLL) return hipErrorInvalidValue;
+    if (ksplit > 1 && part == nullptr) return hipErrorInvalidValue;
+    uint16_t* yd = ksplit == 1 ? static_cast<uint16_t*>(y) : nullptr;
+    if (x_f32)
+      hipLaunchKernelGGL(wo_gemm_mfma_kernel<float>, dim3((unsigned)tiles), dim3(256), 0, stream,
+                         static_cast<const float*>(x), static_cast<const uint16_t*>(w), yd, part,
+                         M, N, K, per);
+    else
+      hipLaunchKernelGGL(wo_gemm_mfma_kernel<uint16_t>, dim3((unsigned)tiles), dim3(256), 0,
+                         stream, static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(w),
+                         yd, part, M, N, K, per);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || ksplit == 1) return e;
+    const size_t quads = (size_t)M * N / 4;
+    hipLaunchKernelGGL(wo_finish_kernel, dim3((unsigned)((quads + 255) / 256)), dim3(256), 0,
+                       stream, part, static_cast<uint16_t*>(y), M, N, ksplit);
+    return hipGetLastError();
+  }
+  if (ksplit != 1) return hipErrorInvalidValue;
+  const dim3 grid((N + 255) / 256, min(M, 65535));
+  if (dtype == 0) {
+    if (!x_f32) return hipErrorInvalidValue;  // fp32 configurations have fp32 rows
+    hipLaunchKernelGGL((wo_gemm_generic_kernel<float, float>), grid, dim3(256), 0, stream,
+                       static_cast<const float*>(x), static_cast<const float*>(w),
+                       static_cast<float*>(y), M, N, K);
+  } else if (x_f32) {
+    hipLaunchKernelGGL((wo_gemm_generic_kernel<float, uint16_t>), grid, dim3(256), 0, stream,
+                       static_cast<const float*>(x), static_cast<const uint16_t*>(w),
+                       static_cast<uint16_t*>(y), M, N, K);
+  } else {
+    hipLaunchKernelGGL((wo_gemm_generic_kernel<uint16_t, uint16_t>), grid, dim3(256), 0, stream,
+                       static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(w),
+                       static_cast<uint16_t*>(y), M, N, K);
+  }
+  return hipGetLastError();
+}
+
+bool fold_uv_o_supported(int d_v) { return d_v > 0 && d_v <= FOLD_VMAX; }
+
+hipError_t launch_fold_uv_o(int dtype, const void* w_uv, const void* w_o, void* w_fold, int H,
+                            int d_v, int d_c, int d, hipStream_t stream) {
+  if (H <= 0 || d_c <= 0 || d <= 0) return hipSuccess;
+  if (!fold_uv_o_supported(d_v) || H > 65535 || (d + FOLD_R - 1) / FOLD_R > 65535)
+    return hipErrorInvalidValue;
+  const dim3 grid((d_c + 255) / 256, (d + FOLD_R - 1) / FOLD_R, H);
+  if (dtype == 0)
+    hipLaunchKernelGGL(fold_uv_o_kernel<float>, grid, dim3(256), 0, stream,
+                       static_cast<const float*>(w_uv), static_cast<const float*>(w_o),
+                       static_cast<float*>(w_fold), H, d_v, d_c, d);
+  else
+    hipLaunchKernelGGL(fold_uv_o_kernel<uint16_t>, grid, dim3(256), 0, stream,
+                       static_cast<const uint16_t*>(w_uv), static_cast<const uint16_t*>(w_o),
+                       static_cast<uint16_t*>(w_fold), H, d_v, d_c, d);
+  return hipGetLastError();
+}
+
+}  // namespace mla

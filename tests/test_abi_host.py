@@ -193,6 +193,42 @@ def test_producer_and_rope_validation(lib):
     assert r(ctypes.byref(v3_cfg(d_rope=0)), FAKE, 128, FAKE, 4, 0.0, None) == OK
 
 
+def test_output_side_validation(lib):
+    """mla_o_proj / mla_fold_uv_o / mla_o_proj_folded: host checks and the
+    split-k workspace (a whole number of fp32 [M, d_model] partial slices)."""
+    cfg = v3_cfg(d_v=40)
+    c = ctypes.byref(cfg)
+    ws = lib.mla_o_proj_workspace_size
+    M, d = 128, 5120
+    for folded in (0, 1):
+        need = ws(c, M, d, folded)
+        assert need % 256 == 0 and need >= 2 * M * d * 4           # k is split
+        assert need == -(-(need // (M * d * 4) * M * d * 4) // 256) * 256
+    assert ws(c, 0, d, 0) == 0
+    assert ws(c, M, 0, 0) == ctypes.c_size_t(-1).value
+    assert ws(ctypes.byref(v3_cfg(d_v=0)), M, d, 0) == ctypes.c_size_t(-1).value
+    assert ws(ctypes.byref(v3_cfg(dtype=0)), M, d, 0) == 0          # fp32: no split
+    need = ws(c, M, d, 0)
+    f = lib.mla_o_proj
+    assert f(c, None, FAKE, FAKE, M, d, FAKE, need, None) == NULL
+    assert f(c, FAKE, FAKE, FAKE_MIS, M, d, FAKE, need, None) == ALIGN
+    assert f(c, FAKE, FAKE, FAKE, M, 0, FAKE, need, None) == DIM
+    assert f(c, FAKE, FAKE, FAKE, -1, d, FAKE, need, None) == DIM
+    assert f(c, FAKE, FAKE, FAKE, M, d, None, 0, None) == WS
+    assert f(c, FAKE, FAKE, FAKE, M, d, FAKE, need - 1, None) == WS
+    assert f(c, FAKE, FAKE, FAKE, 0, d, None, 0, None) == OK
+    g = lib.mla_o_proj_folded
+    needf = ws(c, M, d, 1)
+    assert g(c, FAKE, None, FAKE, M, d, FAKE, needf, None) == NULL
+    assert g(c, FAKE, FAKE, FAKE, M, d, FAKE, needf - 1, None) == WS
+    assert g(c, FAKE, FAKE, FAKE, 0, d, None, 0, None) == OK
+    h = lib.mla_fold_uv_o
+    assert h(c, None, FAKE, FAKE, d, None) == NULL
+    assert h(c, FAKE, FAKE, FAKE_MIS, d, None) == ALIGN
+    assert h(c, FAKE, FAKE, FAKE, 0, None) == DIM
+    assert h(ctypes.byref(v3_cfg(d_v=257)), FAKE, FAKE, FAKE, d, None) == DIM
+
+
 def test_debug_helpers_validation(lib):
     cfg = v3_cfg()
     c = ctypes.byref(cfg)

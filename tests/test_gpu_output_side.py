@@ -1,0 +1,179 @@
+"""GPU parity of the output side through the C ABI, against the fp64 oracle
+on the same seeded inputs:
+
+* mla_o_proj (y = W^O over the concatenated heads): per element within bf16
+  rounding (2^-8 relative) plus an fp32-accumulation floor, or 1e-5 relative
+  for fp32;
+* mla_fold_uv_o (W^UV folded into W^O): per element, the same bound;
+* mla_o_proj_folded (the folded matrix on the fp32 latent outputs, rounded to
+  bf16 as they are read): within 2e-2 of max|y|, the bound of the bf16 path;
+* MFMA kernel with and without a k split, ragged token and output tiles, the
+  generic kernel (widths that are not a multiple of 32 or 4) and fp32;
+* the k-split partial sums are added in a fixed order: reruns are bit-exact;
+* at the V2-scale widths and full size, with the launch configuration the
+  benchmark times: every output of W^O, sampled rows of the folded matrix and
+  of its product.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from mla_latent_kv_36_amd import binding as mla
+from workloads import TINY, V2_MULTI, make_output_inputs
+from workloads.device import to_dev
+
+from gpu_util import cfg_of, note
+
+pytestmark = pytest.mark.gpu
+TDT = {"bf16": torch.bfloat16, "f32": torch.float32}
+
+CASES = {
+    # MFMA kernel, k split: 12 tokens, the V2-scale heads, d = 5120
+    "v2_reduced": V2_MULTI.scaled(B=3, T=4),
+    # two token tiles, the second ragged (70 tokens), output tile ragged
+    "v2_many_tokens": V2_MULTI.scaled(B=70, T=1, d_model=200),
+    # generic kernel: an output width that is not a multiple of 4
+    "bf16_odd_width": V2_MULTI.scaled(B=2, T=2, d_model=198),
+    # generic kernel: k = H * d_v = 30 is not a multiple of 32
+    "bf16_odd_k": V2_MULTI.scaled(B=2, T=3, H=3, d_v=10, d_c=64, d_model=64),
+    # fp32 configuration: the generic kernel
+    "tiny_f32": TINY.scaled(B=2, T=3, d_model=48),
+}
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    mla.load()
+
+
+def _ws(cfg, M, d, folded):
+    n = mla.mla_o_proj_workspace_size(cfg, M, d, folded)
+    return torch.empty(n, dtype=torch.uint8, device="cuda") if n > 0 else None
+
+
+def _o_proj(w, oi):
+    cfg = cfg_of(w)
+    dt = TDT[w.dtype]
+    M = w.B * w.T
+    y = torch.full((M, w.d_model), float("nan"), dtype=dt, device="cuda")
+    mla.mla_o_proj(cfg, to_dev(oi.attn, dt, "cuda"), to_dev(oi.w_o, dt, "cuda"), y,
+                   _ws(cfg, M, w.d_model, False))
+    torch.cuda.synchronize()
+    return y
+
+
+def _fold(w, oi):
+    cfg = cfg_of(w)
+    dt = TDT[w.dtype]
+    wf = torch.full((w.d_model, w.H * w.d_c), float("nan"), dtype=dt, device="cuda")
+    mla.mla_fold_uv_o(cfg, to_dev(oi.w_uv, dt, "cuda"), to_dev(oi.w_o, dt, "cuda"), wf)
+    torch.cuda.synchronize()
+    return wf
+
+
+def _folded(w, oi, wf):
+    cfg = cfg_of(w)
+    M = w.B * w.T
+    y = torch.full((M, w.d_model), float("nan"), dtype=TDT[w.dtype], device="cuda")
+    mla.mla_o_proj_folded(cfg, torch.from_numpy(oi.o_lat).cuda(), wf, y,
+                          _ws(cfg, M, w.d_model, True))
+    torch.cuda.synchronize()
+    return y
+
+
+def _assert_rounded(got, want, dtype):
+    got = np.asarray(got, np.float64)
+    mx = float(np.max(np.abs(want)))
+    if dtype == "bf16":
+        bound = 2.0 ** -8 * np.abs(want) + 1e-4 * mx
+    else:
+        bound = 1e-5 * np.abs(want) + 1e-6 * mx
+    err = np.abs(got - want)
+    assert np.all(np.isfinite(got))
+    assert np.all(err <= bound), float(np.max(err / np.maximum(bound, 1e-30)))
+
+
+def _assert_within(got, want, tol):
+    got = np.asarray(got, np.float64)
+    assert np.all(np.isfinite(got))
+    err = float(np.max(np.abs(got - want)))
+    assert err <= tol * float(np.max(np.abs(want))), err / float(np.max(np.abs(want)))
+
+
+def _tol(w):
+    return 2e-2 if w.dtype == "bf16" else 1e-4
+
+
+@pytest.mark.parametrize("name", list(CASES))
+def test_o_proj_matches_oracle(name):
+    w = CASES[name]
+    oi = make_output_inputs(w)
+    note(f"o_proj {name} M={w.B * w.T} K={w.H * w.d_v} d={w.d_model}")
+    y = _o_proj(w, oi)
+    _assert_rounded(y.float().cpu().numpy(), oracle.o_proj_ref(oi.attn, oi.w_o), w.dtype)
+
+
+@pytest.mark.parametrize("name", list(CASES))
+def test_fold_and_folded_product_match_oracle(name):
+    w = CASES[name]
+    if w.name == V2_MULTI.name and w.d_model == V2_MULTI.d_model:
+        w = w.scaled(d_model=256)   # the full-width fold is checked by rows below
+    oi = make_output_inputs(w)
+    note(f"fold {name} H={w.H} d_v={w.d_v} d_c={w.d_c} d={w.d_model}")
+    wf = _fold(w, oi)
+    wf_ref = oracle.fold_uv_o_ref(oi.w_uv, oi.w_o)
+    _assert_rounded(wf.float().cpu().numpy(), wf_ref, w.dtype)
+    y = _folded(w, oi, wf)
+    _assert_within(y.float().cpu().numpy(), oracle.o_proj_folded_ref(oi.o_lat, wf_ref), _tol(w))
+
+
+def test_unfolded_chain_matches_oracle():
+    """out_proj then o_proj on the GPU (the per-head outputs rounded to bf16 in
+    between, as the library hands them on) against the fp64 chain."""
+    w = CASES["v2_reduced"]
+    oi = make_output_inputs(w)
+    cfg = cfg_of(w)
+    M = w.B * w.T
+    note("output side chain")
+    attn = torch.empty((M, w.H, w.d_v), dtype=torch.bfloat16, device="cuda")
+    mla.mla_out_proj(cfg, torch.from_numpy(oi.o_lat).cuda(), to_dev(oi.w_uv, torch.bfloat16, "cuda"),
+                     attn)
+    y = torch.empty((M, w.d_model), dtype=torch.bfloat16, device="cuda")
+    mla.mla_o_proj(cfg, attn, to_dev(oi.w_o, torch.bfloat16, "cuda"), y,
+                   _ws(cfg, M, w.d_model, False))
+    torch.cuda.synchronize()
+    want = oracle.o_proj_ref(oracle.out_proj_ref(oi.o_lat, oi.w_uv), oi.w_o)
+    _assert_within(y.float().cpu().numpy(), want, 2e-2)
+
+
+def test_o_proj_rerun_bit_exact():
+    w = CASES["v2_reduced"]
+    cfg = cfg_of(w)
+    assert mla.mla_o_proj_workspace_size(cfg, w.B * w.T, w.d_model) > 0   # k is split
+    oi = make_output_inputs(w)
+    note("o_proj rerun")
+    a, b = _o_proj(w, oi), _o_proj(w, oi)
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+def test_output_side_full_size_v2():
+    """The V2-scale output side at full size: 128 tokens (32 sequences x 4),
+    128 heads, d_v = 40, d = 5120.  Every output of W^O; the folded matrix
+    (5,120 x 65,536) and its product on 48 sampled output rows."""
+    w = V2_MULTI
+    oi = make_output_inputs(w)
+    note("output side v2 full size")
+    y = _o_proj(w, oi)
+    _assert_rounded(y.float().cpu().numpy(), oracle.o_proj_ref(oi.attn, oi.w_o), w.dtype)
+    wf = _fold(w, oi)
+    yf = _folded(w, oi, wf).float().cpu().numpy()
+    rows = np.sort(np.random.default_rng(77).choice(w.d_model, 48, replace=False))
+    rows[-1] = w.d_model - 1
+    wf_ref = oracle.fold_uv_o_ref(oi.w_uv, oi.w_o[rows])
+    got_rows = wf[torch.from_numpy(rows).cuda()].float().cpu().numpy()
+    _assert_rounded(got_rows, wf_ref, w.dtype)
+    want = oracle.o_proj_folded_ref(oi.o_lat, wf_ref)          # [M, 48]
+    _assert_within(yf[:, rows], want, 2e-2)

@@ -186,3 +186,33 @@ def make_producer_inputs(w: Workload, seed: int | None = None) -> ProducerInputs
     w_kr = rnd(rng.standard_normal((w.d_r, d), dtype=np.float32) * s)
     return ProducerInputs(hidden=hidden, w_dkv=w_dkv, w_kr=w_kr)
 
+
+@dataclass
+class OutputInputs:
+    """Inputs of the output side of one batch (M = B * T tokens): per-head
+    outputs, latent outputs, W^UV and the output projection W^O."""
+    attn: np.ndarray     # [M, H, d_v]  (what the W^UV up-projection hands on)
+    o_lat: np.ndarray    # [M, H, d_c]  float32 (what decode hands on)
+    w_uv: np.ndarray     # [H, d_v, d_c]
+    w_o: np.ndarray      # [d, H * d_v]
+
+
+def make_output_inputs(w: Workload, seed: int | None = None) -> OutputInputs:
+    """Draws for the output side, from their own ``default_rng`` stream (seed
+    2000 + the workload's seed by default).  Order: ``attn [M, H, d_v]`` ~ N(0, 1);
+    ``o_lat [M, H, d_c]`` ~ N(0, 1) in float32; ``W^UV [H, d_v, d_c]`` ~ N(0, 1)
+    times 1/sqrt(d_c); ``W^O [d, H*d_v]`` ~ N(0, 1) times 1/sqrt(H*d_v) (standard
+    deviation 1/sqrt(fan-in)).  Rounded to bf16 like the rest when the workload
+    is bf16 (o_lat stays float32)."""
+    if w.d_model <= 0:
+        raise ValueError(f"workload {w.name} has no model width for the output side")
+    rng = np.random.default_rng(2000 + w.seed if seed is None else seed)
+    rnd = bf16_round if w.dtype == "bf16" else (lambda a: a.astype(np.float32))
+    M, H = w.B * w.T, w.H
+    attn = rnd(rng.standard_normal((M, H, w.d_v), dtype=np.float32))
+    o_lat = rng.standard_normal((M, H, w.d_c), dtype=np.float32)
+    w_uv = rnd(rng.standard_normal((H, w.d_v, w.d_c), dtype=np.float32)
+               * np.float32(1.0 / np.sqrt(w.d_c)))
+    w_o = rnd(rng.standard_normal((w.d_model, H * w.d_v), dtype=np.float32)
+              * np.float32(1.0 / np.sqrt(H * w.d_v)))
+    return OutputInputs(attn=attn, o_lat=o_lat, w_uv=w_uv, w_o=w_o)
