@@ -44,6 +44,12 @@ constexpr int WO_KC = 256;         // k per LDS chunk (8 MFMA k-steps)
 constexpr int WO_LD = WO_KC + 8;   // bf16 per LDS row: 528 B
 constexpr int WO_PIECES = WO_KC / 8;               // 16-byte bf16 pieces per row
 constexpr int WO_PER = WO_TM * WO_PIECES / 256;    // pieces per thread and operand
+constexpr int WO_NT = 256;         // threads of the direct kernel: 4 waves x 16 weight rows
+constexpr int WO_DEPTH = 4;        // direct kernel: chunks of 4 k steps in flight per wave
+constexpr int WO_DC = 8;           // direct kernel: chunks per k split (32 k steps)
+// 16 zero bytes in global memory (never written): the weight fragment of a
+// step past the range
+__device__ __align__(16) uint32_t kZero16[4] = {0u, 0u, 0u, 0u};
 
 typedef __attribute__((__vector_size__(4 * sizeof(uint16_t)))) uint16_t u16x4;
 
@@ -161,8 +167,83 @@ __global__ __launch_bounds__(256, 2) void wo_gemm_mfma_kernel(
   }
 }
 
+// The same product for at most 16 tokens, with no LDS and no barrier: each
+// wave loads its own A fragments (16 weight rows, row l & 15, k 8(l >> 4) ..
+// +7 of each 32-k step) and the B fragments of the 16 token rows straight
+// into a register ring WO_DEPTH chunks of 4 k steps deep.  A chunk's MFMAs
+// wait only for that chunk's loads; the token rows, the same for every wave,
+// come from the caches.  A split is at most WO_DC chunks (the k split makes
+// it so), loaded on clamped indices; the steps past the range multiply a
+// weight fragment of zeros.
+template <typename XE>
+__global__ __launch_bounds__(WO_NT) void wo_stream_direct_kernel(
+    const XE* __restrict__ x, const uint16_t* __restrict__ w, uint16_t* __restrict__ y,
+    float* __restrict__ part, int M, int N, int K, int steps_per_split) {
+  const int ntn = (N + WO_TN - 1) / WO_TN;
+  const int total = (int)gridDim.x;
+  const int full = total - total % 8;
+  const int i = blockIdx.x;
+  const int t = i < full ? (i % 8) * (full / 8) + i / 8 : i;
+  const int n0 = (t % ntn) * WO_TN;
+  const int z = t / ntn;
+  const int nk = K / 32;
+  const int s_begin = z * steps_per_split;
+  const int nsteps = min(s_begin + steps_per_split, nk) - s_begin;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int l16 = lane & 15;
+  const int g = lane >> 4;
+
+  const uint16_t* wrow = w + (size_t)min(n0 + 16 * wave + l16, N - 1) * K + 32 * s_begin + 8 * g;
+  const XE* xrow = x + (size_t)min(l16, M - 1) * K + 32 * s_begin + 8 * g;
+  // steps past the range read their weight fragment from a block of zeros
+  // (an address select: selecting the loaded value instead would make the
+  // compiler branch around the load and wait for it)
+  auto load = [&](int c, bf16x8* a, bf16x8* b) {
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const int st = 4 * c + s;
+      const int off = 32 * min(st, nsteps - 1);
+      const uint16_t* pa = st < nsteps ? wrow + off : reinterpret_cast<const uint16_t*>(kZero16);
+      a[s] = *reinterpret_cast<const bf16x8*>(pa);
+      b[s] = __builtin_bit_cast(bf16x8, load_piece(xrow + off));
+    }
+  };
+  bf16x8 wa[WO_DEPTH][4], xb[WO_DEPTH][4];
+#pragma unroll
+  for (int d = 0; d < WO_DEPTH; ++d) load(d, wa[d], xb[d]);
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  // straight-line code over the split's WO_DC chunks: with a loop, the
+  // compiler waits for every load in flight at the loop head
+#pragma unroll
+  for (int c = 0; c < WO_DC; ++c) {
+    const int d = c % WO_DEPTH;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) acc = mfma16(wa[d][s], xb[d][s], acc);
+    if (c + WO_DEPTH < WO_DC) {
+      // the refill stays right here: hoisted above the MFMAs, its data
+      // would be waited for at once
+      __builtin_amdgcn_sched_barrier(0);
+      load(c + WO_DEPTH, wa[d], xb[d]);   // clamped past the range
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+  const int n = n0 + 16 * wave + 4 * g;
+  const int m = l16;
+  if (n >= N || m >= M) return;
+  if (y != nullptr) {
+    u16x4 h;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) h[e] = f32_to_bf16(acc[e]);
+    *reinterpret_cast<u16x4*>(y + (size_t)m * N + n) = h;
+  } else {
+    *reinterpret_cast<f32x4*>(part + ((size_t)z * M + m) * N + n) = acc;
+  }
+}
+
 // y[m, n .. n+3] = sum over splits z (in order) of part[z, m, n .. n+3],
-// rounded to bf16; one thread per 4 outputs.
+// rounded to bf16; one thread per 4 outputs.  The loads of up to 16 splits
+// are issued (on clamped indices) before the first is added.
 __global__ __launch_bounds__(256) void wo_finish_kernel(const float* __restrict__ part,
                                                         uint16_t* __restrict__ y, int M, int N,
                                                         int ksplit) {
@@ -170,13 +251,21 @@ __global__ __launch_bounds__(256) void wo_finish_kernel(const float* __restrict_
   const size_t total = (size_t)M * N / 4;
   if (q >= total) return;
   const size_t MN = (size_t)M * N;
-  f32x4 s = *reinterpret_cast<const f32x4*>(part + 4 * q);
-  for (int z = 1; z < ksplit; ++z) {
-    const f32x4 v = *reinterpret_cast<const f32x4*>(part + z * MN + 4 * q);
-    s[0] += v[0];
-    s[1] += v[1];
-    s[2] += v[2];
-    s[3] += v[3];
+  f32x4 s = {0.f, 0.f, 0.f, 0.f};
+  for (int z0 = 0; z0 < ksplit; z0 += 16) {
+    f32x4 v[16];
+#pragma unroll
+    for (int k = 0; k < 16; ++k)
+      v[k] = *reinterpret_cast<const f32x4*>(part + (size_t)min(z0 + k, ksplit - 1) * MN + 4 * q);
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      if (z0 + k < ksplit) {
+        s[0] += v[k][0];
+        s[1] += v[k][1];
+        s[2] += v[k][2];
+        s[3] += v[k][3];
+      }
+    }
   }
   u16x4 h;
 #pragma unroll
@@ -249,6 +338,8 @@ bool wo_gemm_mfma_supported(int dtype, int N, int K) {
 
 int wo_gemm_ksplit(int dtype, int M, int N, int K, int target_workgroups) {
   if (!wo_gemm_mfma_supported(dtype, N, K) || M <= 0) return 1;
+  // up to 16 tokens: the direct kernel, WO_DC chunks of 4 k steps per split
+  if (M <= 16) return (K / 32 + 4 * WO_DC - 1) / (4 * WO_DC);
   const long long tiles = (long long)((N + WO_TN - 1) / WO_TN) * ((M + WO_TM - 1) / WO_TM);
   const int nk = K / 32;
   long long ks = (target_workgroups + tiles - 1) / tiles;
@@ -261,6 +352,28 @@ int wo_gemm_ksplit(int dtype, int M, int N, int K, int target_workgroups) {
 hipError_t launch_wo_gemm(int dtype, bool x_f32, const void* x, const void* w, void* y,
                           float* part, int ksplit, int M, int N, int K, hipStream_t stream) {
   if (M <= 0 || N <= 0) return hipSuccess;
+  if (wo_gemm_mfma_supported(dtype, N, K) && M <= 16) {
+    const int nk = K / 32;
+    if (ksplit != (nk + 4 * WO_DC - 1) / (4 * WO_DC)) return hipErrorInvalidValue;
+    const long long tiles = (long long)((N + WO_TN - 1) / WO_TN) * ksplit;
+    if (tiles > 0x7fffffffLL) return hipErrorInvalidValue;
+    if (ksplit > 1 && part == nullptr) return hipErrorInvalidValue;
+    uint16_t* yd = ksplit == 1 ? static_cast<uint16_t*>(y) : nullptr;
+    if (x_f32)
+      hipLaunchKernelGGL(wo_stream_direct_kernel<float>, dim3((unsigned)tiles), dim3(WO_NT), 0,
+                         stream, static_cast<const float*>(x), static_cast<const uint16_t*>(w),
+                         yd, part, M, N, K, 4 * WO_DC);
+    else
+      hipLaunchKernelGGL(wo_stream_direct_kernel<uint16_t>, dim3((unsigned)tiles), dim3(WO_NT), 0,
+                         stream, static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(w),
+                         yd, part, M, N, K, 4 * WO_DC);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || ksplit == 1) return e;
+    const size_t quads = (size_t)M * N / 4;
+    hipLaunchKernelGGL(wo_finish_kernel, dim3((unsigned)((quads + 255) / 256)), dim3(256), 0,
+                       stream, part, static_cast<uint16_t*>(y), M, N, ksplit);
+    return hipGetLastError();
+  }
   if (wo_gemm_mfma_supported(dtype, N, K)) {
     const int nk = K / 32;
     const int per = (nk + ksplit - 1) / ksplit;
