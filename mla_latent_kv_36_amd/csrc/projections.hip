@@ -158,20 +158,15 @@ __global__ __launch_bounds__(PJ_NT) void absorb_q_mfma_kernel(
 
   // B fragments (query rows) of the first tile are requested before the
   // weight, so both loads are in flight together.
-  // The loads are unconditional, on a clamped row and offset, and what lies
-  // outside is replaced by zeros afterwards: conditional loads would each be
-  // waited for before the next is issued.
+  // The loads are unconditional, on a clamped row and offset, and nothing is
+  // selected on the loaded values (a select, like a conditional load, makes
+  // the compiler wait for the load at once): rows past mend feed outputs that
+  // are not stored, k-steps past d_n are not multiplied, and k past d_n
+  // within the last step meets the zero rows of the staged weight.
   auto load_q = [&](int m0, bf16x8* bq) {
-    const int m = m0 + i16;
-    const uint16_t* qrow = q_nope + ((size_t)min(m, mend - 1) * H + h) * d_n;
-    bf16x8 raw[AB_KS];
+    const uint16_t* qrow = q_nope + ((size_t)min(m0 + i16, mend - 1) * H + h) * d_n;
 #pragma unroll
-    for (int ks = 0; ks < AB_KS; ++ks) raw[ks] = load_bf16x8(qrow + min(32 * ks + 8 * g, d_n - 8));
-#pragma unroll
-    for (int ks = 0; ks < AB_KS; ++ks) {
-      const bool in = ks < nks && m < mend && 32 * ks + 8 * g < d_n;
-      bq[ks] = in ? raw[ks] : bf16x8{};
-    }
+    for (int ks = 0; ks < AB_KS; ++ks) bq[ks] = load_bf16x8(qrow + min(32 * ks + 8 * g, d_n - 8));
   };
   bf16x8 bq[AB_KS];
   load_q(mbeg, bq);
@@ -184,18 +179,22 @@ __global__ __launch_bounds__(PJ_NT) void absorb_q_mfma_kernel(
   u32x4 sv[ST];
 #pragma unroll
   for (int u = 0; u < ST; ++u) {
-    const int i = tid + u * PJ_NT;
+    // clamped like the stores below, so that a thread past the last piece
+    // loads (and rewrites) exactly that piece
+    const int i = min(tid + u * PJ_NT, pieces - 1);
     const int d = i / (AB_CT / 8), ch = i % (AB_CT / 8);
     sv[u] = *reinterpret_cast<const u32x4*>(wsrc + (size_t)min(d, d_n - 1) * d_c + ch * 8);
   }
+  // every load is issued before the first is used
+  __builtin_amdgcn_sched_barrier(0);
+  // branch-free (a branch would make the compiler wait for every load): a
+  // clamped index rewrites the last piece with the same value
 #pragma unroll
   for (int u = 0; u < ST; ++u) {
-    const int i = tid + u * PJ_NT;
+    const int i = min(tid + u * PJ_NT, pieces - 1);
     const int d = i / (AB_CT / 8), ch = i % (AB_CT / 8);
-    if (i < pieces) {
-      const u32x4 z = {0u, 0u, 0u, 0u};
-      *reinterpret_cast<u32x4*>(wl + d * AB_LD + ch * 16) = d < d_n ? sv[u] : z;
-    }
+    const u32x4 z = {0u, 0u, 0u, 0u};
+    *reinterpret_cast<u32x4*>(wl + d * AB_LD + ch * 16) = d < d_n ? sv[u] : z;
   }
   __syncthreads();
 
@@ -265,24 +264,14 @@ __global__ __launch_bounds__(PJ_NT) void out_proj_mfma_kernel(
   const int nks = d_c >> 5;
   const int vrow = vb * OP_VT + 16 * wave + i16;  // A row of this lane
 
-  // W^UV fragments: unconditional loads on a clamped row and k-step, zeros
-  // selected afterwards (conditional loads would be waited for one by one)
-  bf16x8 a[OP_KS];
-  const uint16_t* wrow = w_uv + ((size_t)h * d_v + min(vrow, d_v - 1)) * d_c + 8 * g;
-#pragma unroll
-  for (int ks = 0; ks < OP_KS; ++ks) a[ks] = load_bf16x8(wrow + 32 * min(ks, nks - 1));
-#pragma unroll
-  for (int ks = 0; ks < OP_KS; ++ks)
-    if (!(ks < nks && vrow < d_v)) a[ks] = bf16x8{};
-
-  const int v0 = vb * OP_VT + 16 * wave + 4 * g;  // this lane's 4 output columns
+  // The first tile of o_lat is requested before the weight: memory loads
+  // complete in issue order, so its staging below then waits for it alone
+  // while the weight is still in flight.  A thread's loads (up to OP_ST, on
+  // clamped rows) are all issued before the first is used.
   const int q4 = d_c >> 2;                        // float4 chunks per row
-  for (int m0 = mbeg; m0 < mend; m0 += 16) {
-    // stage rows m0 .. m0+15 (zeros past mend) as bf16 hi / lo; a thread's
-    // loads (up to OP_ST, on clamped rows) are all issued before the first
-    // is used
-    constexpr int OP_ST = 16 * (32 * OP_KS / 4) / PJ_NT;
-    f32x4 xs[OP_ST];
+  constexpr int OP_ST = 16 * (32 * OP_KS / 4) / PJ_NT;
+  f32x4 xs[OP_ST];
+  auto load_x = [&](int m0) {
 #pragma unroll
     for (int u = 0; u < OP_ST; ++u) {
       const int i = min(tid + u * PJ_NT, 16 * q4 - 1);
@@ -290,10 +279,30 @@ __global__ __launch_bounds__(PJ_NT) void out_proj_mfma_kernel(
       xs[u] = *reinterpret_cast<const f32x4*>(
           o_lat + ((size_t)min(m0 + r, mend - 1) * H + h) * d_c + 4 * c4);
     }
+  };
+  load_x(mbeg);
+
+  // W^UV fragments: unconditional loads on a clamped row and k-step.  Rows
+  // past d_v only feed outputs that are not stored and k-steps past d_c are
+  // not multiplied, so nothing is selected on the loaded values (a select
+  // would wait for each load at once).
+  bf16x8 a[OP_KS];
+  const uint16_t* wrow = w_uv + ((size_t)h * d_v + min(vrow, d_v - 1)) * d_c + 8 * g;
+#pragma unroll
+  for (int ks = 0; ks < OP_KS; ++ks) a[ks] = load_bf16x8(wrow + 32 * min(ks, nks - 1));
+  // every load is issued before the first o_lat value is used
+  __builtin_amdgcn_sched_barrier(0);
+
+  const int v0 = vb * OP_VT + 16 * wave + 4 * g;  // this lane's 4 output columns
+  // one 16-row tile whose o_lat is in xs
+  auto tile = [&](int m0) __attribute__((always_inline)) {
+    // stage rows m0 .. m0+15 (zeros past mend) as bf16 hi / lo
+    // (branch-free: a clamped index rewrites the last chunk with the same
+    // values, and rows past mend are zeroed by a select; a branch here would
+    // make the compiler wait for the weight loads too)
 #pragma unroll
     for (int u = 0; u < OP_ST; ++u) {
-      const int i = tid + u * PJ_NT;
-      if (i >= 16 * q4) continue;
+      const int i = min(tid + u * PJ_NT, 16 * q4 - 1);
       const int r = i / q4, c4 = i - r * q4;
       f32x4 x = xs[u];
       if (m0 + r >= mend) x = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -330,6 +339,13 @@ __global__ __launch_bounds__(PJ_NT) void out_proj_mfma_kernel(
       }
     }
     __syncthreads();  // the next tile overwrites the staging buffer
+  };
+  // The first tile is straight-line code: at a loop head the compiler would
+  // wait for the weight as well before staging it.
+  tile(mbeg);
+  for (int m0 = mbeg + 16; m0 < mend; m0 += 16) {
+    load_x(m0);
+    tile(m0);
   }
 }
 
