@@ -1,8 +1,9 @@
 #!/usr/bin/env python3
 """Benchmark one absorbed-MLA decode step on one MI355X.
 
-A step is the whole path for one batch: mla_absorb_q -> mla_cache_append ->
-mla_decode (split-KV + log-sum-exp merge) -> mla_out_proj, on the DeepSeek-V3
+A step is the whole path for one batch: mla_absorb_q and mla_cache_append (in
+one call, mla_absorb_q_append) -> mla_decode (split-KV + log-sum-exp merge) ->
+mla_out_proj, on the DeepSeek-V3
 shape workload (16 sequences x 4,096 cached rows, 128 heads, d_c = 512,
 d_rope = 64, bf16).  Inputs are seeded synthetic draws, resident in HBM before
 timing starts.  To measure HBM rather than the 256 MB last-level cache, the
@@ -319,6 +320,7 @@ def main() -> int:
         "decode": capture(lambda st: st.decode()),
         "absorb_q": capture(lambda st: st.absorb()),
         "cache_append": capture(lambda st: st.append()),
+        "absorb_q_append": capture(lambda st: st.absorb_append()),
         "out_proj": capture(lambda st: st.out_proj()),
     }
     stream = torch.cuda.current_stream()
@@ -342,6 +344,7 @@ def main() -> int:
     ms_decode = timed(graphs["decode"])
     ms_absorb = timed(graphs["absorb_q"])
     ms_append = timed(graphs["cache_append"])
+    ms_absorb_append = timed(graphs["absorb_q_append"])
     ms_out = timed(graphs["out_proj"])
 
     W = w.d_c + w.d_r
@@ -399,6 +402,7 @@ def main() -> int:
         "latent_cache_GBps_step": cache_bytes / (ms_step * 1e-3) / 1e9,
         "decode_tokens_per_s": tokens / (ms_decode * 1e-3),
         "phases_us": {"absorb_q": ms_absorb * 1e3, "cache_append": ms_append * 1e3,
+                      "absorb_q_append": ms_absorb_append * 1e3,
                       "decode": ms_decode * 1e3, "out_proj": ms_out * 1e3},
     }
     if w.d_model > 0:

@@ -120,6 +120,23 @@ mla_status mla_cache_append(const mla_config* cfg, void* pool, int32_t num_block
                             int32_t T_new, int32_t max_seq_len_host, void* stream);
 
 /*
+ * mla_absorb_q_append -- mla_absorb_q and mla_cache_append of one decode step
+ * in one call: the two are independent (the absorbed query does not read the
+ * cache), so the append's rows are copied by extra workgroups of the absorb
+ * launch (one kernel launch instead of two) where the bf16 MFMA absorb kernel
+ * applies, and by the two usual launches otherwise.  Arguments, checks and
+ * results are exactly those of the two calls (the first failing check of
+ * mla_absorb_q, then of mla_cache_append, is returned, and nothing is launched
+ * then); M == 0 or B * T_new == 0 leaves out that part.
+ */
+mla_status mla_absorb_q_append(const mla_config* cfg, const void* q_nope, const void* q_rope,
+                               const void* w_uk, void* q_abs, int32_t M, void* pool,
+                               int32_t num_blocks, const int32_t* block_table,
+                               int32_t max_blocks, const int32_t* seq_lens,
+                               const void* new_rows, int32_t B, int32_t T_new,
+                               int32_t max_seq_len_host, void* stream);
+
+/*
  * Split-KV planning for mla_decode.  Each range of cache rows is attended on
  * its own and the partial results are merged by log-sum-exp.  Two plans:
  *  - plain (num_splits > 0, or the library's choice for equal lengths): the

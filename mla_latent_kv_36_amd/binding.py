@@ -49,6 +49,8 @@ _SIGNATURES = {
     "mla_abi_version": (_I, []),
     "mla_absorb_q": (_I, [_CFG, _P, _P, _P, _P, _I, _P]),
     "mla_cache_append": (_I, [_CFG, _P, _I, _P, _I, _P, _P, _I, _I, _I, _P]),
+    "mla_absorb_q_append": (_I, [_CFG, _P, _P, _P, _P, _I, _P, _I, _P, _I, _P, _P, _I, _I, _I,
+                                 _P]),
     "mla_decode_num_splits": (_I, [_CFG, _I, _I, _I, ctypes.c_int64]),
     "mla_decode_workspace_size": (ctypes.c_size_t, [_CFG, _I, _I, _I, ctypes.c_int64, _I]),
     "mla_decode": (_I, [_CFG, _P, _P, _I, _P, _I, _P, _I, _I, _I, _I, _I, ctypes.c_int64, _P,
@@ -138,6 +140,26 @@ def mla_cache_append(cfg: MlaConfig, pool: torch.Tensor, block_table: torch.Tens
                                    _ptr(block_table), block_table.shape[1], _ptr(seq_lens),
                                    _ptr(new_rows), B, T_new, int(max_seq_len_host),
                                    _stream(stream)))
+
+
+def mla_absorb_q_append(cfg: MlaConfig, q_nope: torch.Tensor, q_rope: Optional[torch.Tensor],
+                        w_uk: torch.Tensor, q_abs: torch.Tensor, pool: torch.Tensor,
+                        block_table: torch.Tensor, seq_lens: torch.Tensor,
+                        new_rows: torch.Tensor, max_seq_len_host: int, stream=None) -> None:
+    """mla_absorb_q and mla_cache_append in one call (one launch where the
+    MFMA absorb kernel applies)."""
+    dt = _TORCH_DTYPE[cfg.dtype]
+    _dev(q_nope, dt, "q_nope"), _dev(w_uk, dt, "w_uk"), _dev(q_abs, dt, "q_abs")
+    if q_rope is not None:
+        _dev(q_rope, dt, "q_rope")
+    _dev(pool, dt, "pool"), _dev(new_rows, dt, "new_rows")
+    _dev(block_table, torch.int32, "block_table"), _dev(seq_lens, torch.int32, "seq_lens")
+    B, T_new = new_rows.shape[0], new_rows.shape[1]
+    _check(load().mla_absorb_q_append(ctypes.byref(cfg), _ptr(q_nope), _ptr(q_rope), _ptr(w_uk),
+                                      _ptr(q_abs), q_nope.shape[0], _ptr(pool), pool.shape[0],
+                                      _ptr(block_table), block_table.shape[1], _ptr(seq_lens),
+                                      _ptr(new_rows), B, T_new, int(max_seq_len_host),
+                                      _stream(stream)))
 
 
 def mla_decode_num_splits(cfg: MlaConfig, B: int, T: int, max_seq_len_host: int,

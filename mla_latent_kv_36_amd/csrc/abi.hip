@@ -137,8 +137,11 @@ const char* mla_status_string(int32_t status) {
 
 int32_t mla_abi_version(void) { return 2; }
 
-mla_status mla_absorb_q(const mla_config* cfg, const void* q_nope, const void* q_rope,
-                        const void* w_uk, void* q_abs, int32_t M, void* stream) {
+// Host checks of mla_absorb_q's arguments; *work = false when there is
+// nothing to launch (M == 0).
+static mla_status check_absorb(const mla_config* cfg, const void* q_nope, const void* q_rope,
+                               const void* w_uk, const void* q_abs, int32_t M, bool* work) {
+  *work = false;
   mla_status st = check_cfg(cfg);
   if (st != MLA_OK) return st;
   if (M < 0 || cfg->d_nope <= 0 || cfg->d_nope > kMaxDnope) return MLA_ERR_DIM;
@@ -150,15 +153,17 @@ mla_status mla_absorb_q(const mla_config* cfg, const void* q_nope, const void* q
       (q_rope != nullptr && !aligned16(q_rope)))
     return MLA_ERR_ALIGN;
   if ((int64_t)(M + 15) / 16 > 65535) return MLA_ERR_DIM;
-  return hip_status(mla::launch_absorb_q(cfg->dtype, q_nope, q_rope, w_uk, q_abs, M,
-                                         cfg->n_heads, cfg->d_nope, cfg->d_c, cfg->d_rope,
-                                         static_cast<hipStream_t>(stream)));
+  *work = true;
+  return MLA_OK;
 }
 
-mla_status mla_cache_append(const mla_config* cfg, void* pool, int32_t num_blocks,
-                            const int32_t* block_table, int32_t max_blocks,
-                            const int32_t* seq_lens, const void* new_rows, int32_t B,
-                            int32_t T_new, int32_t max_seq_len_host, void* stream) {
+// Host checks of mla_cache_append's arguments; *work = false when there is
+// nothing to launch.
+static mla_status check_append(const mla_config* cfg, const void* pool, int32_t num_blocks,
+                               const int32_t* block_table, int32_t max_blocks,
+                               const int32_t* seq_lens, const void* new_rows, int32_t B,
+                               int32_t T_new, int32_t max_seq_len_host, bool* work) {
+  *work = false;
   mla_status st = check_cfg(cfg);
   if (st != MLA_OK) return st;
   if (B < 0 || T_new < 0 || num_blocks <= 0 || max_blocks <= 0 || max_seq_len_host < 0)
@@ -170,10 +175,62 @@ mla_status mla_cache_append(const mla_config* cfg, void* pool, int32_t num_block
   if (!aligned16(pool) || !aligned16(new_rows) || !aligned16(block_table) || !aligned16(seq_lens))
     return MLA_ERR_ALIGN;
   if ((int64_t)B * T_new > 0x7fffffffLL) return MLA_ERR_DIM;
+  *work = true;
+  return MLA_OK;
+}
+
+mla_status mla_absorb_q(const mla_config* cfg, const void* q_nope, const void* q_rope,
+                        const void* w_uk, void* q_abs, int32_t M, void* stream) {
+  bool work;
+  mla_status st = check_absorb(cfg, q_nope, q_rope, w_uk, q_abs, M, &work);
+  if (st != MLA_OK || !work) return st;
+  return hip_status(mla::launch_absorb_q(cfg->dtype, q_nope, q_rope, w_uk, q_abs, M,
+                                         cfg->n_heads, cfg->d_nope, cfg->d_c, cfg->d_rope,
+                                         static_cast<hipStream_t>(stream)));
+}
+
+mla_status mla_cache_append(const mla_config* cfg, void* pool, int32_t num_blocks,
+                            const int32_t* block_table, int32_t max_blocks,
+                            const int32_t* seq_lens, const void* new_rows, int32_t B,
+                            int32_t T_new, int32_t max_seq_len_host, void* stream) {
+  bool work;
+  mla_status st = check_append(cfg, pool, num_blocks, block_table, max_blocks, seq_lens, new_rows,
+                               B, T_new, max_seq_len_host, &work);
+  if (st != MLA_OK || !work) return st;
   const int row_bytes = (cfg->d_c + cfg->d_rope) * (int)elem_size(cfg->dtype);
   return hip_status(mla::launch_append(pool, num_blocks, block_table, max_blocks, seq_lens,
                                        new_rows, B, T_new, cfg->block_size, row_bytes,
                                        static_cast<hipStream_t>(stream)));
+}
+
+mla_status mla_absorb_q_append(const mla_config* cfg, const void* q_nope, const void* q_rope,
+                               const void* w_uk, void* q_abs, int32_t M, void* pool,
+                               int32_t num_blocks, const int32_t* block_table,
+                               int32_t max_blocks, const int32_t* seq_lens,
+                               const void* new_rows, int32_t B, int32_t T_new,
+                               int32_t max_seq_len_host, void* stream) {
+  bool wa, wp;
+  mla_status st = check_absorb(cfg, q_nope, q_rope, w_uk, q_abs, M, &wa);
+  if (st != MLA_OK) return st;
+  st = check_append(cfg, pool, num_blocks, block_table, max_blocks, seq_lens, new_rows, B, T_new,
+                    max_seq_len_host, &wp);
+  if (st != MLA_OK) return st;
+  mla::AppendArgs ap{};
+  if (wp) {
+    ap.pool = pool;
+    ap.num_blocks = num_blocks;
+    ap.table = block_table;
+    ap.max_blocks = max_blocks;
+    ap.seq_lens = seq_lens;
+    ap.new_rows = new_rows;
+    ap.T_new = T_new;
+    ap.block_size = cfg->block_size;
+    ap.row_bytes = (cfg->d_c + cfg->d_rope) * (int)elem_size(cfg->dtype);
+    ap.rows = B * T_new;
+  }
+  return hip_status(mla::launch_absorb_q_append(
+      cfg->dtype, wa ? q_nope : nullptr, q_rope, w_uk, q_abs, wa ? M : 0, cfg->n_heads,
+      cfg->d_nope, cfg->d_c, cfg->d_rope, ap, static_cast<hipStream_t>(stream)));
 }
 
 int32_t mla_decode_num_splits(const mla_config* cfg, int32_t B, int32_t T,

@@ -44,6 +44,25 @@ hipError_t launch_absorb_q(int dtype, const void* q_nope, const void* q_rope,
                            int d_r, hipStream_t stream);
 hipError_t launch_out_proj(int dtype, const float* o_lat, const void* w_uv, void* out,
                            int M, int H, int d_c, int d_v, hipStream_t stream);
+// The cache append's arguments, for a kernel that carries the append along
+// with its own work (rows == 0: no append).
+struct AppendArgs {
+  void* pool;
+  int num_blocks;
+  const int32_t* table;
+  int max_blocks;
+  const int32_t* seq_lens;
+  const void* new_rows;
+  int T_new;
+  int block_size;
+  int row_bytes;
+  int rows;  // B * T_new
+};
+// absorb_q (M == 0: none) and the append in one launch where the MFMA absorb
+// kernel applies, else the two launches in turn.
+hipError_t launch_absorb_q_append(int dtype, const void* q_nope, const void* q_rope,
+                                  const void* w_uk, void* q_abs, int M, int H, int d_n, int d_c,
+                                  int d_r, const AppendArgs& ap, hipStream_t stream);
 hipError_t launch_append(void* pool, int num_blocks, const int32_t* block_table,
                          int max_blocks, const int32_t* seq_lens, const void* new_rows,
                          int B, int T_new, int block_size, int row_bytes,

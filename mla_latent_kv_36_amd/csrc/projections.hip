@@ -144,12 +144,38 @@ constexpr int OP_KS = 16;         // at most 16 k-steps of 32: d_c <= 512
 // staged in LDS (rows past d_nope zeroed, so the contraction is padded to a
 // multiple of 32), then each wave takes its 32 columns x all d_nope into
 // registers with transposing reads: the A operand, rows = latent columns.
+//
+// With ap.rows > 0 the grid has ceil(ap.rows / 4) more workgroups along x,
+// placed first, that append the new cache rows instead, one row per wave (the
+// append of a decode step rides along with the absorb: one launch less).
+// They come first in dispatch order so that their chain of dependent loads
+// (length, page id, row) runs under the absorb rather than after it.
 __global__ __launch_bounds__(PJ_NT) void absorb_q_mfma_kernel(
     const uint16_t* __restrict__ q_nope, const uint16_t* __restrict__ q_rope,
     const uint16_t* __restrict__ w_uk, uint16_t* __restrict__ q_abs, int M, int H, int d_n,
-    int d_c, int d_r) {
+    int d_c, int d_r, const AppendArgs ap) {
   extern __shared__ __align__(16) uint8_t wl[];  // [KP][AB_LD]
-  const int h = blockIdx.x, cb = blockIdx.y;
+  const int apx = (ap.rows + PJ_NT / 64 - 1) / (PJ_NT / 64);  // append workgroups along x
+  if ((int)blockIdx.x < apx) {
+    // row r = b * T_new + i goes to position seq_lens[b] + i; rows whose page
+    // or page id is out of range are skipped (as mla_cache_append does)
+    if (blockIdx.y != 0 || blockIdx.z != 0) return;
+    const int r = (int)blockIdx.x * (PJ_NT / 64) + (int)(threadIdx.x >> 6);
+    if (r >= ap.rows) return;
+    const int b = r / ap.T_new, i = r - b * ap.T_new;
+    const int pos = ap.seq_lens[b] + i;
+    const int page = pos / ap.block_size;
+    if (pos < 0 || page >= ap.max_blocks) return;
+    const int blk = ap.table[(size_t)b * ap.max_blocks + page];
+    if (blk < 0 || blk >= ap.num_blocks) return;
+    u32x4* dst = reinterpret_cast<u32x4*>(static_cast<uint8_t*>(ap.pool) +
+        ((size_t)blk * ap.block_size + (pos - page * ap.block_size)) * ap.row_bytes);
+    const u32x4* src = reinterpret_cast<const u32x4*>(
+        static_cast<const uint8_t*>(ap.new_rows) + (size_t)r * ap.row_bytes);
+    for (int k = threadIdx.x & 63; k < ap.row_bytes / 16; k += 64) dst[k] = src[k];
+    return;
+  }
+  const int h = (int)blockIdx.x - apx, cb = blockIdx.y;
   const int mbeg = blockIdx.z * PJ_MW, mend = min(M, mbeg + PJ_MW);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int i16 = lane & 15, g = lane >> 4;
@@ -368,7 +394,7 @@ hipError_t launch_absorb_q(int dtype, const void* q_nope, const void* q_rope, co
     const size_t shmem = (size_t)((d_n + 31) & ~31) * AB_LD;
     hipLaunchKernelGGL(absorb_q_mfma_kernel, grid, dim3(PJ_NT), shmem, stream,
                        (const uint16_t*)q_nope, (const uint16_t*)q_rope, (const uint16_t*)w_uk,
-                       (uint16_t*)q_abs, M, H, d_n, d_c, d_r);
+                       (uint16_t*)q_abs, M, H, d_n, d_c, d_r, AppendArgs{});
     return hipGetLastError();
   }
   const dim3 grid(H, (d_c + ABS_NT - 1) / ABS_NT, (M + ABS_MT - 1) / ABS_MT);
@@ -401,6 +427,25 @@ hipError_t launch_out_proj(int dtype, const float* o_lat, const void* w_uv, void
     hipLaunchKernelGGL(out_proj_kernel<uint16_t>, grid, dim3(256), 0, stream, o_lat,
                        (const uint16_t*)w_uv, (uint16_t*)out, M, H, d_c, d_v);
   return hipGetLastError();
+}
+
+hipError_t launch_absorb_q_append(int dtype, const void* q_nope, const void* q_rope,
+                                  const void* w_uk, void* q_abs, int M, int H, int d_n, int d_c,
+                                  int d_r, const AppendArgs& ap, hipStream_t stream) {
+  const long long extra = ((long long)ap.rows + PJ_NT / 64 - 1) / (PJ_NT / 64);
+  if (M > 0 && ap.rows > 0 && dtype == 1 && absorb_mfma_fits(d_n, d_c, d_r) &&
+      ap.row_bytes % 16 == 0 && (long long)H + extra <= 0x7fffffffLL) {
+    const dim3 grid((unsigned)(H + extra), d_c / AB_CT, (M + PJ_MW - 1) / PJ_MW);
+    const size_t shmem = (size_t)((d_n + 31) & ~31) * AB_LD;
+    hipLaunchKernelGGL(absorb_q_mfma_kernel, grid, dim3(PJ_NT), shmem, stream,
+                       (const uint16_t*)q_nope, (const uint16_t*)q_rope, (const uint16_t*)w_uk,
+                       (uint16_t*)q_abs, M, H, d_n, d_c, d_r, ap);
+    return hipGetLastError();
+  }
+  hipError_t e = launch_absorb_q(dtype, q_nope, q_rope, w_uk, q_abs, M, H, d_n, d_c, d_r, stream);
+  if (e != hipSuccess || ap.rows <= 0) return e;
+  return launch_append(ap.pool, ap.num_blocks, ap.table, ap.max_blocks, ap.seq_lens, ap.new_rows,
+                       ap.rows / ap.T_new, ap.T_new, ap.block_size, ap.row_bytes, stream);
 }
 
 }  // namespace mla

@@ -54,6 +54,13 @@ class DecodeStep:
         mla.mla_cache_append(self.cfg, self.pool, self.block_table, self.lengths, self.new_rows,
                              self.max_len_after, stream)
 
+    def absorb_append(self, stream=None):
+        """absorb and append in one call (one launch where the MFMA absorb
+        kernel applies)."""
+        mla.mla_absorb_q_append(self.cfg, self.q_nope, self.q_rope, self.w_uk,
+                                self.q_abs.view(self.M, self.H, -1), self.pool, self.block_table,
+                                self.lengths, self.new_rows, self.max_len_after, stream)
+
     def decode(self, stream=None):
         mla.mla_decode(self.cfg, self.q_abs, self.pool, self.block_table, self.seq_lens,
                        self.max_len_after, self.o_lat, self.lse, causal=self.causal,
@@ -65,7 +72,6 @@ class DecodeStep:
                          stream)
 
     def run(self, stream=None):
-        self.absorb(stream)
-        self.append(stream)
+        self.absorb_append(stream)
         self.decode(stream)
         self.out_proj(stream)

@@ -155,6 +155,23 @@ def test_absorb_and_out_proj_validation(lib):
     assert lib.mla_out_proj(c, FAKE, FAKE, FAKE, 0, None) == OK
 
 
+def test_absorb_append_validation(lib):
+    """mla_absorb_q_append reports the checks of mla_absorb_q, then those of
+    mla_cache_append, and launches nothing on an error."""
+    c = ctypes.byref(v3_cfg())
+    f = lib.mla_absorb_q_append
+    args = lambda **k: [c, k.get("qn", FAKE), FAKE, FAKE, FAKE, k.get("M", 4), k.get("pool", FAKE),
+                        10, FAKE, 4, FAKE, FAKE, k.get("B", 2), k.get("T", 2), k.get("cap", 10),
+                        None]
+    assert f(*args(qn=None)) == NULL
+    assert f(*args(M=-1)) == DIM
+    assert f(*args(cap=4 * 64 + 1)) == CAP
+    assert f(*args(pool=None)) == NULL
+    assert f(*args(pool=FAKE_MIS)) == ALIGN
+    assert f(*args(B=-1)) == DIM
+    assert f(*args(M=0, T=0)) == OK      # nothing to do on either side
+
+
 def test_producer_and_rope_validation(lib):
     cfg = v3_cfg()
     c = ctypes.byref(cfg)
