@@ -248,7 +248,7 @@ def main() -> int:
     ap.add_argument("--workload", default="v3_decode")
     ap.add_argument("--rotate", type=int, default=8)
     ap.add_argument("--num-splits", type=int, default=0)
-    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--cpu-seconds", type=float, default=20.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="only run a plain device copy of this many MiB five times "
