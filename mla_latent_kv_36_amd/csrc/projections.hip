@@ -132,7 +132,13 @@ __device__ __forceinline__ void store_bf16x4(uint16_t* p, const f32x4& v) {
 }
 
 constexpr int PJ_NT = 256;        // 4 waves
-constexpr int PJ_MW = 64;         // query rows per workgroup (4 tiles of 16)
+constexpr int PJ_MW = 64;         // query rows per workgroup for large M (4 tiles of 16)
+
+// Query rows per workgroup.  A workgroup's rows past the first 16 are handled
+// one tile after another, each tile's loads a memory round trip of its own;
+// up to 256 rows (decode batches) every workgroup takes a single tile, and the
+// weight slice is read once per tile (from L2 after the first).
+__host__ __device__ inline int pj_rows_per_wg(int M) { return M <= 256 ? 16 : PJ_MW; }
 constexpr int AB_CT = 128;        // latent columns per absorb workgroup (32 per wave)
 constexpr int AB_KS = 6;          // at most 6 k-steps of 32: d_nope <= 192 (55 KiB staged)
 constexpr int AB_LD = 2 * AB_CT + 32;  // LDS row stride (bytes) of the staged weight
@@ -150,10 +156,11 @@ constexpr int OP_KS = 16;         // at most 16 k-steps of 32: d_c <= 512
 // append of a decode step rides along with the absorb: one launch less).
 // They come first in dispatch order so that their chain of dependent loads
 // (length, page id, row) runs under the absorb rather than after it.
+template <int NKS>  // k-steps of 32 covering d_nope: ceil(d_nope / 32)
 __global__ __launch_bounds__(PJ_NT) void absorb_q_mfma_kernel(
     const uint16_t* __restrict__ q_nope, const uint16_t* __restrict__ q_rope,
     const uint16_t* __restrict__ w_uk, uint16_t* __restrict__ q_abs, int M, int H, int d_n,
-    int d_c, int d_r, const AppendArgs ap) {
+    int d_c, int d_r, int mt, const AppendArgs ap) {
   extern __shared__ __align__(16) uint8_t wl[];  // [KP][AB_LD]
   const int apx = (ap.rows + PJ_NT / 64 - 1) / (PJ_NT / 64);  // append workgroups along x
   if ((int)blockIdx.x < apx) {
@@ -176,10 +183,10 @@ __global__ __launch_bounds__(PJ_NT) void absorb_q_mfma_kernel(
     return;
   }
   const int h = (int)blockIdx.x - apx, cb = blockIdx.y;
-  const int mbeg = blockIdx.z * PJ_MW, mend = min(M, mbeg + PJ_MW);
+  const int mbeg = blockIdx.z * mt, mend = min(M, mbeg + mt);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int i16 = lane & 15, g = lane >> 4;
-  const int nks = (d_n + 31) >> 5;
+  constexpr int nks = NKS;
   const int W = d_c + d_r;
 
   // B fragments (query rows) of the first tile are requested before the
@@ -192,32 +199,29 @@ __global__ __launch_bounds__(PJ_NT) void absorb_q_mfma_kernel(
   auto load_q = [&](int m0, bf16x8* bq) {
     const uint16_t* qrow = q_nope + ((size_t)min(m0 + i16, mend - 1) * H + h) * d_n;
 #pragma unroll
-    for (int ks = 0; ks < AB_KS; ++ks) bq[ks] = load_bf16x8(qrow + min(32 * ks + 8 * g, d_n - 8));
+    for (int ks = 0; ks < nks; ++ks) bq[ks] = load_bf16x8(qrow + min(32 * ks + 8 * g, d_n - 8));
   };
   bf16x8 bq[AB_KS];
   load_q(mbeg, bq);
 
-  // the weight slice: every piece is loaded (clamped, unconditional) before
-  // the first is stored, so staging costs one memory latency
+  // the weight slice: every piece is loaded (unconditional) before the first
+  // is stored, so staging costs one memory latency; nks * 32 rows of 16
+  // pieces make exactly 2 * nks pieces per thread
   const uint16_t* wsrc = w_uk + (size_t)h * d_n * d_c + cb * AB_CT;
-  constexpr int ST = AB_KS * 32 * (AB_CT / 8) / PJ_NT;  // pieces per thread, at most
-  const int pieces = nks * 32 * (AB_CT / 8);
+  constexpr int ST = nks * 32 * (AB_CT / 8) / PJ_NT;
+  static_assert(ST * PJ_NT == nks * 32 * (AB_CT / 8), "whole passes");
   u32x4 sv[ST];
 #pragma unroll
   for (int u = 0; u < ST; ++u) {
-    // clamped like the stores below, so that a thread past the last piece
-    // loads (and rewrites) exactly that piece
-    const int i = min(tid + u * PJ_NT, pieces - 1);
+    const int i = tid + u * PJ_NT;
     const int d = i / (AB_CT / 8), ch = i % (AB_CT / 8);
     sv[u] = *reinterpret_cast<const u32x4*>(wsrc + (size_t)min(d, d_n - 1) * d_c + ch * 8);
   }
   // every load is issued before the first is used
   __builtin_amdgcn_sched_barrier(0);
-  // branch-free (a branch would make the compiler wait for every load): a
-  // clamped index rewrites the last piece with the same value
 #pragma unroll
   for (int u = 0; u < ST; ++u) {
-    const int i = min(tid + u * PJ_NT, pieces - 1);
+    const int i = tid + u * PJ_NT;
     const int d = i / (AB_CT / 8), ch = i % (AB_CT / 8);
     const u32x4 z = {0u, 0u, 0u, 0u};
     *reinterpret_cast<u32x4*>(wl + d * AB_LD + ch * 16) = d < d_n ? sv[u] : z;
@@ -240,23 +244,27 @@ __global__ __launch_bounds__(PJ_NT) void absorb_q_mfma_kernel(
     }
 
   const int col0 = cb * AB_CT + 32 * wave + 4 * g;  // + 16 ct: this lane's 4 columns
-  for (int m0 = mbeg; m0 < mend; m0 += 16) {
+  // one 16-row tile whose query fragments are in bq
+  auto tile = [&](int m0) __attribute__((always_inline)) {
     const int m = m0 + i16;
-    const bool mok = m < mend;
     f32x4 acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
-    for (int ks = 0; ks < AB_KS; ++ks) {
-      if (ks < nks) {
-        acc[0] = mfma16(a[0][ks], bq[ks], acc[0]);
-        acc[1] = mfma16(a[1][ks], bq[ks], acc[1]);
-      }
+    for (int ks = 0; ks < nks; ++ks) {
+      acc[0] = mfma16(a[0][ks], bq[ks], acc[0]);
+      acc[1] = mfma16(a[1][ks], bq[ks], acc[1]);
     }
-    if (m0 + 16 < mend) load_q(m0 + 16, bq);
-    if (mok) {
+    if (m < mend) {
       uint16_t* dst = q_abs + ((size_t)m * H + h) * W + col0;
       store_bf16x4(dst, acc[0]);
       store_bf16x4(dst + 16, acc[1]);
     }
+  };
+  // the first tile as straight-line code: in a loop, the compiler moves its
+  // query loads down to their use, behind the staging and its barrier
+  tile(mbeg);
+  for (int m0 = mbeg + 16; m0 < mend; m0 += 16) {
+    load_q(m0, bq);
+    tile(m0);
   }
 
   if (cb == 0) {  // the rotary part is carried over unchanged, 16 bytes at a time
@@ -281,10 +289,10 @@ constexpr int OP_LD = 2 * 32 * OP_KS + 16;  // bytes per staged row (d_c <= 512)
 
 __global__ __launch_bounds__(PJ_NT) void out_proj_mfma_kernel(
     const float* __restrict__ o_lat, const uint16_t* __restrict__ w_uv,
-    uint16_t* __restrict__ out, int M, int H, int d_c, int d_v) {
+    uint16_t* __restrict__ out, int M, int H, int d_c, int d_v, int mt) {
   __shared__ __align__(16) uint8_t st[2][16 * OP_LD];  // hi, lo
   const int h = blockIdx.x, vb = blockIdx.y;
-  const int mbeg = blockIdx.z * PJ_MW, mend = min(M, mbeg + PJ_MW);
+  const int mbeg = blockIdx.z * mt, mend = min(M, mbeg + mt);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int i16 = lane & 15, g = lane >> 4;
   const int nks = d_c >> 5;
@@ -375,6 +383,27 @@ __global__ __launch_bounds__(PJ_NT) void out_proj_mfma_kernel(
   }
 }
 
+// absorb_q_mfma_kernel for ceil(d_n / 32) k-steps (1 .. AB_KS)
+hipError_t launch_absorb_kernel(dim3 grid, size_t shmem, hipStream_t stream,
+                                const uint16_t* q_nope, const uint16_t* q_rope,
+                                const uint16_t* w_uk, uint16_t* q_abs, int M, int H, int d_n,
+                                int d_c, int d_r, int mt, const AppendArgs& ap) {
+#define AB_LAUNCH(K)                                                                     \
+  hipLaunchKernelGGL(absorb_q_mfma_kernel<K>, grid, dim3(PJ_NT), shmem, stream, q_nope, \
+                     q_rope, w_uk, q_abs, M, H, d_n, d_c, d_r, mt, ap)
+  switch ((d_n + 31) >> 5) {
+    case 1: AB_LAUNCH(1); break;
+    case 2: AB_LAUNCH(2); break;
+    case 3: AB_LAUNCH(3); break;
+    case 4: AB_LAUNCH(4); break;
+    case 5: AB_LAUNCH(5); break;
+    case 6: AB_LAUNCH(6); break;
+    default: return hipErrorInvalidValue;
+  }
+#undef AB_LAUNCH
+  return hipGetLastError();
+}
+
 bool absorb_mfma_fits(int d_n, int d_c, int d_r) {
   return d_c % AB_CT == 0 && d_n % 8 == 0 && d_n > 0 && d_n <= 32 * AB_KS && d_r % 8 == 0;
 }
@@ -390,12 +419,12 @@ hipError_t launch_absorb_q(int dtype, const void* q_nope, const void* q_rope, co
                            hipStream_t stream) {
   if (M <= 0) return hipSuccess;
   if (dtype == 1 && absorb_mfma_fits(d_n, d_c, d_r)) {
-    const dim3 grid(H, d_c / AB_CT, (M + PJ_MW - 1) / PJ_MW);
+    const int mt = pj_rows_per_wg(M);
+    const dim3 grid(H, d_c / AB_CT, (M + mt - 1) / mt);
     const size_t shmem = (size_t)((d_n + 31) & ~31) * AB_LD;
-    hipLaunchKernelGGL(absorb_q_mfma_kernel, grid, dim3(PJ_NT), shmem, stream,
-                       (const uint16_t*)q_nope, (const uint16_t*)q_rope, (const uint16_t*)w_uk,
-                       (uint16_t*)q_abs, M, H, d_n, d_c, d_r, AppendArgs{});
-    return hipGetLastError();
+    return launch_absorb_kernel(grid, shmem, stream, (const uint16_t*)q_nope,
+                                (const uint16_t*)q_rope, (const uint16_t*)w_uk, (uint16_t*)q_abs,
+                                M, H, d_n, d_c, d_r, mt, AppendArgs{});
   }
   const dim3 grid(H, (d_c + ABS_NT - 1) / ABS_NT, (M + ABS_MT - 1) / ABS_MT);
   const size_t shmem = (size_t)ABS_MT * d_n * sizeof(float);
@@ -414,9 +443,10 @@ hipError_t launch_out_proj(int dtype, const float* o_lat, const void* w_uv, void
                            int H, int d_c, int d_v, hipStream_t stream) {
   if (M <= 0) return hipSuccess;
   if (dtype == 1 && out_proj_mfma_fits(d_c, d_v)) {
-    const dim3 grid(H, (d_v + OP_VT - 1) / OP_VT, (M + PJ_MW - 1) / PJ_MW);
+    const int mt = pj_rows_per_wg(M);
+    const dim3 grid(H, (d_v + OP_VT - 1) / OP_VT, (M + mt - 1) / mt);
     hipLaunchKernelGGL(out_proj_mfma_kernel, grid, dim3(PJ_NT), 0, stream, o_lat,
-                       (const uint16_t*)w_uv, (uint16_t*)out, M, H, d_c, d_v);
+                       (const uint16_t*)w_uv, (uint16_t*)out, M, H, d_c, d_v, mt);
     return hipGetLastError();
   }
   const dim3 grid(H, (d_v + OP_T - 1) / OP_T, (M + OP_T - 1) / OP_T);
@@ -435,12 +465,12 @@ hipError_t launch_absorb_q_append(int dtype, const void* q_nope, const void* q_r
   const long long extra = ((long long)ap.rows + PJ_NT / 64 - 1) / (PJ_NT / 64);
   if (M > 0 && ap.rows > 0 && dtype == 1 && absorb_mfma_fits(d_n, d_c, d_r) &&
       ap.row_bytes % 16 == 0 && (long long)H + extra <= 0x7fffffffLL) {
-    const dim3 grid((unsigned)(H + extra), d_c / AB_CT, (M + PJ_MW - 1) / PJ_MW);
+    const int mt = pj_rows_per_wg(M);
+    const dim3 grid((unsigned)(H + extra), d_c / AB_CT, (M + mt - 1) / mt);
     const size_t shmem = (size_t)((d_n + 31) & ~31) * AB_LD;
-    hipLaunchKernelGGL(absorb_q_mfma_kernel, grid, dim3(PJ_NT), shmem, stream,
-                       (const uint16_t*)q_nope, (const uint16_t*)q_rope, (const uint16_t*)w_uk,
-                       (uint16_t*)q_abs, M, H, d_n, d_c, d_r, ap);
-    return hipGetLastError();
+    return launch_absorb_kernel(grid, shmem, stream, (const uint16_t*)q_nope,
+                                (const uint16_t*)q_rope, (const uint16_t*)w_uk, (uint16_t*)q_abs,
+                                M, H, d_n, d_c, d_r, mt, ap);
   }
   hipError_t e = launch_absorb_q(dtype, q_nope, q_rope, w_uk, q_abs, M, H, d_n, d_c, d_r, stream);
   if (e != hipSuccess || ap.rows <= 0) return e;
