@@ -104,8 +104,13 @@ __global__ __launch_bounds__(256, 2) void wo_gemm_mfma_kernel(
   for (int j = 0; j < 4; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   // A chunk: 64 rows x up to 256 k of both operands in 16-byte pieces, 32 per
-  // row (a wave covers two rows, 1 KB contiguous per operand).  Rows past M
-  // or N and k past the split are zero.
+  // row (a wave covers two rows, 1 KB contiguous per operand); the next
+  // chunk's loads are issued before this chunk's MFMAs.  Every load is
+  // unconditional (a conditional load makes the compiler wait for all loads
+  // in flight): rows past M or N are read clamped and feed outputs that are
+  // not stored, and weight pieces past the split are read from a block of
+  // zeros (their token pieces, clamped, are finite).  A second chunk in
+  // flight was measured slower.
   uint4 vx[WO_PER], vw[WO_PER];
   auto load_chunk = [&](int sc) {
     const int steps = min(WO_KC / 32, s_end - sc);
@@ -115,16 +120,15 @@ __global__ __launch_bounds__(256, 2) void wo_gemm_mfma_kernel(
       const int q = tid + 256 * u;
       const int r = q / WO_PIECES, c = q % WO_PIECES;
       const bool kin = c < steps * 4;
-      const int m = m0 + r, n = n0 + r;
-      vx[u] = uint4{0u, 0u, 0u, 0u};
-      vw[u] = uint4{0u, 0u, 0u, 0u};
-      if (kin && m < M) vx[u] = load_piece(x + (size_t)m * K + k0 + 8 * c);
-      if (kin && n < N) vw[u] = load_piece(w + (size_t)n * K + k0 + 8 * c);
+      const int kk = k0 + 8 * c;
+      vx[u] = load_piece(x + (size_t)min(m0 + r, M - 1) * K + min(kk, K - 8));
+      vw[u] = load_piece(kin ? w + (size_t)min(n0 + r, N - 1) * K + kk
+                             : reinterpret_cast<const uint16_t*>(kZero16));
     }
   };
-  if (s_begin < s_end) load_chunk(s_begin);
   const int l16 = lane & 15;
   const int kq = 8 * (lane >> 4);
+  load_chunk(s_begin);
   for (int sc = s_begin; sc < s_end; sc += WO_KC / 32) {
     const int steps = min(WO_KC / 32, s_end - sc);
 #pragma unroll
@@ -135,7 +139,7 @@ __global__ __launch_bounds__(256, 2) void wo_gemm_mfma_kernel(
       *reinterpret_cast<uint4*>(&sw[r * WO_LD + 8 * c]) = vw[u];
     }
     __syncthreads();
-    if (sc + WO_KC / 32 < s_end) load_chunk(sc + WO_KC / 32);
+    load_chunk(sc + WO_KC / 32);   // past the split: zero weight pieces, never used
     // wave w: weight rows 16w + (l & 15) (A), tokens 16j + (l & 15) (B), k
     // 32s + 8(l >> 4) .. +7
     for (int s = 0; s < steps; ++s) {
