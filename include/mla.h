@@ -8,7 +8,7 @@
  *                     softmax, and sum the cached latents (split-KV + merge)
  *   mla_out_proj      up-project the latent output once per head through W^UV
  *
- * and, on the input side, mla_kv_produce (the cached row made from the token's
+ * (mla_absorb_q_append issues the first two as one launch), and, on the input side, mla_kv_produce (the cached row made from the token's
  * hidden vector, with RoPE on k^R, written into the cache in place of
  * mla_cache_append) and mla_rope (the same rotation for the query's rotary part);
  * on the output side, mla_o_proj (the output projection W^O over the heads) and
