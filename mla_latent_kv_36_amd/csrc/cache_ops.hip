@@ -66,6 +66,7 @@ __global__ __launch_bounds__(256) void validate_kernel(const int32_t* __restrict
                                                       int block_size, int num_blocks,
                                                       int32_t* flag) {
   const int b = blockIdx.y;
+  if (b >= B) return;
   const int n = seq_lens[b];
   const long long need = n > 0 ? ((long long)n + block_size - 1) / block_size : 0;
   if (need > max_blocks && blockIdx.x == 0 && threadIdx.x == 0) atomicOr(flag, 2);
