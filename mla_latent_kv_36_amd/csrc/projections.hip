@@ -135,10 +135,13 @@ constexpr int PJ_NT = 256;        // 4 waves
 constexpr int PJ_MW = 64;         // query rows per workgroup for large M (4 tiles of 16)
 
 // Query rows per workgroup.  A workgroup's rows past the first 16 are handled
-// one tile after another, each tile's loads a memory round trip of its own;
-// up to 256 rows (decode batches) every workgroup takes a single tile, and the
-// weight slice is read once per tile (from L2 after the first).
-__host__ __device__ inline int pj_rows_per_wg(int M) { return M <= 256 ? 16 : PJ_MW; }
+// one tile after another, each tile's loads a memory round trip of its own,
+// while the weight slice is read once per workgroup (more workgroups read it
+// again, from L2).  Measured at 128 query rows: two tiles per workgroup beat
+// one by ~1 us; up to 64 rows every workgroup takes a single tile.
+__host__ __device__ inline int pj_rows_per_wg(int M) {
+  return M <= 64 ? 16 : M <= 256 ? 32 : PJ_MW;
+}
 constexpr int AB_CT = 128;        // latent columns per absorb workgroup (32 per wave)
 constexpr int AB_KS = 6;          // at most 6 k-steps of 32: d_nope <= 192 (55 KiB staged)
 constexpr int AB_LD = 2 * AB_CT + 32;  // LDS row stride (bytes) of the staged weight
