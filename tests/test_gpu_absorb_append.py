@@ -86,3 +86,33 @@ def test_fused_skips_rows_outside_the_table():
         pools.append(dev_bits(pool))
     assert np.array_equal(pools[0], pools[1])
     assert not np.array_equal(pools[0], dev_bits(dev["pool"]))   # the other rows were written
+
+
+@pytest.mark.parametrize("M", [70, 200])
+def test_projections_two_tiles_per_workgroup(M):
+    """65 .. 256 query rows: each workgroup of mla_absorb_q and mla_out_proj
+    takes two 16-row tiles (the second ragged or absent in the last
+    workgroup).  Against the fp64 oracle: q_abs within bf16 rounding of each
+    element plus an fp32-accumulation floor, out within 2e-2 of max|out|."""
+    import oracle
+    from workloads import V2_MULTI
+    from workloads.device import to_dev
+    w = V2_MULTI.scaled(B=M, T=1, N=64)
+    bt = make_inputs(w)
+    cfg = cfg_of(w)
+    note(f"projections with {M} query rows")
+    qn = to_dev(bt.q_nope.reshape(M, w.H, -1), torch.bfloat16, "cuda")
+    qr = to_dev(bt.q_rope.reshape(M, w.H, -1), torch.bfloat16, "cuda")
+    q_abs = torch.empty((M, w.H, w.d_c + w.d_r), dtype=torch.bfloat16, device="cuda")
+    mla.mla_absorb_q(cfg, qn, qr, to_dev(bt.w_uk, torch.bfloat16, "cuda"), q_abs)
+    o_lat = np.random.default_rng(5).standard_normal((M, w.H, w.d_c)).astype(np.float32)
+    out = torch.empty((M, w.H, w.d_v), dtype=torch.bfloat16, device="cuda")
+    mla.mla_out_proj(cfg, torch.from_numpy(o_lat).cuda(), to_dev(bt.w_uv, torch.bfloat16, "cuda"), out)
+    torch.cuda.synchronize()
+    want = oracle.absorb_q_ref(bt.q_nope.reshape(M, w.H, -1), bt.q_rope.reshape(M, w.H, -1), bt.w_uk)
+    got = q_abs.float().cpu().numpy()
+    bound = 2.0 ** -8 * np.abs(want) + 1e-4 * np.max(np.abs(want))
+    assert np.all(np.abs(got - want) <= bound)
+    want_o = oracle.out_proj_ref(o_lat, bt.w_uv)
+    got_o = out.float().cpu().numpy()
+    assert np.max(np.abs(got_o - want_o)) <= 2e-2 * np.max(np.abs(want_o))
