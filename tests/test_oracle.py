@@ -371,8 +371,72 @@ def rope_angle_pin(rope) -> bool:
     return bool(np.allclose(y, want, rtol=0, atol=1e-12))
 
 
+def _producer_weights(rng, d, d_c, d_r):
+    return rng.standard_normal((d_c, d)), rng.standard_normal((d_r, d))
+
+
+def producer_chunking_pin(produce_append) -> bool:
+    """A sequence's cache cannot depend on how its tokens were cut into decode
+    steps: producing tokens 0..N-1 in one call must fill the same slots with
+    the same rows as producing them over steps of 3, 1, 5 and 2 tokens, each
+    step starting where the previous one stopped.  Two sequences with
+    different starting lengths and a permuted block table, so positions,
+    pages and slots all differ between the sequences."""
+    rng = np.random.default_rng(24)
+    d, d_c, d_r, bs = 10, 6, 8, 4
+    w_dkv, w_kr = _producer_weights(rng, d, d_c, d_r)
+    start = np.array([0, 5])
+    N = 11
+    hidden = rng.standard_normal((2, N, d))
+    table = np.array([[2, 0, 7, 1], [5, 3, 6, 4]])
+    pool0 = np.full((8, bs, d_c + d_r), np.nan)
+    whole = produce_append(pool0, table, start, hidden, w_dkv, w_kr, bs)
+    pool, done = pool0, 0
+    for T in (3, 1, 5, 2):
+        pool = produce_append(pool, table, start + done, hidden[:, done:done + T], w_dkv, w_kr, bs)
+        done += T
+    same_slots = np.array_equal(np.isnan(whole), np.isnan(pool))
+    filled = ~np.isnan(whole)
+    return bool(same_slots and np.allclose(whole[filled], pool[filled], rtol=1e-13, atol=1e-13))
+
+
+def producer_self_score_pin(produce_append) -> bool:
+    """RoPE scores depend only on the distance between positions ("Attention,
+    Part 2", section "Why position needs its own key"): a token's produced
+    rotary key, scored against any query rotated to that token's own position,
+    equals the unrotated product q . (W^KR h).  The produced token i of
+    sequence b must therefore sit at position seq_lens_before[b] + i; the
+    lengths before the step are nonzero, so step-local positions 0..T-1 would
+    leave a distance of seq_lens_before[b]."""
+    rng = np.random.default_rng(25)
+    d, d_c, d_r, bs, T = 9, 4, 6, 8, 3
+    w_dkv, w_kr = _producer_weights(rng, d, d_c, d_r)
+    start = np.array([5, 37])
+    hidden = rng.standard_normal((2, T, d))
+    table = np.array([[3, 0, 4, 1, 6, 2], [7, 9, 8, 10, 5, 11]])
+    pool = produce_append(np.zeros((12, bs, d_c + d_r)), table, start, hidden, w_dkv, w_kr, bs)
+    q = rng.standard_normal(d_r)
+    for b in range(2):
+        for i in range(T):
+            pos = int(start[b]) + i
+            k_rot = pool[table[b, pos // bs], pos % bs, d_c:]
+            q_rot = oracle.rope_ref(q[None], np.array([pos]))[0]
+            want = q @ (w_kr @ hidden[b, i])
+            if not math.isclose(q_rot @ k_rot, want, rel_tol=1e-11, abs_tol=1e-11):
+                return False
+    return True
+
+
 def test_producer_one_hot_reads_weight_columns():
     assert producer_one_hot_pin(oracle.kv_produce_ref)
+
+
+def test_produced_rows_do_not_depend_on_step_chunking():
+    assert producer_chunking_pin(oracle.produce_append_ref)
+
+
+def test_produced_rotary_key_sits_at_its_absolute_position():
+    assert producer_self_score_pin(oracle.produce_append_ref)
 
 
 def test_producer_latent_is_never_rotated():

@@ -153,6 +153,33 @@ def test_producer_pins_reject_planted_bug(bug):
                 and rope_angle_pin(rope))
 
 
+def _produce_append_variant(bug):
+    """produce_append_ref with one planted mistake: "step_local_positions"
+    rotates token i of every step at position i instead of
+    seq_lens_before[b] + i."""
+    def produce_append(pool, block_table, seq_lens_before, hidden, w_dkv, w_kr, block_size):
+        B, T, _ = hidden.shape
+        rows = []
+        for b in range(B):
+            first = 0 if bug == "step_local_positions" else int(seq_lens_before[b])
+            rows.append(oracle.kv_produce_ref(hidden[b], w_dkv, w_kr, first + np.arange(T)))
+        return oracle.append_ref(pool, block_table, seq_lens_before, np.stack(rows), block_size)
+    return produce_append
+
+
+def test_producer_append_pins_reject_step_local_positions():
+    from test_oracle import producer_chunking_pin, producer_self_score_pin
+    bad = _produce_append_variant("step_local_positions")
+    assert not producer_chunking_pin(bad)
+    assert not producer_self_score_pin(bad)
+
+
+def test_producer_append_pins_accept_the_unmutated_variant():
+    from test_oracle import producer_chunking_pin, producer_self_score_pin
+    good = _produce_append_variant("none")
+    assert producer_chunking_pin(good) and producer_self_score_pin(good)
+
+
 def test_producer_pins_accept_the_unmutated_variant():
     from test_oracle import producer_one_hot_pin, producer_position_pin, rope_angle_pin
     produce = _produce_variant("none")
