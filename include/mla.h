@@ -25,6 +25,8 @@
  *  - Pointers named as device buffers are device (HBM) addresses; the caller owns
  *    every buffer.  The library never allocates, frees, or keeps a pointer after
  *    a call returns, and holds no global mutable state: calls are thread-safe.
+ *    The one exception is mla_decode_noalloc, which keeps its split partials
+ *    in a scratch array of its own on each GPU (see there).
  *  - `stream` is a hipStream_t passed as void* (NULL = the default stream).  Calls
  *    only enqueue work on it: MLA_OK means "validated and launched", not "done".
  *  - All arguments are checked on the host before anything is launched; a call
@@ -196,6 +198,34 @@ mla_status mla_decode(const mla_config* cfg, const void* q_abs, const void* pool
                       int32_t T, int32_t causal, int32_t num_splits,
                       int64_t total_tokens_host, void* workspace, size_t workspace_bytes,
                       float* o_lat, float* lse, void* stream);
+
+/*
+ * mla_decode_noalloc -- mla_decode for callers that cannot allocate device
+ * memory: code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc.  Same arguments and results as mla_decode, minus the
+ * workspace: the split partials go to a scratch array that the library owns,
+ * mla_decode_noalloc_scratch_bytes() bytes (64 MiB) on each GPU it runs on,
+ * reserved with the library's code on that GPU and held until the process
+ * ends.  The call itself allocates and frees nothing.
+ *  - num_splits = 0: the library's split choice, cut down to the most splits
+ *    whose partials fit the scratch array (one split needs none), so the
+ *    results can differ from mla_decode's in rounding only.
+ *  - num_splits > 0 whose partials do not fit: MLA_ERR_WORKSPACE, nothing
+ *    launched.
+ *  - MLA_ERR_HIP if the scratch array's device address cannot be looked up
+ *    (done once per GPU, on the first call that needs it, for the device of
+ *    `stream`).
+ * Every call on one GPU uses the same array, which keeps the last call's
+ * contents: calls that overlap in time on one GPU (other streams, other host
+ * threads) race and give wrong results.  Calls ordered on one stream are safe.
+ */
+mla_status mla_decode_noalloc(const mla_config* cfg, const void* q_abs, const void* pool,
+                              int32_t num_blocks, const int32_t* block_table,
+                              int32_t max_blocks, const int32_t* seq_lens,
+                              int32_t max_seq_len_host, int32_t B, int32_t T, int32_t causal,
+                              int32_t num_splits, int64_t total_tokens_host, float* o_lat,
+                              float* lse, void* stream);
+size_t mla_decode_noalloc_scratch_bytes(void);
 
 /*
  * mla_out_proj -- output-side up-projection, applied once per head after the

@@ -4,6 +4,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "launch.h"
 #include "mla.h"
 
@@ -116,6 +118,52 @@ size_t partial_bytes(const mla_config* c, int B, int T, const Plan& pl, size_t* 
 }
 
 mla_status hip_status(hipError_t e) { return e == hipSuccess ? MLA_OK : MLA_ERR_HIP; }
+
+// Scratch memory of mla_decode_noalloc: the split partials of one call, in a
+// device array that the library owns (one copy per GPU, held until the
+// process ends).  `scratch` names the array only in device code; the host
+// uses its device address, looked up once per device with hipGetSymbolAddress
+// while that device is current.  Calls on one GPU share the array, so calls
+// that overlap in time on one GPU (different streams, or different host
+// threads) race on it.  Nothing in it has to start at zero: the partial rows
+// and the balanced plan's table are written before they are read in every
+// call.
+constexpr size_t kScratchBytes = (size_t)64 << 20;
+constexpr int kMaxDevices = 64;
+__device__ __align__(256) uint8_t scratch[kScratchBytes];
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];
+
+// The device address of `scratch` on the device of stream s (the current
+// device for the null stream).
+hipError_t scratch_address(hipStream_t s, void** out) {
+  int cur = 0;
+  hipError_t e = hipGetDevice(&cur);
+  if (e != hipSuccess) return e;
+  int dev = cur;
+  if (s != nullptr) {
+    hipDevice_t d = 0;
+    e = hipStreamGetDevice(s, &d);
+    if (e != hipSuccess) return e;
+    dev = (int)d;
+  }
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    if (dev != cur && (e = hipSetDevice(dev)) != hipSuccess) return e;
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (dev != cur) {
+      const hipError_t r = hipSetDevice(cur);
+      if (e == hipSuccess) e = r;
+    }
+    if (e != hipSuccess) return e;
+    if (ptr == nullptr) return hipErrorInvalidSymbol;
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return hipSuccess;
+}
 
 }  // namespace
 
@@ -249,12 +297,15 @@ size_t mla_decode_workspace_size(const mla_config* cfg, int32_t B, int32_t T,
   return partial_bytes(cfg, B, T, pl, nullptr, nullptr);
 }
 
-mla_status mla_decode(const mla_config* cfg, const void* q_abs, const void* pool,
-                      int32_t num_blocks, const int32_t* block_table, int32_t max_blocks,
-                      const int32_t* seq_lens, int32_t max_seq_len_host, int32_t B,
-                      int32_t T, int32_t causal, int32_t num_splits,
-                      int64_t total_tokens_host, void* workspace, size_t workspace_bytes,
-                      float* o_lat, float* lse, void* stream) {
+// Host checks of mla_decode's arguments (everything but the workspace);
+// *work = false when there is nothing to launch (B == 0).
+static mla_status check_decode(const mla_config* cfg, const void* q_abs, const void* pool,
+                               int32_t num_blocks, const int32_t* block_table,
+                               int32_t max_blocks, const int32_t* seq_lens,
+                               int32_t max_seq_len_host, int32_t B, int32_t T, int32_t causal,
+                               int32_t num_splits, const float* o_lat, const float* lse,
+                               bool* work) {
+  *work = false;
   mla_status st = check_cfg(cfg);
   if (st != MLA_OK) return st;
   if (B < 0 || T < 1 || num_blocks <= 0 || max_blocks <= 0 || max_seq_len_host < 0 ||
@@ -267,15 +318,24 @@ mla_status mla_decode(const mla_config* cfg, const void* q_abs, const void* pool
       o_lat == nullptr)
     return MLA_ERR_NULL;
   if (!aligned16(q_abs) || !aligned16(pool) || !aligned16(o_lat) || !aligned16(block_table) ||
-      !aligned16(seq_lens) || (lse != nullptr && !aligned16(lse)) ||
-      (workspace != nullptr && !aligned16(workspace)))
+      !aligned16(seq_lens) || (lse != nullptr && !aligned16(lse)))
     return MLA_ERR_ALIGN;
+  *work = true;
+  return MLA_OK;
+}
 
-  const Plan pl = make_plan(cfg, B, T, max_seq_len_host, total_tokens_host, num_splits);
+// Launches a checked decode under plan pl with its partials in `workspace`
+// (at least partial_bytes(pl) bytes when pl needs a merge).
+static mla_status launch_decode_plan(const mla_config* cfg, const Plan& pl, const void* q_abs,
+                                     const void* pool, int32_t num_blocks,
+                                     const int32_t* block_table, int32_t max_blocks,
+                                     const int32_t* seq_lens, int32_t max_seq_len_host,
+                                     int32_t B, int32_t T, int32_t causal, void* workspace,
+                                     float* o_lat, float* lse, hipStream_t s) {
   size_t lse_off = 0;
   size_t plan_off = 0;
-  const size_t need = pl.splits > 1 ? partial_bytes(cfg, B, T, pl, &lse_off, &plan_off) : 0;
-  if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return MLA_ERR_WORKSPACE;
+  const bool merge = pl.splits > 1;
+  if (merge) partial_bytes(cfg, B, T, pl, &lse_off, &plan_off);
 
   mla::DecodeParams p{};
   p.q_abs = q_abs;
@@ -284,9 +344,9 @@ mla_status mla_decode(const mla_config* cfg, const void* q_abs, const void* pool
   p.seq_lens = seq_lens;
   p.o_lat = o_lat;
   p.lse = lse;
-  p.part_o = need > 0 ? static_cast<float*>(workspace) : nullptr;
-  p.part_lse = need > 0 ? reinterpret_cast<float*>(static_cast<char*>(workspace) + lse_off)
-                        : nullptr;
+  p.part_o = merge ? static_cast<float*>(workspace) : nullptr;
+  p.part_lse = merge ? reinterpret_cast<float*>(static_cast<char*>(workspace) + lse_off)
+                     : nullptr;
   p.B = B;
   p.T = T;
   p.H = cfg->n_heads;
@@ -303,15 +363,66 @@ mla_status mla_decode(const mla_config* cfg, const void* q_abs, const void* pool
   p.plan = pl.balanced ? reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + plan_off)
                        : nullptr;
 
-  hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e = use_mfma(cfg, T) ? mla::launch_decode_mfma(p, s)
                                   : mla::launch_decode_generic(p, cfg->dtype, s);
   if (e != hipSuccess) return MLA_ERR_HIP;
-  if (pl.splits > 1) {
+  if (merge) {
     e = mla::launch_combine(p, s);
     if (e != hipSuccess) return MLA_ERR_HIP;
   }
   return MLA_OK;
+}
+
+mla_status mla_decode(const mla_config* cfg, const void* q_abs, const void* pool,
+                      int32_t num_blocks, const int32_t* block_table, int32_t max_blocks,
+                      const int32_t* seq_lens, int32_t max_seq_len_host, int32_t B,
+                      int32_t T, int32_t causal, int32_t num_splits,
+                      int64_t total_tokens_host, void* workspace, size_t workspace_bytes,
+                      float* o_lat, float* lse, void* stream) {
+  bool work;
+  mla_status st = check_decode(cfg, q_abs, pool, num_blocks, block_table, max_blocks, seq_lens,
+                               max_seq_len_host, B, T, causal, num_splits, o_lat, lse, &work);
+  if (st != MLA_OK || !work) return st;
+  if (workspace != nullptr && !aligned16(workspace)) return MLA_ERR_ALIGN;
+  const Plan pl = make_plan(cfg, B, T, max_seq_len_host, total_tokens_host, num_splits);
+  const size_t need = pl.splits > 1 ? partial_bytes(cfg, B, T, pl, nullptr, nullptr) : 0;
+  if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return MLA_ERR_WORKSPACE;
+  return launch_decode_plan(cfg, pl, q_abs, pool, num_blocks, block_table, max_blocks, seq_lens,
+                            max_seq_len_host, B, T, causal, workspace, o_lat, lse,
+                            static_cast<hipStream_t>(stream));
+}
+
+size_t mla_decode_noalloc_scratch_bytes(void) { return kScratchBytes; }
+
+mla_status mla_decode_noalloc(const mla_config* cfg, const void* q_abs, const void* pool,
+                              int32_t num_blocks, const int32_t* block_table,
+                              int32_t max_blocks, const int32_t* seq_lens,
+                              int32_t max_seq_len_host, int32_t B, int32_t T, int32_t causal,
+                              int32_t num_splits, int64_t total_tokens_host, float* o_lat,
+                              float* lse, void* stream) {
+  bool work;
+  mla_status st = check_decode(cfg, q_abs, pool, num_blocks, block_table, max_blocks, seq_lens,
+                               max_seq_len_host, B, T, causal, num_splits, o_lat, lse, &work);
+  if (st != MLA_OK || !work) return st;
+  Plan pl = make_plan(cfg, B, T, max_seq_len_host, total_tokens_host, num_splits);
+  if (pl.splits > 1 && partial_bytes(cfg, B, T, pl, nullptr, nullptr) > kScratchBytes) {
+    // an explicit split count must fit as asked; the library's choice is cut
+    // to the most splits whose partials fit (one split needs none)
+    if (num_splits > 0) return MLA_ERR_WORKSPACE;
+    const size_t per_split =
+        (size_t)B * T * cfg->n_heads * ((size_t)cfg->d_c + 1) * sizeof(float) + 512;
+    int fit = (int)(kScratchBytes / per_split);
+    if (fit > pl.splits) fit = pl.splits;
+    for (;; --fit) {
+      pl = make_plan(cfg, B, T, max_seq_len_host, total_tokens_host, fit < 1 ? 1 : fit);
+      if (pl.splits <= 1 || partial_bytes(cfg, B, T, pl, nullptr, nullptr) <= kScratchBytes) break;
+    }
+  }
+  void* ws = nullptr;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (pl.splits > 1 && scratch_address(s, &ws) != hipSuccess) return MLA_ERR_HIP;
+  return launch_decode_plan(cfg, pl, q_abs, pool, num_blocks, block_table, max_blocks, seq_lens,
+                            max_seq_len_host, B, T, causal, ws, o_lat, lse, s);
 }
 
 mla_status mla_out_proj(const mla_config* cfg, const float* o_lat, const void* w_uv, void* out,

@@ -88,6 +88,31 @@ def test_decode_validation(lib):
     assert _decode(lib, cfg, B=0) == OK
 
 
+def _decode_noalloc(lib, cfg, q=FAKE, pool=FAKE, nb=10, bt=FAKE, mb=4, sl=FAKE, cap=256, B=2,
+                    T=1, causal=1, ns=0, tot=0, o=FAKE, lse=None):
+    return lib.mla_decode_noalloc(ctypes.byref(cfg) if cfg is not None else None, q, pool, nb,
+                                  bt, mb, sl, cap, B, T, causal, ns, tot, o, lse, None)
+
+
+def test_decode_noalloc_validation(lib):
+    cfg = v3_cfg()
+    assert binding.mla_decode_noalloc_scratch_bytes() == 64 << 20
+    # the same argument checks as mla_decode, before anything else
+    assert _decode_noalloc(lib, None) == NULL
+    assert _decode_noalloc(lib, v3_cfg(dtype=7)) == DTYPE
+    assert _decode_noalloc(lib, cfg, T=0) == DIM
+    assert _decode_noalloc(lib, cfg, causal=2) == DIM
+    assert _decode_noalloc(lib, cfg, cap=4 * 64 + 1) == CAP
+    assert _decode_noalloc(lib, cfg, q=None) == NULL
+    assert _decode_noalloc(lib, cfg, q=FAKE_MIS) == ALIGN
+    assert _decode_noalloc(lib, cfg, B=0) == OK
+    # an explicit split count whose partials exceed the scratch array is
+    # refused with nothing launched
+    B, T, cap = 40, 2, 32768
+    assert mla.mla_decode_workspace_size(cfg, B, T, cap, B * cap, 64) > 64 << 20
+    assert _decode_noalloc(lib, cfg, B=B, T=T, mb=512, cap=cap, ns=64, tot=B * cap) == WS
+
+
 def test_workspace_and_split_plan(lib):
     cfg = v3_cfg()
     # one split needs no workspace
