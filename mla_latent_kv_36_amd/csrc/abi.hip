@@ -11,7 +11,6 @@
 
 namespace {
 
-constexpr int kCUs = 256;            // compute units of one MI355X
 constexpr int kMaxDc = 2048;         // generic kernel: latent columns per row
 constexpr int kMaxDnope = 4096;      // absorb kernel: LDS holds 16 rows of q_nope
 constexpr int kMaxSplits = 65535;
@@ -41,10 +40,42 @@ bool use_mfma(const mla_config* c, int T) {
   return mla::decode_mfma_supported(c->dtype, c->d_c, c->d_rope, c->block_size, T, c->n_heads);
 }
 
+// Compute units and XCDs of the device a plan is made for: the device of
+// `stream` (the current device for the null stream, or when `from_stream` is
+// false, as for the sizing calls, which take no stream).  Queried at every
+// call, so a partitioned or smaller device gets its own plan.  A host with no
+// device to ask (sizing on a machine without a GPU) plans for one MI355X:
+// 256 compute units in 8 XCDs.
+struct DeviceShape {
+  int cus;
+  int xcds;
+};
+DeviceShape device_shape(hipStream_t stream, bool from_stream) {
+  DeviceShape d{256, 8};
+  int dev = 0;
+  if (from_stream && stream != nullptr) {
+    hipDevice_t sd = 0;
+    if (hipStreamGetDevice(stream, &sd) != hipSuccess) return d;
+    dev = (int)sd;
+  } else if (hipGetDevice(&dev) != hipSuccess) {
+    (void)hipGetLastError();
+    return d;
+  }
+  int cus = 0, xcds = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
+      cus > 0)
+    d.cus = cus;
+  if (hipDeviceGetAttribute(&xcds, hipDeviceAttributeNumberOfXccs, dev) == hipSuccess && xcds > 0)
+    d.xcds = xcds;
+  if (d.xcds > d.cus) d.xcds = 1;
+  (void)hipGetLastError();
+  return d;
+}
+
 // Split plan: the rows of the longest sequence are cut into `splits` ranges of
-// `chunk` rows each (a multiple of the decode kernel's granule: its 32-row
-// pipeline unit for the MFMA kernel, a page for the generic one).  Shorter
-// sequences use the leading ranges only.
+// `chunk` rows each (a multiple of the decode kernel's granule: 32 rows for
+// the MFMA kernel, a page for the generic one).  Shorter sequences use the
+// leading ranges only.
 struct Plan {
   int splits;     // splits per sequence; a balanced plan: work items K per 64-row group
   int chunk;      // rows per split (plain plan)
@@ -53,45 +84,49 @@ struct Plan {
 
 int granule(const mla_config* c, int T) { return use_mfma(c, T) ? 32 : c->block_size; }
 
-int heuristic_splits(const mla_config* c, int B, int T, int gran_max, int64_t total_tokens) {
+int64_t groups_of(const mla_config* c, int T) { return (int64_t)T * c->n_heads / 64; }
+
+// MFMA kernel, plain plan: units of work are (64-row query group, 32-row unit
+// of the cache).  The kernel's LDS ring fits one workgroup per compute unit,
+// so aim for one wave of workgroups over the chip, but keep at least 8 units
+// per workgroup so the partial outputs (128 KiB per workgroup) stay well below
+// the cache bytes read.
+int mfma_splits(const mla_config* c, int T, int gran_max, int64_t gran_total, int cus) {
+  const int64_t work = gran_total * groups_of(c, T);
+  int64_t chunk = (work + cus - 1) / cus;
+  if (chunk < 8) chunk = 8;
+  return (int)((gran_max + chunk - 1) / chunk);
+}
+
+int heuristic_splits(const mla_config* c, int B, int T, int gran_max, int64_t gran_total,
+                     int cus) {
   if (gran_max <= 1) return 1;
-  const int64_t g = granule(c, T);
-  const int64_t gran_total =
-      total_tokens > 0 ? (total_tokens + g - 1) / g + B : (int64_t)B * gran_max;
-  if (use_mfma(c, T)) {
-    // Units of work are (64-row query group, 32-row unit of the cache).  The
-    // kernel's LDS ring fits one workgroup per compute unit, so aim for one
-    // wave of workgroups over the chip, but keep at least 8 units per
-    // workgroup so the partial outputs (128 KiB per workgroup) stay well below
-    // the cache bytes read.
-    const int64_t groups = (int64_t)T * c->n_heads / 64;
-    const int64_t work = gran_total * groups;
-    int64_t chunk = (work + kCUs - 1) / kCUs;
-    if (chunk < 8) chunk = 8;
-    return (int)((gran_max + chunk - 1) / chunk);
-  }
-  const int64_t rows = (int64_t)B * T * c->n_heads;
-  int64_t s = (4 * kCUs + rows - 1) / rows;
+  if (use_mfma(c, T)) return mfma_splits(c, T, gran_max, gran_total, cus);
+  const int64_t qrows = (int64_t)B * T * c->n_heads;
+  int64_t s = (4 * (int64_t)cus + qrows - 1) / qrows;
   if (s > gran_max) s = gran_max;
   return (int)(s < 1 ? 1 : s);
 }
 
 // The library's choice for the MFMA kernel when the lengths may differ (their
 // total is unknown or below B x the longest): a balanced plan with one work
-// item per compute unit, kCUs / G per 64-row group, when that is more than
+// item per compute unit, CUs / G per 64-row group, when that is more than
 // one per sequence.  Each sequence then gets a number of splits in proportion
 // to its length, so that no work item holds much more than the average.
 Plan make_plan(const mla_config* c, int B, int T, int max_seq_len, int64_t total_tokens,
-               int num_splits) {
+               int num_splits, const DeviceShape& dev) {
   const int g = granule(c, T);
   const int gran_max = max_seq_len > 0 ? (max_seq_len + g - 1) / g : 0;
+  const int64_t gran_total =
+      total_tokens > 0 ? (total_tokens + g - 1) / g + B : (int64_t)B * gran_max;
   if (num_splits == 0 && use_mfma(c, T) && gran_max > 1 && B > 0) {
     const bool equal = total_tokens > 0 && total_tokens >= (int64_t)B * max_seq_len;
-    const int64_t groups = (int64_t)T * c->n_heads / 64;
-    const int64_t K = kCUs / groups;
+    const int64_t K = dev.cus / groups_of(c, T);
     if (!equal && K > B) return Plan{(int)K, 0, true};
   }
-  int want = num_splits > 0 ? num_splits : heuristic_splits(c, B, T, gran_max, total_tokens);
+  int want = num_splits > 0
+                 ? num_splits
+                 : heuristic_splits(c, B, T, gran_max, gran_total, dev.cus);
   if (want > gran_max) want = gran_max;
   if (want < 1) want = 1;
   const int chunk = gran_max > 0 ? (gran_max + want - 1) / want : 1;
@@ -284,7 +319,8 @@ mla_status mla_absorb_q_append(const mla_config* cfg, const void* q_nope, const 
 int32_t mla_decode_num_splits(const mla_config* cfg, int32_t B, int32_t T,
                               int32_t max_seq_len_host, int64_t total_tokens_host) {
   if (check_cfg(cfg) != MLA_OK || B < 0 || T < 1 || max_seq_len_host < 0) return 1;
-  return make_plan(cfg, B, T, max_seq_len_host, total_tokens_host, 0).splits;
+  return make_plan(cfg, B, T, max_seq_len_host, total_tokens_host, 0, device_shape(nullptr, false))
+      .splits;
 }
 
 size_t mla_decode_workspace_size(const mla_config* cfg, int32_t B, int32_t T,
@@ -292,7 +328,8 @@ size_t mla_decode_workspace_size(const mla_config* cfg, int32_t B, int32_t T,
                                  int32_t num_splits) {
   if (check_cfg(cfg) != MLA_OK || B < 0 || T < 1 || max_seq_len_host < 0 || num_splits < 0)
     return (size_t)-1;
-  const Plan pl = make_plan(cfg, B, T, max_seq_len_host, total_tokens_host, num_splits);
+  const Plan pl = make_plan(cfg, B, T, max_seq_len_host, total_tokens_host, num_splits,
+                            device_shape(nullptr, false));
   if (pl.splits <= 1) return 0;
   return partial_bytes(cfg, B, T, pl, nullptr, nullptr);
 }
@@ -326,7 +363,8 @@ static mla_status check_decode(const mla_config* cfg, const void* q_abs, const v
 
 // Launches a checked decode under plan pl with its partials in `workspace`
 // (at least partial_bytes(pl) bytes when pl needs a merge).
-static mla_status launch_decode_plan(const mla_config* cfg, const Plan& pl, const void* q_abs,
+static mla_status launch_decode_plan(const mla_config* cfg, const Plan& pl,
+                                     const DeviceShape& dev, const void* q_abs,
                                      const void* pool, int32_t num_blocks,
                                      const int32_t* block_table, int32_t max_blocks,
                                      const int32_t* seq_lens, int32_t max_seq_len_host,
@@ -359,6 +397,7 @@ static mla_status launch_decode_plan(const mla_config* cfg, const Plan& pl, cons
   p.causal = causal;
   p.num_splits = pl.splits;
   p.chunk_rows = pl.chunk;
+  p.xcds = dev.xcds;
   p.scale_log2 = softmax_scale(cfg) * 1.4426950408889634f;
   p.plan = pl.balanced ? reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + plan_off)
                        : nullptr;
@@ -384,12 +423,13 @@ mla_status mla_decode(const mla_config* cfg, const void* q_abs, const void* pool
                                max_seq_len_host, B, T, causal, num_splits, o_lat, lse, &work);
   if (st != MLA_OK || !work) return st;
   if (workspace != nullptr && !aligned16(workspace)) return MLA_ERR_ALIGN;
-  const Plan pl = make_plan(cfg, B, T, max_seq_len_host, total_tokens_host, num_splits);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const DeviceShape dev = device_shape(s, true);
+  const Plan pl = make_plan(cfg, B, T, max_seq_len_host, total_tokens_host, num_splits, dev);
   const size_t need = pl.splits > 1 ? partial_bytes(cfg, B, T, pl, nullptr, nullptr) : 0;
   if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return MLA_ERR_WORKSPACE;
-  return launch_decode_plan(cfg, pl, q_abs, pool, num_blocks, block_table, max_blocks, seq_lens,
-                            max_seq_len_host, B, T, causal, workspace, o_lat, lse,
-                            static_cast<hipStream_t>(stream));
+  return launch_decode_plan(cfg, pl, dev, q_abs, pool, num_blocks, block_table, max_blocks,
+                            seq_lens, max_seq_len_host, B, T, causal, workspace, o_lat, lse, s);
 }
 
 size_t mla_decode_noalloc_scratch_bytes(void) { return kScratchBytes; }
@@ -404,7 +444,9 @@ mla_status mla_decode_noalloc(const mla_config* cfg, const void* q_abs, const vo
   mla_status st = check_decode(cfg, q_abs, pool, num_blocks, block_table, max_blocks, seq_lens,
                                max_seq_len_host, B, T, causal, num_splits, o_lat, lse, &work);
   if (st != MLA_OK || !work) return st;
-  Plan pl = make_plan(cfg, B, T, max_seq_len_host, total_tokens_host, num_splits);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const DeviceShape dev = device_shape(s, true);
+  Plan pl = make_plan(cfg, B, T, max_seq_len_host, total_tokens_host, num_splits, dev);
   if (pl.splits > 1 && partial_bytes(cfg, B, T, pl, nullptr, nullptr) > kScratchBytes) {
     // an explicit split count must fit as asked; the library's choice is cut
     // to the most splits whose partials fit (one split needs none)
@@ -414,15 +456,14 @@ mla_status mla_decode_noalloc(const mla_config* cfg, const void* q_abs, const vo
     int fit = (int)(kScratchBytes / per_split);
     if (fit > pl.splits) fit = pl.splits;
     for (;; --fit) {
-      pl = make_plan(cfg, B, T, max_seq_len_host, total_tokens_host, fit < 1 ? 1 : fit);
+      pl = make_plan(cfg, B, T, max_seq_len_host, total_tokens_host, fit < 1 ? 1 : fit, dev);
       if (pl.splits <= 1 || partial_bytes(cfg, B, T, pl, nullptr, nullptr) <= kScratchBytes) break;
     }
   }
   void* ws = nullptr;
-  hipStream_t s = static_cast<hipStream_t>(stream);
   if (pl.splits > 1 && scratch_address(s, &ws) != hipSuccess) return MLA_ERR_HIP;
-  return launch_decode_plan(cfg, pl, q_abs, pool, num_blocks, block_table, max_blocks, seq_lens,
-                            max_seq_len_host, B, T, causal, ws, o_lat, lse, s);
+  return launch_decode_plan(cfg, pl, dev, q_abs, pool, num_blocks, block_table, max_blocks,
+                            seq_lens, max_seq_len_host, B, T, causal, ws, o_lat, lse, s);
 }
 
 mla_status mla_out_proj(const mla_config* cfg, const float* o_lat, const void* w_uv, void* out,
@@ -478,7 +519,7 @@ constexpr float kDefaultRopeBase = 10000.0f;
 // The producer's k split aims at half the compute units: a longer k range per
 // workgroup, but half the partial sums to write and add (measured faster at
 // the V2-scale width than one workgroup per compute unit).
-constexpr int kProduceWorkgroups = kCUs / 2;
+int produce_workgroups() { return device_shape(nullptr, false).cus / 2; }
 
 // 0 selects the default base; anything else must be a finite value > 1
 bool rope_base_of(float in, float* out) {
@@ -496,7 +537,7 @@ extern "C" size_t mla_kv_produce_workspace_size(const mla_config* cfg, int32_t M
                                                 int32_t d_model) {
   if (check_cfg(cfg) != MLA_OK || M < 0 || d_model <= 0) return (size_t)-1;
   if (M == 0) return 0;
-  const int ks = mla::kv_produce_ksplit(cfg->dtype, M, d_model, cfg->d_c, cfg->d_rope, kProduceWorkgroups);
+  const int ks = mla::kv_produce_ksplit(cfg->dtype, M, d_model, cfg->d_c, cfg->d_rope, produce_workgroups());
   return round256((size_t)ks * M * (cfg->d_c + cfg->d_rope) * sizeof(float));
 }
 
@@ -525,7 +566,7 @@ extern "C" mla_status mla_kv_produce(const mla_config* cfg, const void* hidden, 
     return MLA_ERR_ALIGN;
   const size_t need = mla_kv_produce_workspace_size(cfg, M, d_model);
   if (workspace == nullptr || workspace_bytes < need) return MLA_ERR_WORKSPACE;
-  const int ks = mla::kv_produce_ksplit(cfg->dtype, M, d_model, cfg->d_c, cfg->d_rope, kProduceWorkgroups);
+  const int ks = mla::kv_produce_ksplit(cfg->dtype, M, d_model, cfg->d_c, cfg->d_rope, produce_workgroups());
   return hip_status(mla::launch_kv_produce(
       cfg->dtype, hidden, d_model, w_dkv, w_kr, base, static_cast<float*>(workspace), ks, pool,
       num_blocks, block_table, max_blocks, seq_lens, B, T_new, cfg->block_size, cfg->d_c,
@@ -549,7 +590,7 @@ extern "C" mla_status mla_rope(const mla_config* cfg, void* x, int32_t heads,
 namespace {
 // The output-side product aims at two workgroups per compute unit (its
 // launch bounds allow two resident), splitting k when the tiles are fewer.
-constexpr int kOutputWorkgroups = 2 * kCUs;
+int output_workgroups() { return 2 * device_shape(nullptr, false).cus; }
 
 // k of the output-side product: H * d_v for W^O, H * d_c for the folded
 // matrix; 0 when it does not fit an int32.
@@ -560,7 +601,7 @@ int64_t output_k(const mla_config* c, bool folded) {
 
 size_t output_workspace(const mla_config* c, int M, int d_model, bool folded) {
   const int64_t K = output_k(c, folded);
-  const int ks = mla::wo_gemm_ksplit(c->dtype, M, d_model, (int)K, kOutputWorkgroups);
+  const int ks = mla::wo_gemm_ksplit(c->dtype, M, d_model, (int)K, output_workgroups());
   return ks > 1 ? round256((size_t)ks * M * d_model * sizeof(float)) : 0;
 }
 
@@ -583,7 +624,7 @@ mla_status output_call(const mla_config* cfg, bool folded, const void* x, const 
       (workspace != nullptr && !aligned16(workspace)))
     return MLA_ERR_ALIGN;
   const int K = (int)output_k(cfg, folded);
-  const int ks = mla::wo_gemm_ksplit(cfg->dtype, M, d_model, K, kOutputWorkgroups);
+  const int ks = mla::wo_gemm_ksplit(cfg->dtype, M, d_model, K, output_workgroups());
   if (ks > 1 && (workspace == nullptr || workspace_bytes < output_workspace(cfg, M, d_model, folded)))
     return MLA_ERR_WORKSPACE;
   // the latent outputs are fp32; so are the per-head outputs of an fp32 configuration

@@ -325,13 +325,13 @@ __global__ __launch_bounds__(NT, 1) void decode_mfma_kernel(const DecodeParams p
 
   const int G = (p.T * p.H) / ROWS;
   const int S = p.num_splits;
-  // Workgroup i is dispatched to XCD i % 8, and each XCD has its own L2.  XCD
-  // x gets a contiguous block of (sequence, split) pairs, and all G 64-row
-  // groups of each: the pages of a pair and the absorbed queries of a
-  // sequence then come from HBM once per XCD and from L2 for the other
-  // workgroups that read them.  Ids past the last full set of 8G keep the
-  // plain order.
-  constexpr int XCDS = 8;
+  // Workgroup i is dispatched to XCD i % X (X XCDs, queried on the host), and
+  // each XCD has its own L2.  XCD x gets a contiguous block of (sequence,
+  // split) pairs, and all G 64-row groups of each: the pages of a pair and the
+  // absorbed queries of a sequence then come from HBM once per XCD and from L2
+  // for the other workgroups that read them.  Ids past the last full set of
+  // X G keep the plain order.
+  const int XCDS = p.xcds;
   const int i = blockIdx.x;
   const int full = (int)gridDim.x - (int)gridDim.x % (XCDS * G);
   int g, pair;

@@ -23,6 +23,7 @@ struct DecodeParams {
   int causal;
   int num_splits;             // S
   int chunk_rows;             // cache rows per split (a multiple of the kernel granule)
+  int xcds;                   // MFMA kernel: XCDs of the device (workgroup placement)
   float scale_log2;           // softmax scale * log2(e)
   // Balanced plan (MFMA kernel only): when non-null, num_splits is the number
   // K of work items per 64-row group, split sizes are chosen per sequence on
