@@ -85,34 +85,105 @@ def _blas_threads() -> int:
         return 1
 
 
+def _affinity_cpus() -> int:
+    try:
+        return len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        return os.cpu_count() or 1
+
+
 def cpu_baseline(w, budget_s: float) -> dict:
-    """The fp64 oracle, as it stands, on a sub-batch of the same workload
-    (k sequences of the same shape and distributions), timed on this host."""
+    """The oracle, as it stands, on a sub-batch of the same workload (k
+    sequences of the same shape and distributions, fresh seeded draws), timed
+    on this host: the whole step (absorb, append, decode, out-projection) in
+    float32, whose per-sequence decode is the BLAS products [H x W].[W x n]
+    per new token, as the median of 3 runs; the same in float64 beside it."""
+    import numpy as np
     import oracle
     from workloads import make_inputs
 
-    def run(k):
+    def run(k, dtype):
         bt = make_inputs(w.scaled(B=k), seed=w.seed + 1000)
         t0 = time.perf_counter()
         oracle.step_ref(bt.q_nope, bt.q_rope, bt.w_uk, bt.w_uv, bt.pool, bt.block_table,
-                        bt.lengths, bt.new_rows, w.d_c, w.scale, w.causal, w.block_size)
+                        bt.lengths, bt.new_rows, w.d_c, w.scale, w.causal, w.block_size,
+                        dtype=dtype)
         return time.perf_counter() - t0
 
-    # one sequence first, to size the sample: whole batches of the workload's
-    # shape, repeated until about budget_s of CPU work
-    t1 = run(1)
-    k = int(max(1, min(w.B, budget_s / max(t1, 1e-3))))
-    reps = int(max(1, round(budget_s / max(t1 * k, 1e-3))))
-    dt = sum(run(k) for _ in range(reps))
-    return {"value": reps * k * w.T / dt, "unit": "tokens/s", "cores": _blas_threads(),
+    # one sequence of each precision first, to size the sample so that three
+    # runs of each take about budget_s in all
+    t32, t64 = run(1, np.float32), run(1, np.float64)
+    k = int(max(1, min(w.B, budget_s / max(3 * (t32 + t64), 1e-3))))
+    d32 = sorted(run(k, np.float32) for _ in range(3))
+    d64 = sorted(run(k, np.float64) for _ in range(3))
+    threads = _blas_threads()
+    return {"value": k * w.T / d32[1], "unit": "tokens/s", "cores": threads,
             "kind": "oracle",
-            "sample": f"fp64 numpy oracle, whole step (absorb, append, decode, out-proj), "
-                      f"{reps} x {k} sequences of the workload's shape (fresh seeded draws), "
-                      f"{dt:.1f} s",
-            "host_cpus": os.cpu_count(), "cpu_model": _cpu_model()}
+            "sample": f"float32 oracle, whole step (absorb, append, decode, out-proj) on "
+                      f"{k} of the workload's {w.B} sequences (same shapes and "
+                      f"distributions, fresh seeded draws); median of 3 runs "
+                      f"({', '.join(f'{d:.2f}' for d in d32)} s)",
+            "fp64": {"value": k * w.T / d64[1], "unit": "tokens/s",
+                     "runs_s": [round(d, 3) for d in d64]},
+            "blas_threads": threads, "host_cpus": os.cpu_count(),
+            "affinity_cpus": _affinity_cpus(), "cpu_model": _cpu_model()}
 
 
-def producer_phase(w, bt, steps, torch, mla) -> dict:
+def _stats_us(samples_ms):
+    import numpy as np
+    a = np.asarray(samples_ms, dtype=np.float64) * 1e3
+    return {"median": float(np.median(a)), "p10": float(np.percentile(a, 10)),
+            "p90": float(np.percentile(a, 90)), "reps": int(a.size)}
+
+
+def replay_stats(torch, g, per_replay: int, reps: int, warm: int = 5) -> dict:
+    """Per-call time of a captured graph holding `per_replay` calls (one per
+    rotated copy): `warm` untimed replays, then `reps` replays each between
+    its own pair of HIP events on the replay stream, all enqueued before one
+    synchronisation.  Returns the median, p10 and p90 per call, in us."""
+    stream = torch.cuda.current_stream()
+    for _ in range(warm):
+        g.replay()
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+    ev[0].record(stream)
+    for i in range(reps):
+        g.replay()
+        ev[i + 1].record(stream)
+    torch.cuda.synchronize()
+    return _stats_us([ev[i].elapsed_time(ev[i + 1]) / per_replay for i in range(reps)])
+
+
+def streaming_read(torch, mib: int = 2048, reps: int = 20) -> dict:
+    """The box's achievable HBM rate for a plain streaming read (a sum over a
+    buffer of `mib` MiB, 8x the 256 MB MALL) and for a plain copy."""
+    n = (mib << 20) // 4
+    x = torch.ones(n, dtype=torch.float32, device="cuda")
+    y = torch.empty_like(x)
+    stream = torch.cuda.current_stream()
+
+    def timed(fn):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+        ev[0].record(stream)
+        for i in range(reps):
+            fn()
+            ev[i + 1].record(stream)
+        torch.cuda.synchronize()
+        return sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(reps))[reps // 2]
+
+    ms_read = timed(lambda: x.sum())
+    ms_copy = timed(lambda: y.copy_(x))
+    del x, y
+    return {"read_GBps": (mib << 20) / (ms_read * 1e-3) / 1e9,
+            "copy_GBps": 2 * (mib << 20) / (ms_copy * 1e-3) / 1e9,
+            "bytes": mib << 20, "read_kernel": "torch sum (fp32)",
+            "copy_kernel": "torch copy_ (fp32)", "median_of": reps}
+
+
+def producer_phase(w, bt, steps, torch, mla, reps) -> dict:
     """mla_kv_produce for the step's new tokens (W^DKV / W^KR down-projection,
     RoPE on k^R, written into the cache), replayed over enough copies of the
     hidden vectors and weights (>= 512 MiB in all) that the 256 MB MALL cannot
@@ -142,27 +213,17 @@ def producer_phase(w, bt, steps, torch, mla) -> dict:
     with torch.cuda.graph(g):
         for k in range(copies):
             call(k)
-    stream = torch.cuda.current_stream()
-    for _ in range(2):
-        g.replay()
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    reps = 5
-    e0.record(stream)
-    for _ in range(reps):
-        g.replay()
-    e1.record(stream)
-    torch.cuda.synchronize()
-    us = e0.elapsed_time(e1) * 1e3 / (reps * copies)
+    st_us = replay_stats(torch, g, copies, reps)
+    us = st_us["median"]
     algo = read_bytes + M * N * elem
     return {"call": "mla_kv_produce", "kernels": "kv_proj_mfma_kernel + kv_rope_append_kernel",
             "d_model": d, "tokens": M, "us": us, "bound": "hbm",
             "algorithmic_bytes": algo, "GBps": algo / (us * 1e-6) / 1e9,
-            "frac": algo / (us * 1e-6) / 1e9 / HBM_PEAK_GBPS,
+            "frac": algo / (us * 1e-6) / 1e9 / HBM_PEAK_GBPS, "us_stats": st_us,
             "k_split_workspace_bytes": nbytes, "rotated_copies": copies}
 
 
-def output_side_phase(w, torch, mla) -> dict:
+def output_side_phase(w, torch, mla, reps) -> dict:
     """The output side after the step's W^UV up-projection: mla_o_proj (W^O over
     the concatenated heads) replayed over enough copies of W^O and the per-head
     outputs (>= 512 MiB in all) that the 256 MB MALL cannot serve them; the
@@ -179,14 +240,14 @@ def output_side_phase(w, torch, mla) -> dict:
     K, Kf = w.H * w.d_v, w.H * w.d_c
     stream = torch.cuda.current_stream()
 
-    def timed(fn, reps):
+    def timed(fn, n):
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record(stream)
-        for _ in range(reps):
+        for _ in range(n):
             fn()
         e1.record(stream)
         torch.cuda.synchronize()
-        return e0.elapsed_time(e1) * 1e3 / reps
+        return e0.elapsed_time(e1) * 1e3 / n
 
     def graph_of(calls):
         g = torch.cuda.CUDAGraph()
@@ -207,12 +268,13 @@ def output_side_phase(w, torch, mla) -> dict:
     n_ws = mla.mla_o_proj_workspace_size(cfg, M, d, False)
     ws = torch.empty(max(n_ws, 256), dtype=torch.uint8, device="cuda")
     g = graph_of([lambda a=a, wo=wo: mla.mla_o_proj(cfg, a, wo, y, ws) for a, wo in sets])
-    us = timed(g.replay, 5) / copies
+    st_o = replay_stats(torch, g, copies, reps)
+    us = st_o["median"]
     algo = wo_bytes + M * K * elem + M * d * elem
     out = {"o_proj": {"call": "mla_o_proj", "kernels": "wo_gemm_mfma_kernel + wo_finish_kernel",
                       "tokens": M, "k": K, "d_model": d, "us": us, "bound": "hbm",
                       "algorithmic_bytes": algo, "GBps": algo / (us * 1e-6) / 1e9,
-                      "frac": algo / (us * 1e-6) / 1e9 / HBM_PEAK_GBPS,
+                      "frac": algo / (us * 1e-6) / 1e9 / HBM_PEAK_GBPS, "us_stats": st_o,
                       "k_split_workspace_bytes": n_ws, "rotated_copies": copies}}
     del sets, base
     # the fold (once per model), then the folded product
@@ -227,29 +289,144 @@ def output_side_phase(w, torch, mla) -> dict:
     n_wsf = mla.mla_o_proj_workspace_size(cfg, M, d, True)
     wsf = torch.empty(max(n_wsf, 256), dtype=torch.uint8, device="cuda")
     g2 = graph_of([lambda: mla.mla_o_proj_folded(cfg, o_lat, wf, y, wsf)])
-    us_f = timed(g2.replay, 5)
+    st_f = replay_stats(torch, g2, 1, reps)
+    us_f = st_f["median"]
     algo_f = d * Kf * elem + M * Kf * 4 + M * d * elem
     out["o_proj_folded"] = {"call": "mla_o_proj_folded",
                             "kernels": "wo_gemm_mfma_kernel + wo_finish_kernel",
                             "us": us_f, "bound": "hbm", "algorithmic_bytes": algo_f,
                             "GBps": algo_f / (us_f * 1e-6) / 1e9,
                             "frac": algo_f / (us_f * 1e-6) / 1e9 / HBM_PEAK_GBPS,
-                            "k_split_workspace_bytes": n_wsf,
+                            "us_stats": st_f, "k_split_workspace_bytes": n_wsf,
                             "weight_bytes_vs_w_o": d * Kf / (d * K)}
     del wf, g2
     return out
 
 
+def log(msg: str) -> None:
+    """A progress line on stderr (the JSON line alone goes to stdout)."""
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def decode_work(w, bt):
+    """Algorithmic bytes (the cache rows read, once per sequence) and flops of
+    one mla_decode call on batch bt."""
+    W = w.d_c + w.d_r
+    elem = 2 if w.dtype == "bf16" else 4
+    cache_bytes = int(bt.seq_lens.sum()) * W * elem
+    # (query, cached row) pairs: with the causal mask query t of a sequence of
+    # n rows (after the append) sees n - T + t + 1 of them
+    if w.causal:
+        pairs = sum(int(n) * w.T - w.T * (w.T - 1) // 2 for n in bt.seq_lens)
+    else:
+        pairs = sum(int(n) * w.T for n in bt.seq_lens)
+    return cache_bytes, pairs * w.H * (2 * W + 2 * w.d_c)
+
+
+def roofline(cache_bytes, flops, us):
+    """The bound the workload's arithmetic intensity puts it under (T = 1
+    decode sits below the ridge, many queries per row above it) and the
+    fractions of both peaks."""
+    gbps = cache_bytes / (us * 1e-6) / 1e9
+    tflops = flops / (us * 1e-6) / 1e12
+    mfma_bound = flops / cache_bytes > MFMA_BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBPS * 1e9)
+    return {"bound": "mfma" if mfma_bound else "hbm",
+            "achieved": tflops if mfma_bound else gbps,
+            "peak": MFMA_BF16_PEAK_TFLOPS if mfma_bound else HBM_PEAK_GBPS,
+            "unit": "TFLOP/s" if mfma_bound else "GB/s",
+            "frac": (tflops / MFMA_BF16_PEAK_TFLOPS) if mfma_bound else (gbps / HBM_PEAK_GBPS),
+            "cache_GBps": gbps, "hbm_frac": gbps / HBM_PEAK_GBPS,
+            "mfma_tflops": tflops, "mfma_frac": tflops / MFMA_BF16_PEAK_TFLOPS}
+
+
+def make_steps(w, bt, rotate, num_splits, mla, DecodeStep, copy_weights=True):
+    """One DecodeStep per rotated copy: independent copies of the cache pool
+    (and of the weights, when copy_weights) so that no call of a replay reads
+    what the previous one left in the 256 MB MALL."""
+    from workloads.device import upload
+    cfg = mla.make_config(w.H, w.d_c, w.d_r, w.d_n, w.d_v, w.block_size, 0.0, w.dtype)
+    total_tokens = int(bt.seq_lens.sum())
+    base = upload(bt)
+    steps = []
+    for r in range(rotate):
+        dev = dict(base)
+        if r > 0:
+            for k in (("pool", "w_uk", "w_uv") if copy_weights else ("pool",)):
+                dev[k] = base[k].clone()
+        steps.append(DecodeStep(cfg, q_nope=dev["q_nope"], q_rope=dev["q_rope"],
+                                w_uk=dev["w_uk"], w_uv=dev["w_uv"], pool=dev["pool"],
+                                block_table=dev["block_table"], lengths=dev["lengths"],
+                                new_rows=dev["new_rows"], max_len_after=bt.max_seq_len,
+                                causal=w.causal, num_splits=num_splits,
+                                total_tokens=total_tokens))
+    return cfg, steps
+
+
+def capture(torch, steps, fn):
+    """One graph holding fn(step) for every rotated copy, in order."""
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for st in steps:
+            fn(st)
+    return g
+
+
+def extra_workload(name, args, torch, mla, DecodeStep, reps) -> dict:
+    """mla_decode of another workload, timed the same way as the main one
+    (rotated copies, per-replay events), with its own roofline; the
+    multi-token workload also reports its whole step."""
+    from workloads import BY_NAME, make_inputs
+    w = BY_NAME[name]
+    log(f"{name}: drawing inputs")
+    bt = make_inputs(w)
+    cfg, steps = make_steps(w, bt, args.rotate, 0, mla, DecodeStep, copy_weights=False)
+    log(f"{name}: timing")
+    for st in steps:            # the appended rows and absorbed queries decode reads
+        st.absorb_append()
+    torch.cuda.synchronize()
+    g = capture(torch, steps, lambda st: st.decode())
+    dec = replay_stats(torch, g, len(steps), reps)
+    del g
+    cache_bytes, flops = decode_work(w, bt)
+    tokens = w.B * w.T
+    out = {"workload": name, "B": w.B, "T": w.T, "H": w.H, "rows_attended_max": int(bt.seq_lens.max()),
+           "total_rows": int(bt.seq_lens.sum()),
+           "num_splits": mla.mla_decode_num_splits(cfg, w.B, w.T, bt.max_seq_len,
+                                                   int(bt.seq_lens.sum())),
+           "decode_us": dec, "decode_tokens_per_s": tokens / (dec["median"] * 1e-6),
+           "algorithmic_bytes_per_launch": cache_bytes,
+           "algorithmic_flops_per_launch": flops,
+           "roofline": roofline(cache_bytes, flops, dec["median"]),
+           "rotated_copies": len(steps)}
+    if w.T > 1:
+        gs = capture(torch, steps, lambda st: st.run())
+        stp = replay_stats(torch, gs, len(steps), reps)
+        out["step_us"] = stp
+        out["step_tokens_per_s"] = tokens / (stp["median"] * 1e-6)
+        del gs
+    del steps
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return out
+
+
+EXTRA_WORKLOADS = ("varlen_serving", "long_128k", "v2_multi_token")
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="v3_decode")
     ap.add_argument("--rotate", type=int, default=8)
     ap.add_argument("--num-splits", type=int, default=0)
+    ap.add_argument("--phase-reps", type=int, default=50,
+                    help="graph replays per timed phase (each replay: one call per copy)")
     ap.add_argument("--cpu-seconds", type=float, default=20.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extra", action="store_true",
+                    help="skip the other workloads' mla_decode timings")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="only run a plain device copy of this many MiB five times "
                          "(the known-size reference for HBM byte counters) and exit")
@@ -259,8 +436,11 @@ def main() -> int:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported "
               "(the library has no multi-GPU path)", file=sys.stderr)
         return 2
+    if args.steps < 1 or args.warmup < 0 or args.rotate < 1 or args.phase_reps < 1:
+        print("--steps, --rotate and --phase-reps must be >= 1, --warmup >= 0",
+              file=sys.stderr)
+        return 2
 
-    import numpy as np
     import torch
 
     if args.copy_probe_mib > 0:
@@ -279,98 +459,64 @@ def main() -> int:
     from mla_latent_kv_36_amd import build as mbuild
     from mla_latent_kv_36_amd.step import DecodeStep
     from workloads import BY_NAME, make_inputs
-    from workloads.device import upload
 
     if not mbuild.built():
         mbuild.build()
     mla.load()
     w = BY_NAME[args.workload]
     torch.cuda.set_device(0)
+    props = torch.cuda.get_device_properties(0)
+    log(f"{w.name}: drawing inputs")
     bt = make_inputs(w)
-    cfg = mla.make_config(w.H, w.d_c, w.d_r, w.d_n, w.d_v, w.block_size, 0.0, w.dtype)
+    cfg, steps = make_steps(w, bt, args.rotate, args.num_splits, mla, DecodeStep)
     total_tokens = int(bt.seq_lens.sum())
-
-    steps = []
-    base = upload(bt)
-    for r in range(args.rotate):
-        dev = dict(base)
-        if r > 0:   # independent copies of everything large
-            for k in ("pool", "w_uk", "w_uv"):
-                dev[k] = base[k].clone()
-        steps.append(DecodeStep(cfg, q_nope=dev["q_nope"], q_rope=dev["q_rope"],
-                                w_uk=dev["w_uk"], w_uv=dev["w_uv"], pool=dev["pool"],
-                                block_table=dev["block_table"], lengths=dev["lengths"],
-                                new_rows=dev["new_rows"], max_len_after=bt.max_seq_len,
-                                causal=w.causal, num_splits=args.num_splits,
-                                total_tokens=total_tokens))
     splits = mla.mla_decode_num_splits(cfg, w.B, w.T, bt.max_seq_len, total_tokens) \
         if args.num_splits == 0 else args.num_splits
-
-    # Each phase (and the whole step) over all rotated copies is captured once in
-    # a HIP graph and replayed, so the timing sees GPU time, not Python launch cost.
-    def capture(fn):
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g):
-            for st in steps:
-                fn(st)
-        return g
-
-    graphs = {
-        "step": capture(lambda st: st.run()),
-        "decode": capture(lambda st: st.decode()),
-        "absorb_q": capture(lambda st: st.absorb()),
-        "cache_append": capture(lambda st: st.append()),
-        "absorb_q_append": capture(lambda st: st.absorb_append()),
-        "out_proj": capture(lambda st: st.out_proj()),
-    }
     stream = torch.cuda.current_stream()
-    reps = max(1, -(-args.steps // args.rotate))
-    wreps = max(1, -(-args.warmup // args.rotate))
 
-    def timed(g):
-        for _ in range(wreps):
-            g.replay()
-        torch.cuda.synchronize()
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        for _ in range(reps):
-            g.replay()
-        e1.record(stream)
-        torch.cuda.synchronize()
-        return e0.elapsed_time(e1) / (reps * args.rotate)   # ms per call
+    # The step: one graph per rotated copy (absorb + append, decode,
+    # out-projection), replayed in turn: `warmup` untimed steps, then exactly
+    # `steps` timed ones between two synchronisations.
+    step_graphs = [capture(torch, [st], lambda x: x.run()) for st in steps]
+    for i in range(args.warmup):
+        step_graphs[i % len(step_graphs)].replay()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record(stream)
+    for i in range(args.steps):
+        step_graphs[(args.warmup + i) % len(step_graphs)].replay()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall_s = time.perf_counter() - t0
+    ms_step = e0.elapsed_time(e1) / args.steps
+    log(f"{args.steps} steps timed: {ms_step * 1e3:.1f} us per step")
 
-    ms_step = timed(graphs["step"])
-    ms_decode = timed(graphs["decode"])
-    ms_absorb = timed(graphs["absorb_q"])
-    ms_append = timed(graphs["cache_append"])
-    ms_absorb_append = timed(graphs["absorb_q_append"])
-    ms_out = timed(graphs["out_proj"])
+    # Each phase over all rotated copies in one graph, timed per replay.
+    phase_fns = {"decode": lambda st: st.decode(), "absorb_q": lambda st: st.absorb(),
+                 "cache_append": lambda st: st.append(),
+                 "absorb_q_append": lambda st: st.absorb_append(),
+                 "out_proj": lambda st: st.out_proj()}
+    phases = {}
+    for name, fn in phase_fns.items():
+        g = capture(torch, steps, fn)
+        phases[name] = replay_stats(torch, g, len(steps), args.phase_reps)
+        del g
+        log(f"phase {name}: median {phases[name]['median']:.2f} us per call")
+    us_decode = phases["decode"]["median"]
 
-    W = w.d_c + w.d_r
-    elem = 2 if w.dtype == "bf16" else 4
-    cache_bytes = total_tokens * W * elem                       # per decode launch
-    # (query, cached row) pairs: with the causal mask query t of a sequence of
-    # n rows (after the append) sees n - T + t + 1 of them
-    if w.causal:
-        pairs = sum(int(n) * w.T - w.T * (w.T - 1) // 2 for n in bt.seq_lens)
-    else:
-        pairs = sum(int(n) * w.T for n in bt.seq_lens)
-    decode_flops = pairs * w.H * (2 * W + 2 * w.d_c)
-    gbps = cache_bytes / (ms_decode * 1e-3) / 1e9
-    tflops = decode_flops / (ms_decode * 1e-3) / 1e12
-    # the bound is the one the workload's arithmetic intensity puts it under
-    # (T = 1 decode sits below the ridge, many queries per row above it)
-    mfma_bound = decode_flops / cache_bytes > MFMA_BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBPS * 1e9)
+    cache_bytes, decode_flops = decode_work(w, bt)
     tokens = w.B * w.T
     traffic = measured_traffic(w.name, splits)
+    rl = roofline(cache_bytes, decode_flops, us_decode)
     line = {
         "metric": "MLA decode tokens/s & latent-cache GB/s (% HBM peak, % MFMA) on 1 MI355X",
         "value": tokens / (ms_step * 1e-3),
         "unit": "tokens/s",
         "n_gpus": 1,
-        "steps": reps * args.rotate,
-        "warmup": wreps * args.rotate,
+        "steps": args.steps,
+        "warmup": args.warmup,
         "ms_per_step": ms_step,
         "higher_is_better": True,
         "scaling": "weak",
@@ -381,34 +527,42 @@ def main() -> int:
                    "d_rope": w.d_r, "d_nope": w.d_n, "d_v": w.d_v,
                    "cached_rows_before_step": w.N, "rows_attended": int(bt.seq_lens.max()),
                    "block_size": w.block_size, "num_splits": splits,
-                   "rotated_copies": args.rotate, "timing": "HIP graph replay"},
-        "roofline": {"kernel": "mla_decode launch = decode_mfma_kernel + combine_kernel",
-                     "bound": "mfma" if mfma_bound else "hbm",
-                     "achieved": tflops if mfma_bound else gbps,
-                     "peak": MFMA_BF16_PEAK_TFLOPS if mfma_bound else HBM_PEAK_GBPS,
-                     "unit": "TFLOP/s" if mfma_bound else "GB/s",
-                     "frac": (tflops / MFMA_BF16_PEAK_TFLOPS) if mfma_bound
-                     else (gbps / HBM_PEAK_GBPS),
-                     "traffic": traffic["hbm_bytes_per_launch"] if traffic else None,
-                     "traffic_detail": ({k: traffic[k] for k in
-                                         ("fetch_bytes_per_launch", "write_bytes_per_launch",
-                                          "per_kernel", "calibration")}
-                                        if traffic else None),
-                     "algorithmic_bytes_per_launch": cache_bytes,
-                     "avg_launch_us": ms_decode * 1e3,
-                     "algorithmic_flops_per_launch": decode_flops,
-                     "cache_GBps": gbps, "hbm_frac": gbps / HBM_PEAK_GBPS,
-                     "mfma_tflops": tflops, "mfma_frac": tflops / MFMA_BF16_PEAK_TFLOPS},
+                   "rotated_copies": args.rotate,
+                   "timing": "HIP graph replay; step: one graph per rotated copy, "
+                             "replayed in turn; phases: per-replay HIP events"},
+        "roofline": dict(
+            {"kernel": "mla_decode call (split kernel + log-sum-exp merge), median of "
+                       f"{args.phase_reps} replays x {args.rotate} calls"},
+            **{k: rl[k] for k in ("bound", "achieved", "peak", "unit", "frac")},
+            traffic=traffic["hbm_bytes_per_launch"] if traffic else None,
+            traffic_detail=({k: traffic[k] for k in
+                             ("fetch_bytes_per_launch", "write_bytes_per_launch",
+                              "per_kernel", "calibration")} if traffic else None),
+            algorithmic_bytes_per_launch=cache_bytes,
+            algorithmic_flops_per_launch=decode_flops,
+            launch_us=phases["decode"],
+            **{k: rl[k] for k in ("cache_GBps", "hbm_frac", "mfma_tflops", "mfma_frac")}),
+        "wall_s_timed_steps": wall_s,
         "latent_cache_GBps_step": cache_bytes / (ms_step * 1e-3) / 1e9,
-        "decode_tokens_per_s": tokens / (ms_decode * 1e-3),
-        "phases_us": {"absorb_q": ms_absorb * 1e3, "cache_append": ms_append * 1e3,
-                      "absorb_q_append": ms_absorb_append * 1e3,
-                      "decode": ms_decode * 1e3, "out_proj": ms_out * 1e3},
+        "decode_tokens_per_s": tokens / (us_decode * 1e-6),
+        "phases_us": phases,
+        "device": {"name": props.name, "compute_units": props.multi_processor_count,
+                   "gcn_arch": getattr(props, "gcnArchName", "")},
     }
+    del step_graphs
+    line["achievable_hbm"] = streaming_read(torch)
     if w.d_model > 0:
-        line["producer"] = producer_phase(w, bt, steps, torch, mla)
-        line["output_side"] = output_side_phase(w, torch, mla)
+        line["producer"] = producer_phase(w, bt, steps, torch, mla, args.phase_reps)
+        line["output_side"] = output_side_phase(w, torch, mla, args.phase_reps)
+    del steps
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    if not args.no_extra:
+        line["workloads"] = {name: extra_workload(name, args, torch, mla, DecodeStep,
+                                                  args.phase_reps)
+                             for name in EXTRA_WORKLOADS if name != w.name}
     if not args.no_cpu_baseline:
+        log("timing the CPU oracle")
         line["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
     else:
         line["cpu_baseline"] = None

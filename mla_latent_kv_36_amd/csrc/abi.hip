@@ -136,16 +136,18 @@ Plan make_plan(const mla_config* c, int B, int T, int max_seq_len, int64_t total
 
 size_t round256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-// Workspace of a split plan: partial outputs (fp32, d_c per row) and partial
-// log-sum-exps (fp32) for B x S x T*H rows (plain plan) or K x T*H rows (a
-// balanced plan, whose partials are indexed by work item), then, for a
-// balanced plan, the per-sequence table of 4 int32 the merge reads; each
-// region rounded up to 256 bytes.
+// Workspace of a split plan: partial outputs (d_c per row: bf16 from the
+// MFMA kernel, fp32 from the generic one) and partial log-sum-exps (fp32) for
+// B x S x T*H rows (plain plan) or K x T*H rows (a balanced plan, whose
+// partials are indexed by work item), then, for a balanced plan, the
+// per-sequence table of 4 int32 the merge reads; each region rounded up to
+// 256 bytes.
 size_t partial_bytes(const mla_config* c, int B, int T, const Plan& pl, size_t* lse_offset,
                      size_t* plan_offset) {
   const size_t rows =
       (pl.balanced ? (size_t)pl.splits : (size_t)B * pl.splits) * T * c->n_heads;
-  const size_t o_bytes = round256(rows * c->d_c * sizeof(float));
+  const size_t elem = use_mfma(c, T) ? 2 : sizeof(float);
+  const size_t o_bytes = round256(rows * c->d_c * elem);
   const size_t lse_bytes = round256(rows * sizeof(float));
   if (lse_offset) *lse_offset = o_bytes;
   if (plan_offset) *plan_offset = o_bytes + lse_bytes;
@@ -382,7 +384,8 @@ static mla_status launch_decode_plan(const mla_config* cfg, const Plan& pl,
   p.seq_lens = seq_lens;
   p.o_lat = o_lat;
   p.lse = lse;
-  p.part_o = merge ? static_cast<float*>(workspace) : nullptr;
+  p.part_o = merge ? workspace : nullptr;
+  p.part_bf16 = use_mfma(cfg, T) ? 1 : 0;
   p.part_lse = merge ? reinterpret_cast<float*>(static_cast<char*>(workspace) + lse_off)
                      : nullptr;
   p.B = B;

@@ -98,7 +98,6 @@ __device__ __forceinline__ f32x4 mfma16(const bf16x8& a, const bf16x8& b, const 
 }
 
 typedef __attribute__((__vector_size__(4 * sizeof(short)))) short s16x4;
-typedef __attribute__((__vector_size__(8 * sizeof(uint16_t)))) uint16_t u16x8;
 
 __device__ __forceinline__ s16x4 lds_tr16(const uint8_t* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
@@ -738,23 +737,31 @@ __global__ __launch_bounds__(NT, 1) void decode_mfma_kernel(const DecodeParams p
 
     softmax_finish(sm, p, v, lane, m_run, l_run, direct, b, pidx, TH, rb);
     lds_barrier();                         // F
-    float* dst = direct ? p.o_lat + ((size_t)b * TH + rb) * DC
-                        : p.part_o + ((size_t)pidx * TH + rb) * DC;
     // Streaming (non-temporal) stores: the rows are read by the next kernel,
     // not by this one, and lines left dirty in L2 would all be written back
-    // at the end of the launch, which delays the next kernel's start.
+    // at the end of the launch, which delays the next kernel's start.  A
+    // split's partial is stored as bf16: it is a normalised average of cached
+    // rows, so bf16 keeps 8 significant bits of every element whatever its
+    // range, and the merge reads half the bytes.
+    auto store_rows = [&](auto* dst, auto cvt) __attribute__((always_inline)) {
 #pragma unroll
-    for (int rt = 0; rt < 2; ++rt) {
+      for (int rt = 0; rt < 2; ++rt) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int row = 32 * rt + 8 * (r >> 2) + 4 * lhi + (r & 3);
-        const float inv = sm.lrow[row];
+        for (int r = 0; r < 16; ++r) {
+          const int row = 32 * rt + 8 * (r >> 2) + 4 * lhi + (r & 3);
+          const float inv = sm.lrow[row];
 #pragma unroll
-        for (int dt = 0; dt < 4; ++dt)
-          __builtin_nontemporal_store(o[rt][dt][r] * inv,
-                                      &dst[(size_t)row * DC + 128 * v + 32 * dt + l32]);
+          for (int dt = 0; dt < 4; ++dt)
+            __builtin_nontemporal_store(cvt(o[rt][dt][r] * inv),
+                                        &dst[(size_t)row * DC + 128 * v + 32 * dt + l32]);
+        }
       }
-    }
+    };
+    if (direct)
+      store_rows(p.o_lat + ((size_t)b * TH + rb) * DC, [](float x) { return x; });
+    else
+      store_rows(static_cast<uint16_t*>(p.part_o) + ((size_t)pidx * TH + rb) * DC,
+                 [](float x) { return f32_to_bf16(x); });
   }
 }
 

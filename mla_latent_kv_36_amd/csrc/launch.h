@@ -15,7 +15,7 @@ struct DecodeParams {
   const int32_t* seq_lens;    // [B], rows including the T new tokens
   float* o_lat;               // [B, T, H, d_c]
   float* lse;                 // [B, T, H] or nullptr
-  float* part_o;              // [B, S, T*H, d_c] when S > 1
+  void* part_o;               // [B, S, T*H, d_c] when S > 1: bf16 if part_bf16, else fp32
   float* part_lse;            // [B, S, T*H]      when S > 1
   int B, T, H, d_c, d_r, block_size;
   int num_blocks, max_blocks;
@@ -24,6 +24,7 @@ struct DecodeParams {
   int num_splits;             // S
   int chunk_rows;             // cache rows per split (a multiple of the kernel granule)
   int xcds;                   // MFMA kernel: XCDs of the device (workgroup placement)
+  int part_bf16;              // partial outputs stored as bf16 (the MFMA kernel's)
   float scale_log2;           // softmax scale * log2(e)
   // Balanced plan (MFMA kernel only): when non-null, num_splits is the number
   // K of work items per 64-row group, split sizes are chosen per sequence on

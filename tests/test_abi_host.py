@@ -117,8 +117,8 @@ def test_workspace_and_split_plan(lib):
     cfg = v3_cfg()
     # one split needs no workspace
     assert mla.mla_decode_workspace_size(cfg, 16, 1, 4097, 0, 1) == 0
-    # S splits of B x T x H rows: d_c floats + one lse each, both rounded up to
-    # 256 B.  The MFMA kernel splits the longest sequence into ranges of whole
+    # S splits of B x T x H rows: d_c bf16 values (the MFMA kernel's partials)
+    # + one fp32 lse each, both rounded up to 256 B.  The MFMA kernel splits the longest sequence into ranges of whole
     # 32-row units, so S is first reduced to the number of ranges that cover it.
     for B, T, cap, S in [(16, 1, 4097, 8), (4, 1, 131073, 64), (32, 4, 8196, 3)]:
         units = -(-cap // 32)
@@ -126,7 +126,7 @@ def test_workspace_and_split_plan(lib):
         s_eff = -(-units // chunk)
         rows = B * s_eff * T * 128
         r256 = lambda x: -(-x // 256) * 256
-        want = r256(rows * 512 * 4) + r256(rows * 4)
+        want = r256(rows * 512 * 2) + r256(rows * 4)
         assert mla.mla_decode_workspace_size(cfg, B, T, cap, 0, S) == want
     # equal lengths (total = B x longest): the library's choice is a plain
     # plan, a valid split count, sized like that count given explicitly
@@ -142,7 +142,7 @@ def test_workspace_and_split_plan(lib):
         K = 256 // (T * 128 // 64)
         assert mla.mla_decode_num_splits(cfg, B, T, 4097, total) == K
         rows = K * T * 128
-        want = r256(rows * 512 * 4) + r256(rows * 4) + r256(B * 16)
+        want = r256(rows * 512 * 2) + r256(rows * 4) + r256(B * 16)
         assert mla.mla_decode_workspace_size(cfg, B, T, 4097, total, 0) == want
     # no more work items than sequences: the plain plan
     assert mla.mla_decode_num_splits(cfg, 200, 1, 4097, 0) <= 129

@@ -117,9 +117,10 @@ def test_balanced_plan_matches_oracle_and_table(name):
     K = 256 // (T * w.H // 64)
     assert K > B and mla.mla_decode_num_splits(cfg, B, T, cap, 0) == K
     o, lse, ws = _run(w, bt, pool_after, seq_lens)
-    # the table in the workspace tail: (P_b, S_b, ch_b) per sequence
+    # the table in the workspace tail, after the bf16 partial outputs and the
+    # fp32 partial log-sum-exps: (P_b, S_b, ch_b) per sequence
     rows = K * T * w.H
-    off = _r256(rows * w.d_c * 4) + _r256(rows * 4)
+    off = _r256(rows * w.d_c * 2) + _r256(rows * 4)
     table = ws[off:off + 16 * B].cpu().numpy().view(np.int32).reshape(B, 4)[:, :3]
     C, P, S, ch = plan_ref(np.minimum(seq_lens, cap), K)
     assert table[:, 0].tolist() == P
