@@ -17,7 +17,9 @@ from typing import Optional
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libmla.so")
+# MLA_LIBRARY names another build of the same library to load instead (the
+# sanitizer build of the host code, for instance)
+LIB_PATH = os.environ.get("MLA_LIBRARY") or os.path.join(_HERE, "libmla.so")
 
 MLA_F32 = 0
 MLA_BF16 = 1

@@ -2,6 +2,13 @@
 
 Sources are compiled in parallel into ``_build/`` and linked into
 ``libmla.so`` next to this file.  Run ``python -m mla_latent_kv_36_amd.build``.
+
+``python -m mla_latent_kv_36_amd.build --sanitize`` builds ``libmla_san.so``
+instead: the same library with the host code of the C ABI (argument checks,
+split planning, workspace sizing) compiled under AddressSanitizer and
+UndefinedBehaviorSanitizer.  Device code is built as usual.  Load it with
+the sanitizer runtime preloaded (``sanitizer_runtime()``) and
+``MLA_LIBRARY`` pointing at it.
 """
 from __future__ import annotations
 
@@ -17,6 +24,11 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libmla.so")
+SAN_LIB = os.path.join(PKG, "libmla_san.so")
+# host-side sanitizers only; each flag applies to the host compilation
+SAN_FLAGS = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+             "-Xarch_host", "-fno-sanitize-recover=all", "-Xarch_host", "-fno-omit-frame-pointer",
+             "-Xarch_host", "-g"]
 SOURCES = ["abi.hip", "decode_mfma.hip", "decode_generic.hip", "projections.hip",
            "cache_ops.hip", "producer.hip", "output_side.hip"]
 ARCH = "gfx950"
@@ -37,9 +49,9 @@ COMMON_FLAGS = [
 ]
 
 
-def _compile(src: str) -> str:
-    obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [hipcc(), *COMMON_FLAGS, f"-I{INCLUDE}", f"-I{CSRC}", "-c",
+def _compile(src: str, extra=(), suffix: str = "") -> str:
+    obj = os.path.join(BUILD, os.path.splitext(src)[0] + suffix + ".o")
+    cmd = [hipcc(), *COMMON_FLAGS, *extra, f"-I{INCLUDE}", f"-I{CSRC}", "-c",
            os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
@@ -63,10 +75,43 @@ def build(verbose: bool = False) -> str:
     return LIB
 
 
+def build_sanitized(verbose: bool = False) -> str:
+    """libmla_san.so: the C ABI's host code (abi.hip) under ASan and UBSan,
+    the kernel sources as usual; returns the library path."""
+    os.makedirs(BUILD, exist_ok=True)
+    with ThreadPoolExecutor(max_workers=min(len(SOURCES), os.cpu_count() or 1)) as ex:
+        objs = list(ex.map(lambda src: _compile(src, SAN_FLAGS, "_san") if src == "abi.hip"
+                           else _compile(src), SOURCES))
+    tmp = SAN_LIB + ".tmp"
+    cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-shared-libasan",
+           "-fsanitize=address,undefined", *objs, "-o", tmp]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
+    os.replace(tmp, SAN_LIB)
+    if verbose:
+        print(f"built {SAN_LIB}")
+    return SAN_LIB
+
+
+def sanitizer_runtime() -> str:
+    """The shared AddressSanitizer runtime (it carries the UBSan handlers) of
+    the compiler that built libmla_san.so, to preload into the host process."""
+    r = subprocess.run([hipcc(), "-print-file-name=libclang_rt.asan-x86_64.so"],
+                       capture_output=True, text=True)
+    path = r.stdout.strip()
+    if r.returncode != 0 or not os.path.isabs(path) or not os.path.exists(path):
+        raise RuntimeError("libclang_rt.asan-x86_64.so not found next to hipcc's clang")
+    return path
+
+
 def built() -> bool:
     return os.path.exists(LIB)
 
 
 if __name__ == "__main__":
-    build(verbose=True)
+    if "--sanitize" in sys.argv[1:]:
+        build_sanitized(verbose=True)
+    else:
+        build(verbose=True)
     sys.exit(0)

@@ -161,10 +161,15 @@ __device__ __forceinline__ void wait_vmcnt() {
 // rows' rescale factors and the group's rescale flag.  Lane l takes row
 // 16 grp + (l & 15) and P k-slots 8 g8 .. +7 (g8 = l >> 4: k-step g8 >> 1,
 // half g8 & 1); the other 24 scores of the row are in lanes l ^ 16, l ^ 32,
-// l ^ 48.  m_run is the row's reference maximum, l_run the sum in that
-// reference.
+// l ^ 48.  m_run is the row's reference maximum; l_lane is this lane's share
+// of the row sum in that reference (the four shares are added once, after
+// the last unit).
+//
+// The reference is raised only when a score exceeds it by more than the
+// slack, so on almost every unit no score does, and neither the row maximum
+// nor any exchange between lanes is needed: the test is one wave-wide vote.
 __device__ __forceinline__ void softmax_unit(Smem& sm, int u, int valid, int grp, int lane,
-                                             float c_log2, float& m_run, float& l_run) {
+                                             float c_log2, float& m_run, float& l_lane) {
   // Scale and subtract stay separate operations, so the maximal score gives
   // exactly exp2(0) = 1.
 #pragma clang fp contract(off)
@@ -186,35 +191,48 @@ __device__ __forceinline__ void softmax_unit(Smem& sm, int u, int valid, int grp
     for (int e = 0; e < 8; ++e)
       if (16 * (g8 >> 1) + tok_of(8 * (g8 & 1) + e) >= valid) x[e] = -INFINITY;
   }
-  float mx = vmax(vmax(vmax(x[0], x[1]), vmax(x[2], x[3])),
-                  vmax(vmax(x[4], x[5]), vmax(x[6], x[7])));
-  mx = xor32_max(xor16_max(mx));
-  const bool raise = mx > m_run + kRescaleSlack;  // always on the first unit
-  const float m_new = raise ? mx : m_run;
-  const float alpha = raise ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.0f;
-  m_run = m_new;
+  // some score of this lane above the reference by more than the slack
+  // (always on the first unit, whose reference is -inf)
+  const float lim = m_run + kRescaleSlack;
+  const bool over = ((x[0] > lim) | (x[1] > lim)) | ((x[2] > lim) | (x[3] > lim)) |
+                    ((x[4] > lim) | (x[5] > lim)) | ((x[6] > lim) | (x[7] > lim));
+  int raised = 0;
+  float alpha = 1.0f;
+  if (__any(over)) {
+    // the rows' maxima; a row whose maximum passes the slack takes it as its
+    // new reference, and its sum and output are scaled by alpha
+    float mx = vmax(vmax(vmax(x[0], x[1]), vmax(x[2], x[3])),
+                    vmax(vmax(x[4], x[5]), vmax(x[6], x[7])));
+    mx = xor32_max(xor16_max(mx));
+    const bool raise = mx > lim;
+    const float m_new = raise ? mx : m_run;
+    alpha = raise ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.0f;
+    m_run = m_new;
+    l_lane = l_lane * alpha;
+    raised = __any(raise) ? 1 : 0;
+  }
   float ex[8];
   u16x8 pb;
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
-    ex[e] = __builtin_amdgcn_exp2f(x[e] - m_new);
+    ex[e] = __builtin_amdgcn_exp2f(x[e] - m_run);
     pb[e] = f32_to_bf16(ex[e]);
   }
-  float sum = ((ex[0] + ex[1]) + (ex[2] + ex[3])) + ((ex[4] + ex[5]) + (ex[6] + ex[7]));
   *reinterpret_cast<u16x8*>(&sm.p[u & 1][srow * P_LD + 8 * g8]) = pb;
-  sum = xor32_sum(xor16_sum(sum));
-  l_run = l_run * alpha + sum;
+  l_lane += ((ex[0] + ex[1]) + (ex[2] + ex[3])) + ((ex[4] + ex[5]) + (ex[6] + ex[7]));
+  // the value waves read the factors of all 64 rows when any group's flag is
+  // set, so every group writes its rows' factors (1 where nothing rose)
   if (g8 == 0) sm.alpha[u & 1][srow] = alpha;
-  const bool any_raise = __any(raise);
-  if (lane == 0) sm.flag[u & 1][grp] = any_raise ? 1 : 0;
+  if (lane == 0) sm.flag[u & 1][grp] = raised;
 }
 
-// After the last unit: the reciprocals of the group's row sums for the
-// normalisation, and the rows' log-sum-exp (natural log) to the output or to
-// the split's partial.
+// After the last unit: the rows' sums (the four lanes' shares added), the
+// reciprocals of those for the normalisation, and the rows' log-sum-exp
+// (natural log) to the output or to the split's partial.
 __device__ __forceinline__ void softmax_finish(Smem& sm, const DecodeParams& p, int grp, int lane,
-                                               float m_run, float l_run, bool direct, int b,
+                                               float m_run, float l_lane, bool direct, int b,
                                                int pidx, int TH, int rb) {
+  const float l_run = xor32_sum(xor16_sum(l_lane));
   if ((lane >> 4) != 0) return;
   const int srow = 16 * grp + (lane & 15);
   sm.lrow[srow] = 1.0f / l_run;
@@ -620,7 +638,7 @@ __global__ __launch_bounds__(NT, 1) void decode_mfma_kernel(const DecodeParams p
       }
     const int poff = l32 * P_LD + 8 * lhi;  // bf16 elements
 
-    float m_run = -INFINITY, l_run = 0.0f;
+    float m_run = -INFINITY, l_lane = 0.0f;  // reference maximum; this lane's share of the row sum
 
     f32x16 o[2][4];
 #pragma unroll
@@ -720,9 +738,9 @@ __global__ __launch_bounds__(NT, 1) void decode_mfma_kernel(const DecodeParams p
       if (pv_first) {
         if (j >= 0) pv(j, next ? j + 1 : -1);
         else if (next) load_v(j + 1);
-        if (next) softmax_unit(sm, j + 1, unit_valid(j + 1), v, lane, p.scale_log2, m_run, l_run);
+        if (next) softmax_unit(sm, j + 1, unit_valid(j + 1), v, lane, p.scale_log2, m_run, l_lane);
       } else {
-        if (next) softmax_unit(sm, j + 1, unit_valid(j + 1), v, lane, p.scale_log2, m_run, l_run);
+        if (next) softmax_unit(sm, j + 1, unit_valid(j + 1), v, lane, p.scale_log2, m_run, l_lane);
         if (j >= 0) pv(j, next ? j + 1 : -1);
         else if (next) load_v(j + 1);
       }
@@ -735,7 +753,7 @@ __global__ __launch_bounds__(NT, 1) void decode_mfma_kernel(const DecodeParams p
       for (int j = -2; j < U; ++j) step(j, std::false_type{});
     }
 
-    softmax_finish(sm, p, v, lane, m_run, l_run, direct, b, pidx, TH, rb);
+    softmax_finish(sm, p, v, lane, m_run, l_lane, direct, b, pidx, TH, rb);
     lds_barrier();                         // F
     // Streaming (non-temporal) stores: the rows are read by the next kernel,
     // not by this one, and lines left dirty in L2 would all be written back
