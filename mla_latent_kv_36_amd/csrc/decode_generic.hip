@@ -12,6 +12,7 @@
 // the Transformer", section "Absorbed projections", point 3).
 #include "common.h"
 #include "launch.h"
+#include "merge.h"
 
 namespace mla {
 namespace {
@@ -133,218 +134,15 @@ __global__ __launch_bounds__(NT) void decode_generic_kernel(const DecodeParams p
   }
 }
 
-// Log-sum-exp merge of the splits of one query row: with M = max_s lse_s and
-// w_s = exp(lse_s - M), o = sum_s w_s o_s / sum_s w_s, lse = M + log sum_s w_s
-// ("Attention, Part 2: MQA, GQA and MLA": the partial results of disjoint row
-// ranges combine exactly through their log-sum-exp).  Only splits that hold
-// rows of this query are read (the same row arithmetic as the split
-// kernels), in split order, so the result is deterministic.  One wave per
-// query row.  The merge streams the partials once, so the loads of a row are
-// issued together, as many as fit, rather than one split at a time.
-// Partials are fp32 (PT = float) or bf16 (PT = uint16_t, d_c = 512 only).
-constexpr int CMB_ROWS = 4;   // query rows (waves) per workgroup
-
-// 8 of a partial row's 512 columns per lane: fp32 partials, columns 4l .. 4l+3
-// and 256 + 4l .. +3 (two 16-byte loads); bf16 partials, columns 8l .. 8l+7
-// (one 16-byte load).  Raw loads first (`raw`), converted after every load of
-// the row is in flight (`lo`, `hi`: the lane's first and last 4 columns).
-template <typename PT> struct Part8;
-template <> struct Part8<float> {
-  struct Raw { f32x4 a, b; };
-  __device__ __forceinline__ static Raw load(const float* row, int lane) {
-    return {*reinterpret_cast<const f32x4*>(row + 4 * lane),
-            *reinterpret_cast<const f32x4*>(row + 256 + 4 * lane)};
-  }
-  __device__ __forceinline__ static void hold(const Raw& r) { asm volatile("" ::"v"(r.a), "v"(r.b)); }
-  __device__ __forceinline__ static f32x4 lo(const Raw& r) { return r.a; }
-  __device__ __forceinline__ static f32x4 hi(const Raw& r) { return r.b; }
-  __device__ __forceinline__ static float* col_lo(float* out, int lane) { return out + 4 * lane; }
-  __device__ __forceinline__ static float* col_hi(float* out, int lane) { return out + 256 + 4 * lane; }
-};
-template <> struct Part8<uint16_t> {
-  using Raw = u16x8;
-  __device__ __forceinline__ static Raw load(const uint16_t* row, int lane) {
-    return *reinterpret_cast<const u16x8*>(row + 8 * lane);
-  }
-  __device__ __forceinline__ static void hold(const Raw& r) { asm volatile("" ::"v"(r)); }
-  __device__ __forceinline__ static f32x4 lo(const Raw& r) {
-    return {bf16_to_f32(r[0]), bf16_to_f32(r[1]), bf16_to_f32(r[2]), bf16_to_f32(r[3])};
-  }
-  __device__ __forceinline__ static f32x4 hi(const Raw& r) {
-    return {bf16_to_f32(r[4]), bf16_to_f32(r[5]), bf16_to_f32(r[6]), bf16_to_f32(r[7])};
-  }
-  __device__ __forceinline__ static float* col_lo(float* out, int lane) { return out + 8 * lane; }
-  __device__ __forceinline__ static float* col_hi(float* out, int lane) { return out + 8 * lane + 4; }
-};
+// One wave per query row, CMB_ROWS rows per workgroup (merge_row).
+constexpr int CMB_ROWS = 4;
 
 template <typename PT>
 __global__ __launch_bounds__(64 * CMB_ROWS) void combine_kernel(const DecodeParams p) {
-  using P8 = Part8<PT>;
-  const int TH = p.T * p.H;
-  const long long nrows = (long long)p.B * TH;
+  const long long nrows = (long long)p.B * p.T * p.H;
   const long long row = (long long)blockIdx.x * CMB_ROWS + (threadIdx.x >> 6);
   if (row >= nrows) return;
-  const int lane = threadIdx.x & 63;
-  const int b = (int)(row / TH);
-  const int rr = (int)(row - (long long)b * TH);
-  const int t = rr / p.H;
-  // this sequence's splits: the first one's partial index, their count and
-  // the cache rows per split (a balanced plan: from the table the decode
-  // kernel wrote; the plain plan: the same for every sequence)
-  int P0, S, chunk;
-  if (p.plan != nullptr) {
-    const int4 e = *reinterpret_cast<const int4*>(p.plan + 4 * (size_t)b);
-    P0 = __builtin_amdgcn_readfirstlane(e.x);
-    S = __builtin_amdgcn_readfirstlane(e.y);
-    chunk = __builtin_amdgcn_readfirstlane(e.z) * 32;
-    if (S == 0) {  // no visible row in the sequence: o = 0, lse = -inf
-      float* out = p.o_lat + (size_t)row * p.d_c;
-      for (int d = lane; d < p.d_c; d += 64) out[d] = 0.0f;
-      if (lane == 0 && p.lse != nullptr) p.lse[row] = -INFINITY;
-      return;
-    }
-  } else {
-    P0 = b * p.num_splits;
-    S = p.num_splits;
-    chunk = p.chunk_rows;
-  }
-  const PT* part = static_cast<const PT*>(p.part_o);
-  const float* lse_b = p.part_lse + (size_t)P0 * TH + rr;
-  if (S <= 8 && p.d_c == 512) {
-    // The common shape in one memory round trip: the sequence length, every
-    // split's log-sum-exp (lane s) and every split's partial row (8 columns
-    // per lane) are read before any of them is used.  Splits that hold no row
-    // of this query were never written; they are left out by selection, not
-    // by a zero weight, since their memory may hold anything.
-    const PT* po_b = part + ((size_t)P0 * TH + rr) * 512;
-    const size_t sstride = (size_t)TH * 512;
-    const int len = p.seq_lens[b];
-    const float lse_l = lse_b[(size_t)min(lane, S - 1) * TH];
-    typename P8::Raw v[8];
-#pragma unroll
-    for (int k = 0; k < 8; ++k) v[k] = P8::load(po_b + (size_t)min(k, S - 1) * sstride, lane);
-    // every value above is consumed here, so all the loads are issued before
-    // the first wait (the compiler would otherwise interleave waits and loads)
-    __builtin_amdgcn_sched_barrier(0);
-    asm volatile("" ::"v"(len), "v"(lse_l));
-#pragma unroll
-    for (int k = 0; k < 8; ++k) P8::hold(v[k]);
-    const int n_valid = visible_rows(len, p.T, t, p.causal, p.cap);
-    const int ns = __builtin_amdgcn_readfirstlane(min(S, (n_valid + chunk - 1) / chunk));
-    // no branches from here on: a branch would let the compiler move the
-    // loads above behind it, one dependent round trip at a time
-    float M = lane < ns ? lse_l : -INFINITY;
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
-    const float e = lane < ns ? exp2f((lse_l - M) * kLog2e) : 0.0f;
-    float den = e;
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) den += __shfl_xor(den, off);
-    f32x4 a0 = {0.f, 0.f, 0.f, 0.f}, a1 = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      const float w = __shfl(e, k);
-      const f32x4 t0 = a0 + w * P8::lo(v[k]), t1 = a1 + w * P8::hi(v[k]);
-      a0 = k < ns ? t0 : a0;
-      a1 = k < ns ? t1 : a1;
-    }
-    // no visible row (ns == 0): o = 0, lse = -inf
-    const float inv = ns > 0 ? 1.0f / den : 0.0f;
-    // streaming stores: o_lat is read by the next kernel (no L2 lines left
-    // dirty for the end-of-launch write-back)
-    float* out = p.o_lat + (size_t)row * 512;
-    __builtin_nontemporal_store(a0 * inv, reinterpret_cast<f32x4*>(P8::col_lo(out, lane)));
-    __builtin_nontemporal_store(a1 * inv, reinterpret_cast<f32x4*>(P8::col_hi(out, lane)));
-    if (lane == 0 && p.lse != nullptr) p.lse[row] = ns > 0 ? M + logf(den) : -INFINITY;
-    return;
-  }
-  const int n_valid = visible_rows(p.seq_lens[b], p.T, t, p.causal, p.cap);
-  // one row per wave: the split count is the same in every lane
-  const int ns = __builtin_amdgcn_readfirstlane(min(S, (n_valid + chunk - 1) / chunk));
-  float* out = p.o_lat + (size_t)row * p.d_c;
-  const PT* po_b = part + ((size_t)P0 * TH + rr) * p.d_c;
-  const size_t sstride = (size_t)TH * p.d_c;  // elements between splits of one row
-
-  if (ns <= 0) {
-    for (int d = lane; d < p.d_c; d += 64) out[d] = 0.0f;
-    if (lane == 0 && p.lse != nullptr) p.lse[row] = -INFINITY;
-    return;
-  }
-  // split s's log-sum-exp is read by lane s % 64 (all loads of a pass in
-  // flight at once), then reduced across the wave in a fixed order
-  float M = -INFINITY;
-  for (int c = 0; c < ns; c += 64)
-    if (c + lane < ns) M = fmaxf(M, lse_b[(size_t)(c + lane) * TH]);
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
-  float den = 0.0f;
-  for (int c = 0; c < ns; c += 64)
-    if (c + lane < ns) den += exp2f((lse_b[(size_t)(c + lane) * TH] - M) * kLog2e);
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) den += __shfl_xor(den, off);
-  const float inv = 1.0f / den;
-
-  if ((p.d_c & 511) == 0) {
-    // 512 columns per pass, 8 per lane; the loads of up to 8 splits are all
-    // issued before the first is used, so that enough bytes are in flight to
-    // stream the partials at memory speed
-    for (int d0 = 0; d0 < p.d_c; d0 += 512) {
-      f32x4 a0 = {0.f, 0.f, 0.f, 0.f}, a1 = {0.f, 0.f, 0.f, 0.f};
-      for (int s0 = 0; s0 < ns; s0 += 8) {
-        // splits past the last one re-read the last one with weight 0, so
-        // that every load is unconditional
-        float w[8];
-#pragma unroll
-        for (int k = 0; k < 8; ++k) {
-          const float e = exp2f((lse_b[(size_t)min(s0 + k, ns - 1) * TH] - M) * kLog2e);
-          w[k] = s0 + k < ns ? e : 0.0f;
-        }
-        typename P8::Raw v[8];
-#pragma unroll
-        for (int k = 0; k < 8; ++k)
-          v[k] = P8::load(po_b + (size_t)min(s0 + k, ns - 1) * sstride + d0, lane);
-#pragma unroll
-        for (int k = 0; k < 8; ++k) {
-          a0 += w[k] * P8::lo(v[k]);
-          a1 += w[k] * P8::hi(v[k]);
-        }
-      }
-      *reinterpret_cast<f32x4*>(P8::col_lo(out + d0, lane)) = a0 * inv;
-      *reinterpret_cast<f32x4*>(P8::col_hi(out + d0, lane)) = a1 * inv;
-    }
-  } else if constexpr (sizeof(PT) == 4) {
-    const float* pf = reinterpret_cast<const float*>(po_b);
-    if ((p.d_c & 3) == 0) {
-      for (int d = 4 * lane; d < p.d_c; d += 256) {
-        f32x4 a = {0.f, 0.f, 0.f, 0.f};
-        int s = 0;
-        for (; s + 4 <= ns; s += 4) {  // four splits' loads in flight at a time
-          f32x4 v[4];
-          float w[4];
-#pragma unroll
-          for (int k = 0; k < 4; ++k) {
-            v[k] = *reinterpret_cast<const f32x4*>(pf + (size_t)(s + k) * sstride + d);
-            w[k] = exp2f((lse_b[(size_t)(s + k) * TH] - M) * kLog2e);
-          }
-#pragma unroll
-          for (int k = 0; k < 4; ++k) a += w[k] * v[k];
-        }
-        for (; s < ns; ++s) {
-          const f32x4 v = *reinterpret_cast<const f32x4*>(pf + (size_t)s * sstride + d);
-          a += exp2f((lse_b[(size_t)s * TH] - M) * kLog2e) * v;
-        }
-        *reinterpret_cast<f32x4*>(out + d) = a * inv;
-      }
-    } else {
-      for (int d = lane; d < p.d_c; d += 64) {
-        float a = 0.0f;
-        for (int s = 0; s < ns; ++s)
-          a += exp2f((lse_b[(size_t)s * TH] - M) * kLog2e) * pf[(size_t)s * sstride + d];
-        out[d] = a * inv;
-      }
-    }
-  }
-  if (lane == 0 && p.lse != nullptr) p.lse[row] = M + logf(den);
+  merge_row<PT>(p, row, threadIdx.x & 63);
 }
 
 }  // namespace
