@@ -34,6 +34,7 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16
 # used only while these files are unchanged.
 DECODE_SOURCES = ("mla_latent_kv_36_amd/csrc/decode_mfma.hip",
                   "mla_latent_kv_36_amd/csrc/decode_generic.hip",
+                  "mla_latent_kv_36_amd/csrc/merge.h",
                   "mla_latent_kv_36_amd/csrc/common.h",
                   "mla_latent_kv_36_amd/csrc/launch.h",
                   "mla_latent_kv_36_amd/csrc/abi.hip")
