@@ -159,7 +159,9 @@ constexpr int OP_KS = 16;         // at most 16 k-steps of 32: d_c <= 512
 // append of a decode step rides along with the absorb: one launch less).
 // They come first in dispatch order so that their chain of dependent loads
 // (length, page id, row) runs under the absorb rather than after it.
-template <int NKS>  // k-steps of 32 covering d_nope: ceil(d_nope / 32)
+// NKS: k-steps of 32 covering d_nope (ceil(d_nope / 32)); NT: 16-row tiles per
+// workgroup (mt / 16), whose query fragments are all requested at the start.
+template <int NKS, int NT>
 __global__ __launch_bounds__(PJ_NT) void absorb_q_mfma_kernel(
     const uint16_t* __restrict__ q_nope, const uint16_t* __restrict__ q_rope,
     const uint16_t* __restrict__ w_uk, uint16_t* __restrict__ q_abs, int M, int H, int d_n,
@@ -192,8 +194,9 @@ __global__ __launch_bounds__(PJ_NT) void absorb_q_mfma_kernel(
   constexpr int nks = NKS;
   const int W = d_c + d_r;
 
-  // B fragments (query rows) of the first tile are requested before the
-  // weight, so both loads are in flight together.
+  // B fragments (query rows) of every tile are requested before the weight,
+  // so that all of the workgroup's loads are in flight together: one memory
+  // latency per workgroup, not one per tile.
   // The loads are unconditional, on a clamped row and offset, and nothing is
   // selected on the loaded values (a select, like a conditional load, makes
   // the compiler wait for the load at once): rows past mend feed outputs that
@@ -204,8 +207,9 @@ __global__ __launch_bounds__(PJ_NT) void absorb_q_mfma_kernel(
 #pragma unroll
     for (int ks = 0; ks < nks; ++ks) bq[ks] = load_bf16x8(qrow + min(32 * ks + 8 * g, d_n - 8));
   };
-  bf16x8 bq[AB_KS];
-  load_q(mbeg, bq);
+  bf16x8 bq[NT][AB_KS];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) load_q(mbeg + 16 * t, bq[t]);  // rows past mend: clamped
 
   // the weight slice: every piece is loaded (unconditional) before the first
   // is stored, so staging costs one memory latency; nks * 32 rows of 16
@@ -247,14 +251,14 @@ __global__ __launch_bounds__(PJ_NT) void absorb_q_mfma_kernel(
     }
 
   const int col0 = cb * AB_CT + 32 * wave + 4 * g;  // + 16 ct: this lane's 4 columns
-  // one 16-row tile whose query fragments are in bq
-  auto tile = [&](int m0) __attribute__((always_inline)) {
+  // one 16-row tile whose query fragments are in q
+  auto tile = [&](int m0, const bf16x8 (&q)[AB_KS]) __attribute__((always_inline)) {
     const int m = m0 + i16;
     f32x4 acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
     for (int ks = 0; ks < nks; ++ks) {
-      acc[0] = mfma16(a[0][ks], bq[ks], acc[0]);
-      acc[1] = mfma16(a[1][ks], bq[ks], acc[1]);
+      acc[0] = mfma16(a[0][ks], q[ks], acc[0]);
+      acc[1] = mfma16(a[1][ks], q[ks], acc[1]);
     }
     if (m < mend) {
       uint16_t* dst = q_abs + ((size_t)m * H + h) * W + col0;
@@ -262,13 +266,9 @@ __global__ __launch_bounds__(PJ_NT) void absorb_q_mfma_kernel(
       store_bf16x4(dst + 16, acc[1]);
     }
   };
-  // the first tile as straight-line code: in a loop, the compiler moves its
-  // query loads down to their use, behind the staging and its barrier
-  tile(mbeg);
-  for (int m0 = mbeg + 16; m0 < mend; m0 += 16) {
-    load_q(m0, bq);
-    tile(m0);
-  }
+#pragma unroll
+  for (int t = 0; t < NT; ++t)
+    if (mbeg + 16 * t < mend) tile(mbeg + 16 * t, bq[t]);
 
   if (cb == 0) {  // the rotary part is carried over unchanged, 16 bytes at a time
     const int chunks = d_r / 8;
@@ -352,6 +352,9 @@ __global__ __launch_bounds__(PJ_NT) void out_proj_mfma_kernel(
       *reinterpret_cast<u16x4*>(st[0] + r * OP_LD + 8 * c4) = hb;
       *reinterpret_cast<u16x4*>(st[1] + r * OP_LD + 8 * c4) = lb;
     }
+    // the next tile's o_lat is requested now, so that its load runs under
+    // this tile's MFMAs
+    if (m0 + 16 < mend) load_x(m0 + 16);
     __syncthreads();
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
     const int boff = i16 * OP_LD + 16 * g;
@@ -380,10 +383,7 @@ __global__ __launch_bounds__(PJ_NT) void out_proj_mfma_kernel(
   // The first tile is straight-line code: at a loop head the compiler would
   // wait for the weight as well before staging it.
   tile(mbeg);
-  for (int m0 = mbeg + 16; m0 < mend; m0 += 16) {
-    load_x(m0);
-    tile(m0);
-  }
+  for (int m0 = mbeg + 16; m0 < mend; m0 += 16) tile(m0);
 }
 
 // absorb_q_mfma_kernel for ceil(d_n / 32) k-steps (1 .. AB_KS)
@@ -391,9 +391,16 @@ hipError_t launch_absorb_kernel(dim3 grid, size_t shmem, hipStream_t stream,
                                 const uint16_t* q_nope, const uint16_t* q_rope,
                                 const uint16_t* w_uk, uint16_t* q_abs, int M, int H, int d_n,
                                 int d_c, int d_r, int mt, const AppendArgs& ap) {
-#define AB_LAUNCH(K)                                                                     \
-  hipLaunchKernelGGL(absorb_q_mfma_kernel<K>, grid, dim3(PJ_NT), shmem, stream, q_nope, \
+#define AB_LAUNCH_T(K, T)                                                                  \
+  hipLaunchKernelGGL((absorb_q_mfma_kernel<K, T>), grid, dim3(PJ_NT), shmem, stream, q_nope, \
                      q_rope, w_uk, q_abs, M, H, d_n, d_c, d_r, mt, ap)
+#define AB_LAUNCH(K)                      \
+  do {                                    \
+    if (mt <= 16) AB_LAUNCH_T(K, 1);      \
+    else if (mt <= 32) AB_LAUNCH_T(K, 2); \
+    else AB_LAUNCH_T(K, 4);               \
+  } while (0)
+  if (mt > PJ_MW) return hipErrorInvalidValue;
   switch ((d_n + 31) >> 5) {
     case 1: AB_LAUNCH(1); break;
     case 2: AB_LAUNCH(2); break;
@@ -404,6 +411,7 @@ hipError_t launch_absorb_kernel(dim3 grid, size_t shmem, hipStream_t stream,
     default: return hipErrorInvalidValue;
   }
 #undef AB_LAUNCH
+#undef AB_LAUNCH_T
   return hipGetLastError();
 }
 
