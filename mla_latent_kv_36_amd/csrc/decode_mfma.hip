@@ -24,12 +24,15 @@
 //     registers (144 VGPRs, the B operand of v_mfma_f32_16x16x32_bf16), reads
 //     K fragments from LDS, and reads the unit's rotary key columns straight
 //     from memory into registers one unit ahead;
-//   copy waves 4, 5 (on the score waves' SIMDs): the copies;
+//   copy waves 4, 5 (on the score waves' SIMDs): the softmax of rows 32..47
+//     and 48..63, then the copies;
 //   value waves 2, 3, 6, 7: wave v owns latent columns 128v..128v+127 of O for
-//     all 64 rows (128 VGPRs, v_mfma_f32_32x32x16_bf16), reads V with the
-//     transposing LDS read (ds_read_b64_tr_b16), and runs the softmax of rows
-//     16v..16v+15.  The two value waves of a SIMD take softmax and P.V in
-//     opposite orders, so that one's VALU work meets the other's MFMAs.
+//     all 64 rows (128 VGPRs, v_mfma_f32_32x32x16_bf16) and reads V with the
+//     transposing LDS read (ds_read_b64_tr_b16); waves 2 and 3 also run the
+//     softmax of rows 0..15 and 16..31, before their P.V.
+// Each SIMD thus carries MFMAs (score or P.V) and the VALU work of one 16-row
+// softmax: with one wave's VALU work slowed by another's MFMAs on the same
+// SIMD, the four SIMDs then take about the same time per unit.
 // A row's reference maximum is only raised when a unit's maximum exceeds it by
 // more than 2^8, so the accumulator rescale is skipped on almost every unit;
 // probabilities then stay below 2^8, which bf16 and the fp32 sums carry with
@@ -602,8 +605,17 @@ __global__ __launch_bounds__(NT, 1) void decode_mfma_kernel(const DecodeParams p
     if (U > 1) issue(1, page_raw(1));
     int raw_next = page_raw(2);
     if (U > 1) wait_vmcnt<COPIES>(); else wait_vmcnt<0>();  // unit 0 landed
+    // The copy waves also run the online softmax of query rows 32 .. 63 (16
+    // rows each), first in each step: its VALU work then shares a SIMD with a
+    // score wave's MFMAs instead of a value wave's, which balances the four
+    // SIMDs.  Copies of the next unit are issued after it; they have two
+    // steps to land.
+    const int grp = 2 + c;
+    float m_run = -INFINITY, l_lane = 0.0f;  // reference maximum; this lane's share of the row sum
     lds_barrier();                         // B0
     for (int j = -2; j < U; ++j) {
+      if (j + 1 >= 0 && j + 1 < U)
+        softmax_unit(sm, j + 1, unit_valid(j + 1), grp, lane, p.scale_log2, m_run, l_lane);
       if (j + 4 < U) {
         issue(j + 4, raw_next);
         raw_next = page_raw(j + 5);
@@ -615,6 +627,7 @@ __global__ __launch_bounds__(NT, 1) void decode_mfma_kernel(const DecodeParams p
       }
       lds_barrier();                       // E(j)
     }
+    softmax_finish(sm, p, grp, lane, m_run, l_lane, direct, b, pidx, TH, rb);
     lds_barrier();                         // F
   } else {
     // =============================== value waves ===============================
@@ -735,10 +748,9 @@ __global__ __launch_bounds__(NT, 1) void decode_mfma_kernel(const DecodeParams p
     auto step = [&](int j, auto pv_first) __attribute__((always_inline)) {
       const bool next = j + 1 >= 0 && j + 1 < U;
       if (j >= 0) read_p(j);
-      if (pv_first) {
+      if (pv_first) {  // the waves whose softmax rows the copy waves run
         if (j >= 0) pv(j, next ? j + 1 : -1);
         else if (next) load_v(j + 1);
-        if (next) softmax_unit(sm, j + 1, unit_valid(j + 1), v, lane, p.scale_log2, m_run, l_lane);
       } else {
         if (next) softmax_unit(sm, j + 1, unit_valid(j + 1), v, lane, p.scale_log2, m_run, l_lane);
         if (j >= 0) pv(j, next ? j + 1 : -1);
@@ -753,7 +765,7 @@ __global__ __launch_bounds__(NT, 1) void decode_mfma_kernel(const DecodeParams p
       for (int j = -2; j < U; ++j) step(j, std::false_type{});
     }
 
-    softmax_finish(sm, p, v, lane, m_run, l_lane, direct, b, pidx, TH, rb);
+    if (v < 2) softmax_finish(sm, p, v, lane, m_run, l_lane, direct, b, pidx, TH, rb);
     lds_barrier();                         // F
     // Streaming (non-temporal) stores: the rows are read by the next kernel,
     // not by this one, and lines left dirty in L2 would all be written back
