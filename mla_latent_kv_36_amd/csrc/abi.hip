@@ -573,7 +573,8 @@ extern "C" mla_status mla_kv_produce(const mla_config* cfg, const void* hidden, 
   return hip_status(mla::launch_kv_produce(
       cfg->dtype, hidden, d_model, w_dkv, w_kr, base, static_cast<float*>(workspace), ks, pool,
       num_blocks, block_table, max_blocks, seq_lens, B, T_new, cfg->block_size, cfg->d_c,
-      cfg->d_rope, static_cast<hipStream_t>(stream)));
+      cfg->d_rope, device_shape(static_cast<hipStream_t>(stream), true).xcds,
+      static_cast<hipStream_t>(stream)));
 }
 
 extern "C" mla_status mla_rope(const mla_config* cfg, void* x, int32_t heads,
@@ -632,8 +633,9 @@ mla_status output_call(const mla_config* cfg, bool folded, const void* x, const 
     return MLA_ERR_WORKSPACE;
   // the latent outputs are fp32; so are the per-head outputs of an fp32 configuration
   const bool x_f32 = folded || cfg->dtype == MLA_F32;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
   return hip_status(mla::launch_wo_gemm(cfg->dtype, x_f32, x, w, y, static_cast<float*>(workspace),
-                                        ks, M, d_model, K, static_cast<hipStream_t>(stream)));
+                                        ks, M, d_model, K, device_shape(s, true).xcds, s));
 }
 }  // namespace
 

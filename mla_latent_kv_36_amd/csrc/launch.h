@@ -81,18 +81,20 @@ hipError_t launch_kv_produce(int dtype, const void* hidden, int d_model, const v
                              const void* w_kr, float rope_base, float* part, int ksplit,
                              void* pool, int num_blocks, const int32_t* block_table,
                              int max_blocks, const int32_t* seq_lens, int B, int T_new,
-                             int block_size, int d_c, int d_r, hipStream_t stream);
+                             int block_size, int d_c, int d_r, int xcds, hipStream_t stream);
 hipError_t launch_rope(int dtype, void* x, const int32_t* positions, int M, int heads, int d_r,
                        float rope_base, hipStream_t stream);
 // The output side (output_side.hip): y[M, N] = x[M, K] . w[N, K]^T with x bf16
 // (or fp32 when x_f32) and w, y of dtype; k split over ksplit workgroups whose
 // fp32 partial sums (part: ksplit * M * N floats when ksplit > 1) are added
 // in split order.  wo_gemm_ksplit gives the split for a target workgroup
-// count (1 for the generic kernel).
+// count (1 for the generic kernel).  xcds: the device's XCD count (workgroup
+// placement).
 bool wo_gemm_mfma_supported(int dtype, int N, int K);
 int wo_gemm_ksplit(int dtype, int M, int N, int K, int target_workgroups);
 hipError_t launch_wo_gemm(int dtype, bool x_f32, const void* x, const void* w, void* y,
-                          float* part, int ksplit, int M, int N, int K, hipStream_t stream);
+                          float* part, int ksplit, int M, int N, int K, int xcds,
+                          hipStream_t stream);
 // w_fold[d, H * d_c] from w_uv[H, d_v, d_c] and w_o[d, H * d_v] (d_v <= 256).
 bool fold_uv_o_supported(int d_v);
 hipError_t launch_fold_uv_o(int dtype, const void* w_uv, const void* w_o, void* w_fold, int H,

@@ -78,17 +78,18 @@ __device__ __forceinline__ uint4 load_piece(const float* p) {
 template <typename XE>
 __global__ __launch_bounds__(256, 2) void wo_gemm_mfma_kernel(
     const XE* __restrict__ x, const uint16_t* __restrict__ w, uint16_t* __restrict__ y,
-    float* __restrict__ part, int M, int N, int K, int steps_per_split) {
+    float* __restrict__ part, int M, int N, int K, int steps_per_split, int xcds) {
   __shared__ __align__(16) uint16_t sx[WO_TM * WO_LD];
   __shared__ __align__(16) uint16_t sw[WO_TN * WO_LD];
-  // Workgroup i runs on XCD i % 8.  XCD x takes a contiguous block of the
-  // tile numbers (ids past the last full set of 8 keep the plain order).
+  // Workgroup i runs on XCD i % xcds (queried on the host).  XCD x takes a
+  // contiguous block of the tile numbers (ids past the last full set of xcds
+  // keep the plain order).
   const int ntm = (M + WO_TM - 1) / WO_TM;
   const int ntn = (N + WO_TN - 1) / WO_TN;
   const int total = (int)gridDim.x;
-  const int full = total - total % 8;
+  const int full = total - total % xcds;
   const int i = blockIdx.x;
-  const int t = i < full ? (i % 8) * (full / 8) + i / 8 : i;
+  const int t = i < full ? (i % xcds) * (full / xcds) + i / xcds : i;
   const int m0 = (t % ntm) * WO_TM;
   const int n0 = ((t / ntm) % ntn) * WO_TN;
   const int z = t / (ntm * ntn);
@@ -182,12 +183,12 @@ __global__ __launch_bounds__(256, 2) void wo_gemm_mfma_kernel(
 template <typename XE>
 __global__ __launch_bounds__(WO_NT) void wo_stream_direct_kernel(
     const XE* __restrict__ x, const uint16_t* __restrict__ w, uint16_t* __restrict__ y,
-    float* __restrict__ part, int M, int N, int K, int steps_per_split) {
+    float* __restrict__ part, int M, int N, int K, int steps_per_split, int xcds) {
   const int ntn = (N + WO_TN - 1) / WO_TN;
   const int total = (int)gridDim.x;
-  const int full = total - total % 8;
+  const int full = total - total % xcds;
   const int i = blockIdx.x;
-  const int t = i < full ? (i % 8) * (full / 8) + i / 8 : i;
+  const int t = i < full ? (i % xcds) * (full / xcds) + i / xcds : i;
   const int n0 = (t % ntn) * WO_TN;
   const int z = t / ntn;
   const int nk = K / 32;
@@ -354,8 +355,10 @@ int wo_gemm_ksplit(int dtype, int M, int N, int K, int target_workgroups) {
 }
 
 hipError_t launch_wo_gemm(int dtype, bool x_f32, const void* x, const void* w, void* y,
-                          float* part, int ksplit, int M, int N, int K, hipStream_t stream) {
+                          float* part, int ksplit, int M, int N, int K, int xcds,
+                          hipStream_t stream) {
   if (M <= 0 || N <= 0) return hipSuccess;
+  if (xcds < 1) xcds = 1;
   if (wo_gemm_mfma_supported(dtype, N, K) && M <= 16) {
     const int nk = K / 32;
     if (ksplit != (nk + 4 * WO_DC - 1) / (4 * WO_DC)) return hipErrorInvalidValue;
@@ -366,11 +369,11 @@ hipError_t launch_wo_gemm(int dtype, bool x_f32, const void* x, const void* w, v
     if (x_f32)
       hipLaunchKernelGGL(wo_stream_direct_kernel<float>, dim3((unsigned)tiles), dim3(WO_NT), 0,
                          stream, static_cast<const float*>(x), static_cast<const uint16_t*>(w),
-                         yd, part, M, N, K, 4 * WO_DC);
+                         yd, part, M, N, K, 4 * WO_DC, xcds);
     else
       hipLaunchKernelGGL(wo_stream_direct_kernel<uint16_t>, dim3((unsigned)tiles), dim3(WO_NT), 0,
                          stream, static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(w),
-                         yd, part, M, N, K, 4 * WO_DC);
+                         yd, part, M, N, K, 4 * WO_DC, xcds);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || ksplit == 1) return e;
     const size_t quads = (size_t)M * N / 4;
@@ -389,11 +392,11 @@ hipError_t launch_wo_gemm(int dtype, bool x_f32, const void* x, const void* w, v
     if (x_f32)
       hipLaunchKernelGGL(wo_gemm_mfma_kernel<float>, dim3((unsigned)tiles), dim3(256), 0, stream,
                          static_cast<const float*>(x), static_cast<const uint16_t*>(w), yd, part,
-                         M, N, K, per);
+                         M, N, K, per, xcds);
     else
       hipLaunchKernelGGL(wo_gemm_mfma_kernel<uint16_t>, dim3((unsigned)tiles), dim3(256), 0,
                          stream, static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(w),
-                         yd, part, M, N, K, per);
+                         yd, part, M, N, K, per, xcds);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || ksplit == 1) return e;
     const size_t quads = (size_t)M * N / 4;

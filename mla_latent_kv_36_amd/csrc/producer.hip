@@ -51,22 +51,23 @@ __device__ __forceinline__ f32x4 mfma16(const bf16x8& a, const bf16x8& b, const 
 __global__ __launch_bounds__(256) void kv_proj_mfma_kernel(
     const uint16_t* __restrict__ hidden, const uint16_t* __restrict__ w_dkv,
     const uint16_t* __restrict__ w_kr, float* __restrict__ part, int M, int d, int d_c,
-    int d_r, int steps_per_split) {
+    int d_r, int steps_per_split, int xcds) {
   __shared__ __align__(16) uint16_t sa[PJ_TM * PJ_LD];
   __shared__ __align__(16) uint16_t sb[PJ_TN * PJ_LD];
   const int N = d_c + d_r;
-  // Workgroup i runs on XCD i % 8, and each XCD has its own L2.  Tiles are
+  // Workgroup i runs on XCD i % xcds (queried on the host), and each XCD has
+  // its own L2.  Tiles are
   // numbered column tile fastest, then token tile, then k split, and XCD x
   // takes a contiguous block of them: the hidden-vector slice of a (token
   // tile, split) and the weight slice of a (column tile, split) then come
   // from memory once per XCD and from its L2 for the other tiles that read
-  // them.  Ids past the last full set of 8 keep the plain order.
+  // them.  Ids past the last full set of xcds keep the plain order.
   const int ntn = (N + PJ_TN - 1) / PJ_TN;
   const int ntm = (M + PJ_TM - 1) / PJ_TM;
   const int total = (int)gridDim.x;
-  const int full = total - total % 8;
+  const int full = total - total % xcds;
   const int i = blockIdx.x;
-  const int t = i < full ? (i % 8) * (full / 8) + i / 8 : i;
+  const int t = i < full ? (i % xcds) * (full / xcds) + i / xcds : i;
   const int n0 = (t % ntn) * PJ_TN;
   const int m0 = ((t / ntn) % ntm) * PJ_TM;
   const int z = t / (ntn * ntm);
@@ -277,7 +278,7 @@ hipError_t launch_kv_produce(int dtype, const void* hidden, int d_model, const v
                              const void* w_kr, float rope_base, float* part, int ksplit,
                              void* pool, int num_blocks, const int32_t* block_table,
                              int max_blocks, const int32_t* seq_lens, int B, int T_new,
-                             int block_size, int d_c, int d_r, hipStream_t stream) {
+                             int block_size, int d_c, int d_r, int xcds, hipStream_t stream) {
   const int M = B * T_new;
   const int N = d_c + d_r;
   if (M <= 0) return hipSuccess;
@@ -289,7 +290,8 @@ hipError_t launch_kv_produce(int dtype, const void* hidden, int d_model, const v
     if (tiles > 0x7fffffffLL) return hipErrorInvalidValue;
     hipLaunchKernelGGL(kv_proj_mfma_kernel, dim3((unsigned)tiles), dim3(256), 0, stream,
                        static_cast<const uint16_t*>(hidden), static_cast<const uint16_t*>(w_dkv),
-                       static_cast<const uint16_t*>(w_kr), part, M, d_model, d_c, d_r, per);
+                       static_cast<const uint16_t*>(w_kr), part, M, d_model, d_c, d_r, per,
+                       xcds < 1 ? 1 : xcds);
   } else {
     if (ksplit != 1) return hipErrorInvalidValue;
     const dim3 grid((N + 255) / 256, M);
