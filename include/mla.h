@@ -145,7 +145,7 @@ mla_status mla_absorb_q_append(const mla_config* cfg, const void* q_nope, const 
  *    rows of every sequence are cut at the same points into `num_splits`
  *    contiguous ranges of equal size (the last may be shorter or empty);
  *  - balanced (the library's choice for the bf16 kernel with d_c = 512,
- *    d_rope = 64, 64-row pages, H a multiple of 64, when the lengths may
+ *    d_rope = 64 and 64-row pages, when the lengths may
  *    differ: total_tokens_host is 0 or below B x max_seq_len_host): K work
  *    items per 64-row query group (one per compute unit over the grid), and
  *    each sequence gets splits in proportion to its length, chosen on the

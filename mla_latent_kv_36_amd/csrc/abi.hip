@@ -84,7 +84,8 @@ struct Plan {
 
 int granule(const mla_config* c, int T) { return use_mfma(c, T) ? 32 : c->block_size; }
 
-int64_t groups_of(const mla_config* c, int T) { return (int64_t)T * c->n_heads / 64; }
+// 64-row query groups of the MFMA kernel: ceil(H / 64) per new token
+int64_t groups_of(const mla_config* c, int T) { return (int64_t)T * ((c->n_heads + 63) / 64); }
 
 // MFMA kernel, plain plan: units of work are (64-row query group, 32-row unit
 // of the cache).  The kernel's LDS ring fits one workgroup per compute unit,

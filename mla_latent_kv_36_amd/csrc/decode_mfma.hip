@@ -234,12 +234,13 @@ __device__ __forceinline__ void softmax_unit(Smem& sm, int u, int valid, int grp
 // (natural log) to the output or to the split's partial.
 __device__ __forceinline__ void softmax_finish(Smem& sm, const DecodeParams& p, int grp, int lane,
                                                float m_run, float l_lane, bool direct, int b,
-                                               int pidx, int TH, int rb) {
+                                               int pidx, int TH, int rb, int rows_here) {
   const float l_run = xor32_sum(xor16_sum(l_lane));
   if ((lane >> 4) != 0) return;
   const int srow = 16 * grp + (lane & 15);
   sm.lrow[srow] = 1.0f / l_run;
   const float lse = (m_run + log2f(l_run)) * kLn2;
+  if (srow >= rows_here) return;  // past the token's last head: not stored
   if (direct) {
     if (p.lse != nullptr) p.lse[(size_t)b * TH + rb + srow] = lse;
   } else {
@@ -343,7 +344,10 @@ __global__ __launch_bounds__(NT, 1) void decode_mfma_kernel(const DecodeParams p
   const int l32 = lane & 31;
   const int lhi = lane >> 5;
 
-  const int G = (p.T * p.H) / ROWS;
+  // 64-row groups: ceil(H / 64) per new token, the last one partial when H
+  // is not a multiple of 64
+  const int gpt = (p.H + ROWS - 1) / ROWS;
+  const int G = p.T * gpt;
   const int S = p.num_splits;
   // Workgroup i is dispatched to XCD i % X (X XCDs, queried on the host), and
   // each XCD has its own L2.  XCD x gets a contiguous block of (sequence,
@@ -391,8 +395,9 @@ __global__ __launch_bounds__(NT, 1) void decode_mfma_kernel(const DecodeParams p
   }
 
   const int TH = p.T * p.H;
-  const int rb = g * ROWS;  // first query row (t*H + h) of the group
-  const int t = rb / p.H;
+  const int t = g / gpt;                                   // the group's new token
+  const int rb = t * p.H + (g - t * gpt) * ROWS;           // its first query row (t*H + h)
+  const int rows_here = min(ROWS, (t + 1) * p.H - rb);     // 64, or fewer in a token's last group
   // the same for the whole workgroup: kept in scalar registers, so that the
   // range bounds, loop counts and page addresses below are scalar as well
   const int n_valid =
@@ -406,8 +411,8 @@ __global__ __launch_bounds__(NT, 1) void decode_mfma_kernel(const DecodeParams p
   if (tok0 >= tok_end) {
     if (direct) {  // no visible row: o = 0, lse = -inf
       float* dst = p.o_lat + ((size_t)b * TH + rb) * DC;
-      for (int i = tid; i < ROWS * DC; i += NT) dst[i] = 0.0f;
-      if (p.lse != nullptr && tid < ROWS) p.lse[(size_t)b * TH + rb + tid] = -INFINITY;
+      for (int i = tid; i < rows_here * DC; i += NT) dst[i] = 0.0f;
+      if (p.lse != nullptr && tid < rows_here) p.lse[(size_t)b * TH + rb + tid] = -INFINITY;
     }
     return;
   }
@@ -442,8 +447,9 @@ __global__ __launch_bounds__(NT, 1) void decode_mfma_kernel(const DecodeParams p
     bf16x8 qf[2][QSTEPS];  // Q[32w + 16rt + n16][32kk + 8*g4 .. +7]
 #pragma unroll
     for (int rt = 0; rt < 2; ++rt) {
-      const uint16_t* q = static_cast<const uint16_t*>(p.q_abs) +
-                          ((size_t)b * TH + rb + 32 * wave + 16 * rt + n16) * W + 8 * g4;
+      // rows past the group's last re-read it (their results are not stored)
+      const int qr = min(32 * wave + 16 * rt + n16, rows_here - 1);
+      const uint16_t* q = static_cast<const uint16_t*>(p.q_abs) + ((size_t)b * TH + rb + qr) * W + 8 * g4;
 #pragma unroll
       for (int kk = 0; kk < QSTEPS; ++kk)
         qf[rt][kk] = *reinterpret_cast<const bf16x8*>(q + 32 * kk);
@@ -627,7 +633,7 @@ __global__ __launch_bounds__(NT, 1) void decode_mfma_kernel(const DecodeParams p
       }
       lds_barrier();                       // E(j)
     }
-    softmax_finish(sm, p, grp, lane, m_run, l_lane, direct, b, pidx, TH, rb);
+    softmax_finish(sm, p, grp, lane, m_run, l_lane, direct, b, pidx, TH, rb, rows_here);
     lds_barrier();                         // F
   } else {
     // =============================== value waves ===============================
@@ -765,7 +771,7 @@ __global__ __launch_bounds__(NT, 1) void decode_mfma_kernel(const DecodeParams p
       for (int j = -2; j < U; ++j) step(j, std::false_type{});
     }
 
-    if (v < 2) softmax_finish(sm, p, v, lane, m_run, l_lane, direct, b, pidx, TH, rb);
+    if (v < 2) softmax_finish(sm, p, v, lane, m_run, l_lane, direct, b, pidx, TH, rb, rows_here);
     lds_barrier();                         // F
     // Streaming (non-temporal) stores: the rows are read by the next kernel,
     // not by this one, and lines left dirty in L2 would all be written back
@@ -780,10 +786,12 @@ __global__ __launch_bounds__(NT, 1) void decode_mfma_kernel(const DecodeParams p
         for (int r = 0; r < 16; ++r) {
           const int row = 32 * rt + 8 * (r >> 2) + 4 * lhi + (r & 3);
           const float inv = sm.lrow[row];
+          if (row < rows_here) {  // past the token's last head: not stored
 #pragma unroll
-          for (int dt = 0; dt < 4; ++dt)
-            __builtin_nontemporal_store(cvt(o[rt][dt][r] * inv),
-                                        &dst[(size_t)row * DC + 128 * v + 32 * dt + l32]);
+            for (int dt = 0; dt < 4; ++dt)
+              __builtin_nontemporal_store(cvt(o[rt][dt][r] * inv),
+                                          &dst[(size_t)row * DC + 128 * v + 32 * dt + l32]);
+          }
         }
       }
     };
@@ -797,15 +805,15 @@ __global__ __launch_bounds__(NT, 1) void decode_mfma_kernel(const DecodeParams p
 
 }  // namespace
 
-// A 64-row group must hold heads of a single query token (the causal limit is
-// taken per group), hence H a multiple of 64; T is free.
+// A 64-row group holds heads of a single query token (the causal limit is
+// taken per group): ceil(H / 64) groups per token, any H and T.
 bool decode_mfma_supported(int dtype, int d_c, int d_r, int block_size, int T, int H) {
   (void)T;
-  return dtype == 1 && d_c == DC && d_r == DR && block_size == BS && (H % ROWS) == 0;
+  return dtype == 1 && d_c == DC && d_r == DR && block_size == BS && H > 0;
 }
 
 hipError_t launch_decode_mfma(const DecodeParams& p, hipStream_t stream) {
-  const int G = (p.T * p.H) / ROWS;
+  const int G = p.T * ((p.H + ROWS - 1) / ROWS);
   // plain plan: one workgroup per (sequence, split, group); balanced: per
   // (work item, group)
   const long long grid = (p.plan != nullptr ? 1LL : (long long)p.B) * p.num_splits * G;

@@ -34,8 +34,8 @@ struct DecodeParams {
   int32_t* plan;
 };
 
-// The MFMA kernel covers bf16, d_c = 512, d_rope = 64, 64-token pages and H
-// a multiple of 64.
+// The MFMA kernel covers bf16, d_c = 512, d_rope = 64 and 64-token pages, any
+// H and T (ceil(H / 64) query groups of 64 rows per new token).
 bool decode_mfma_supported(int dtype, int d_c, int d_r, int block_size, int T, int H);
 hipError_t launch_decode_mfma(const DecodeParams& p, hipStream_t stream);
 hipError_t launch_decode_generic(const DecodeParams& p, int dtype, hipStream_t stream);

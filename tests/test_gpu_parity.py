@@ -34,10 +34,15 @@ REDUCED = {
     "varlen": VARLEN.scaled(B=5, N=900),
     "long": LONG.scaled(B=2, N=1500),
     "v2_multi": V2_MULTI.scaled(B=3, N=300),
-    "bf16_h16": V3.scaled(B=2, H=16, N=200),        # bf16 through the generic kernel
-    # 16 heads x 4 causal tokens: 64 rows per token set, but each query token
-    # has its own causal limit, so this must not take the 64-row MFMA path
+    # head counts that are not a multiple of 64: the MFMA kernel's last 64-row
+    # group of each token is partial (16 of 64 rows; 64 + 32; 64 + 16 with
+    # three causal tokens, each token's groups under its own causal limit)
+    "bf16_h16": V3.scaled(B=2, H=16, N=200),
     "bf16_h16_t4": V3.scaled(B=2, T=4, H=16, N=200),
+    "bf16_h96": V3.scaled(B=2, H=96, N=333),
+    "bf16_h80_t3": V3.scaled(B=3, T=3, H=80, N=250),
+    # bf16 with a latent width the MFMA kernel does not take: the generic kernel
+    "bf16_dc256_generic": V3.scaled(B=2, d_c=256, N=200),
     # a prefill chunk: 64 causal queries per sequence over a ragged cache
     "prefill": PREFILL.scaled(B=2, T=64, N=200),
 }

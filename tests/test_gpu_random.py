@@ -2,7 +2,8 @@
 oracle: batch sizes, new-token counts, cache lengths (including 1 and page
 boundaries), sequential or permuted pages, causal or not, split counts from
 the library's choice up to more splits than units, and head counts that
-take the MFMA kernel (64, 128) or the generic one (32).  Each case is small
+fill the MFMA kernel's 64-row groups (64, 128) or leave a token's one group
+partial (32).  Each case is small
 enough for the oracle to finish in well under a second; the case list is
 drawn once from a fixed seed, so a failure names a reproducible case."""
 import numpy as np
