@@ -398,27 +398,42 @@ __global__ __launch_bounds__(NT, 1) void decode_mfma_kernel(const DecodeParams p
   const int t = g / gpt;                                   // the group's new token
   const int rb = t * p.H + (g - t * gpt) * ROWS;           // its first query row (t*H + h)
   const int rows_here = min(ROWS, (t + 1) * p.H - rb);     // 64, or fewer in a token's last group
-  // the same for the whole workgroup: kept in scalar registers, so that the
-  // range bounds, loop counts and page addresses below are scalar as well
-  const int n_valid =
-      __builtin_amdgcn_readfirstlane(visible_rows(p.seq_lens[b], p.T, t, p.causal, p.cap));
-  // this range: cache rows tok0 .. tok_end-1 (tok0 is a multiple of UNIT)
+  // this range starts at cache row tok0 (a multiple of UNIT)
   const int tok0 = s * chunk_rows;
-  const int tok_end = min(tok0 + chunk_rows, n_valid);
   // one split and the plain plan: the final output directly
   const bool direct = S == 1 && p.plan == nullptr;
 
-  if (tok0 >= tok_end) {
-    if (direct) {  // no visible row: o = 0, lse = -inf
+  // The sequence length fixes where the range ends.  Each role first requests
+  // what does not depend on it -- the score waves their queries and unit 0's
+  // rotary keys, the copy waves units 0 and 1 -- and reads the length only
+  // then, so that it costs no memory round trip of its own in front of the
+  // first unit.  Page-table entries for those requests are looked up within
+  // the table row but without the range's clamp: a unit that turns out to lie
+  // past the range is copied (from a valid page) and never read.  Page ids
+  // and the length are read through the constant address space: uniform
+  // indexes make them scalar loads (lgkmcnt), whose waits leave the vector
+  // loads and copies in flight.
+  const int32_t __attribute__((address_space(4)))* ctable =
+      (const int32_t __attribute__((address_space(4)))*)(p.block_table + (size_t)b * p.max_blocks);
+  auto page_at = [&](int row) { return ctable[min(row / BS, p.max_blocks - 1)]; };
+  // End of the range (cache rows tok0 .. tok_end-1), the same for the whole
+  // workgroup: kept in scalar registers, so that the range bounds, loop counts
+  // and page addresses below are scalar as well.
+  auto range_end = [&]() {
+    const int len = ((const int32_t __attribute__((address_space(4)))*)p.seq_lens)[b];
+    const int n_valid = __builtin_amdgcn_readfirstlane(visible_rows(len, p.T, t, p.causal, p.cap));
+    return min(tok0 + chunk_rows, n_valid);
+  };
+  // An empty range: wait for the requests in flight, and write o = 0,
+  // lse = -inf when this is the final output (each wave its share).
+  auto empty_range = [&]() {
+    wait_vmcnt<0>();
+    if (direct) {
       float* dst = p.o_lat + ((size_t)b * TH + rb) * DC;
       for (int i = tid; i < rows_here * DC; i += NT) dst[i] = 0.0f;
       if (p.lse != nullptr && tid < rows_here) p.lse[(size_t)b * TH + rb + tid] = -INFINITY;
     }
-    return;
-  }
-  // its 32-row units; only the last unit of the sequence can be partial
-  const int U = (tok_end - tok0 + UNIT - 1) / UNIT;
-  auto unit_valid = [&](int u) { return min(UNIT, tok_end - tok0 - u * UNIT); };
+  };
 
   // One barrier per unit.  Barrier schedule, the same for every wave: B0, then
   // E(j) for j = -2 .. U-1, then F.  In step j (between E(j-1) and E(j)):
@@ -454,19 +469,14 @@ __global__ __launch_bounds__(NT, 1) void decode_mfma_kernel(const DecodeParams p
       for (int kk = 0; kk < QSTEPS; ++kk)
         qf[rt][kk] = *reinterpret_cast<const bf16x8*>(q + 32 * kk);
     }
+    const int raw0 = page_at(tok0), raw1 = page_at(tok0 + UNIT);
     // latent chunk c = 4kk + g4 of token n16 sits at chunk position
     // c ^ lat_sw(n16) (only the low 4 bits of c take part); token tile ti adds
     // 16 KiB
     int loff[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) loff[j] = n16 * 1024 + (((4 * j + g4) ^ lat_sw(n16)) << 4);
-    const int32_t __attribute__((address_space(4)))* ctable =
-        (const int32_t __attribute__((address_space(4)))*)(p.block_table + (size_t)b * p.max_blocks);
     const uint16_t* pool = static_cast<const uint16_t*>(p.pool);
-
-    // Page-table entry of unit u (clamped to the range's last unit), read one
-    // unit before its rotary keys so that the scalar load is not waited for.
-    auto page_raw = [&](int u) { return ctable[(tok0 + min(u, U - 1) * UNIT) / BS]; };
     // rotary columns 512 + 32(kk-16) + 8*g4 .. +7 of token 16ti + n16 of unit
     // u (page-table entry raw), from memory (a unit lies within one page), as
     // kr[kk - 16][ti]
@@ -481,9 +491,23 @@ __global__ __launch_bounds__(NT, 1) void decode_mfma_kernel(const DecodeParams p
           kr[k2][ti] = *reinterpret_cast<const bf16x8*>(rrow + ti * 16 * W + 32 * k2);
     };
 
+    // rotary keys double-buffered by unit parity: unit 0's requested now
+    bf16x8 kra[2][2], krb[2][2];
+    load_kr(0, raw0, kra);
+
+    const int tok_end = range_end();
+    if (tok0 >= tok_end) {
+      empty_range();
+      return;
+    }
+    const int U = (tok_end - tok0 + UNIT - 1) / UNIT;  // 32-row units
+    // Page-table entry of unit u (clamped to the range's last unit), read one
+    // unit before its rotary keys so that the scalar load is not waited for.
+    auto page_raw = [&](int u) { return ctable[(tok0 + min(u, U - 1) * UNIT) / BS]; };
+
     // scores of unit u with its rotary keys in kr; the next unit's rotary keys
     // are read into krn first
-    int raw_next;  // page-table entry of unit u + 1 in scores(u)
+    int raw_next = raw1;  // page-table entry of unit u + 1 in scores(u)
     auto scores = [&](int u, const bf16x8 (&kr)[2][2], bf16x8 (&krn)[2][2])
                       __attribute__((always_inline)) {
       const uint8_t* lat = sm.lat[u & 3];
@@ -544,10 +568,6 @@ __global__ __launch_bounds__(NT, 1) void decode_mfma_kernel(const DecodeParams p
               acc[rt][ti];
     };
 
-    // rotary keys double-buffered by unit parity
-    bf16x8 kra[2][2], krb[2][2];
-    load_kr(0, page_raw(0), kra);
-    raw_next = page_raw(1);
     lds_barrier();                         // B0: unit 0 landed
     // j even: unit j+2 is even, its keys in kra, the next unit's into krb
     for (int j = -2; j < U; j += 2) {
@@ -567,18 +587,10 @@ __global__ __launch_bounds__(NT, 1) void decode_mfma_kernel(const DecodeParams p
     // direct-to-LDS copies of 1 KiB.  Lane l fetches the 16-byte chunk that
     // belongs at LDS chunk position l of its row.
     const int c = wave - 4;
-    // Page ids are read through the constant address space: the index is
-    // uniform, so this is a scalar load (lgkmcnt), and the wait for it does not
-    // drain the copies in flight (vmcnt).
-    const int32_t __attribute__((address_space(4)))* ctable =
-        (const int32_t __attribute__((address_space(4)))*)(p.block_table + (size_t)b * p.max_blocks);
     const uint8_t* pool = static_cast<const uint8_t*>(p.pool);
     int cl[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) cl[i] = (lane ^ lat_sw(c + 2 * i)) << 4;
-    // Page-table entry of unit u (clamped to the range's last unit, so the
-    // read stays inside the range's pages); read one step ahead in the loop.
-    auto page_raw = [&](int u) { return ctable[(tok0 + min(u, U - 1) * UNIT) / BS]; };
     const uint32_t lat_base = (uint32_t)(uintptr_t)&sm.lat[0][0];
     auto issue = [&](int u, int raw) {
       const int blk = clamp_block(raw, p.num_blocks);
@@ -590,6 +602,28 @@ __global__ __launch_bounds__(NT, 1) void decode_mfma_kernel(const DecodeParams p
         copy16_to_lds(src + row * ROW_BYTES, (uint32_t)cl[i & 7], lat + row * 1024);
       }
     };
+    // Only units 0 and 1 are requested before the first barrier, and before
+    // the length is read: every workgroup starts at once, and unit 0 (scored
+    // in step -2) lands sooner when it does not queue behind units 2 and 3 of
+    // the whole chip.  Unit u is then issued in step u - 4, units 2 and 3 in
+    // steps -2 and -1.
+    const bool spec1 = chunk_rows > UNIT;  // the range may hold a unit 1
+    // both page ids first, in one round trip (pinned, or the compiler sinks
+    // the second load below unit 0's copies)
+    const int raw0 = page_at(tok0), raw1 = page_at(tok0 + UNIT);
+    pin_sgpr(raw1);
+    issue(0, raw0);
+    if (spec1) issue(1, raw1);
+    const int tok_end = range_end();
+    if (tok0 >= tok_end) {
+      empty_range();
+      return;
+    }
+    const int U = (tok_end - tok0 + UNIT - 1) / UNIT;  // 32-row units
+    auto unit_valid = [&](int u) { return min(UNIT, tok_end - tok0 - u * UNIT); };
+    // Page-table entry of unit u (clamped to the range's last unit, so the
+    // read stays inside the range's pages); read one step ahead in the loop.
+    auto page_raw = [&](int u) { return ctable[(tok0 + min(u, U - 1) * UNIT) / BS]; };
     // Rows past the visible length of the range's last unit are zeroed once
     // it has landed and before V is read from it: stale contents (possibly
     // NaN) must not reach P.V.  The score waves may read those rows
@@ -603,14 +637,8 @@ __global__ __launch_bounds__(NT, 1) void decode_mfma_kernel(const DecodeParams p
       for (int q = valid * 64 + zt; q < UNIT * 64; q += 128) dl[q] = z;
     };
 
-    // Only units 0 and 1 are requested before the first barrier: every
-    // workgroup starts at once, and unit 0 (scored in step -2) lands sooner
-    // when it does not queue behind units 2 and 3 of the whole chip.  Unit u
-    // is then issued in step u - 4, units 2 and 3 in steps -2 and -1.
-    issue(0, page_raw(0));
-    if (U > 1) issue(1, page_raw(1));
     int raw_next = page_raw(2);
-    if (U > 1) wait_vmcnt<COPIES>(); else wait_vmcnt<0>();  // unit 0 landed
+    if (spec1) wait_vmcnt<COPIES>(); else wait_vmcnt<0>();  // unit 0 landed
     // The copy waves also run the online softmax of query rows 32 .. 63 (16
     // rows each), first in each step: its VALU work then shares a SIMD with a
     // score wave's MFMAs instead of a value wave's, which balances the four
@@ -633,6 +661,7 @@ __global__ __launch_bounds__(NT, 1) void decode_mfma_kernel(const DecodeParams p
       }
       lds_barrier();                       // E(j)
     }
+    wait_vmcnt<0>();  // a unit 1 copied past a one-unit range
     softmax_finish(sm, p, grp, lane, m_run, l_lane, direct, b, pidx, TH, rb, rows_here);
     lds_barrier();                         // F
   } else {
@@ -640,6 +669,13 @@ __global__ __launch_bounds__(NT, 1) void decode_mfma_kernel(const DecodeParams p
     // Value wave v owns latent columns 128v .. 128v+127 of O for all 64 rows,
     // and the softmax of query rows 16v .. 16v+15.
     const int v = (wave & 1) + 2 * (wave >> 2);
+    const int tok_end = range_end();
+    if (tok0 >= tok_end) {
+      empty_range();
+      return;
+    }
+    const int U = (tok_end - tok0 + UNIT - 1) / UNIT;  // 32-row units
+    auto unit_valid = [&](int u) { return min(UNIT, tok_end - tok0 - u * UNIT); };
     // Transposing-read offsets of this lane: in 16-lane group gq, lane i points
     // at token 4*(i >> 2) + 2*lhi + sel (+ 16*ks), columns 128v + 32dt + 16*gq
     // + 4*(i & 3); result lane i holds column .. + i for the 4 tokens.
