@@ -72,6 +72,58 @@ __device__ __forceinline__ float xor16_sum(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+// Makes a uniform value live in a scalar register at this point (no code).
+__device__ __forceinline__ void pin_sgpr(int x) { asm volatile("" ::"s"(x)); }
+
+// Workgroup barrier for LDS traffic only.  __syncthreads() is a release/acquire
+// fence plus s_barrier, and the release makes the wave wait for every vector
+// memory operation in flight -- including the direct-to-LDS copies of units
+// still ahead, which would drain the copy pipeline at every barrier.  Here
+// each wave waits only for its own LDS reads and writes (lgkmcnt(0)); copies
+// are waited for explicitly (vmcnt) before the barrier that publishes them.
+// The signal fences keep the compiler from moving memory accesses across.
+__device__ __forceinline__ void lds_barrier() {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt((0x7 << 4) | 0xF | (3 << 14));  // lgkmcnt(0)
+  __builtin_amdgcn_s_barrier();
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
+// One 16-byte direct-to-LDS copy per lane: lane l reads gbase + voff (its own
+// offset) and writes LDS byte lds + 16*l.  Written as assembly so that the
+// compiler does not track it: its own tracking treats every later LDS read as
+// possibly overlapping a copy in flight and would wait for all copies
+// (vmcnt(0)) before the first one, draining the pipeline.  Completion is
+// instead waited for explicitly with wait_vmcnt before the barrier that hands
+// the slot to the readers.  The copy has no result register; its address
+// operands are read at issue.  On gfx9 a copy that reads M0 needs one wait
+// state after M0 is written (the s_nop).
+// gbase and lds are the same in every lane; they are moved to scalar
+// registers explicitly so that the constraints hold whatever the compiler
+// concludes about their uniformity.
+__device__ __forceinline__ void copy16_to_lds(const uint8_t* gbase, uint32_t voff,
+                                              uint32_t lds) {
+  const uint64_t g = (uint64_t)(uintptr_t)gbase;
+  const uint32_t glo = __builtin_amdgcn_readfirstlane((uint32_t)g);
+  const uint32_t ghi = __builtin_amdgcn_readfirstlane((uint32_t)(g >> 32));
+  const uint8_t* gs = (const uint8_t*)(uintptr_t)(((uint64_t)ghi << 32) | glo);
+  asm volatile(
+      "s_mov_b32 m0, %0\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %1, %2"
+      :
+      : "s"(__builtin_amdgcn_readfirstlane(lds)), "v"(voff), "s"(gs)
+      : "memory");
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  // s_waitcnt vmcnt(N), expcnt and lgkmcnt unconstrained.  gfx9 encoding:
+  // vmcnt bits [3:0] and [15:14], expcnt [6:4], lgkmcnt [11:8].
+  static_assert(N >= 0 && N < 64, "vmcnt");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (((N >> 4) & 3) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
 // Rows a query of new token t may attend to, capped by the host-side bound.
 __device__ __forceinline__ int visible_rows(int seq_len, int T, int t, int causal,
                                             int cap) {

@@ -280,6 +280,166 @@ __global__ __launch_bounds__(PJ_NT) void absorb_q_mfma_kernel(
   }
 }
 
+// absorb_q for a large M.  Workgroup (h, mz): all 512 latent columns of head
+// h for query rows mz*AW_MT .. +AW_MT-1, so that each query row (and its
+// rotary part) is read by one workgroup, every output row is written whole,
+// and the head's weight is staged once per AW_MT rows.  Wave w takes latent
+// columns 128w .. 128w+127 (8 tiles of 16) x all d_nope into registers: the A
+// operand, 32 NKS VGPRs per tile.
+// Everything the workgroup reads is requested at its start, by direct-to-LDS
+// copies: W^UK[h] in rounds of 64 rows (one 1 KiB weight row per copy; the
+// waves take their fragments from each round with transposing reads) and the
+// query rows (four 256-byte rows per copy).  The 16-row tiles then run with
+// no memory wait at all: on this chip one counter covers loads and stores,
+// and a load waited for behind the stores of earlier tiles would wait for
+// those stores too.
+constexpr int AW_DC = 512;
+constexpr int AW_LD = 2 * AW_DC + 32;  // bytes per staged weight row
+constexpr int AW_ROWS = 64;            // weight rows per round
+constexpr int AW_MT = 256;             // query rows per workgroup
+constexpr int AW_QLD = 256;            // bytes per staged query row (d_nope <= 128)
+
+// NKS: k-steps of 32 covering d_nope (<= 4).
+template <int NKS>
+__global__ __launch_bounds__(PJ_NT) void absorb_q_wide_kernel(
+    const uint16_t* __restrict__ q_nope, const uint16_t* __restrict__ q_rope,
+    const uint16_t* __restrict__ w_uk, uint16_t* __restrict__ q_abs, int M, int H, int d_n,
+    int d_r) {
+  extern __shared__ __align__(16) uint8_t wl[];  // [AW_ROWS][AW_LD], then [AW_MT][AW_QLD]
+  uint8_t* ql = wl + AW_ROWS * AW_LD;
+  const int h = blockIdx.x;
+  const int mbeg = blockIdx.y * AW_MT, mend = min(M, mbeg + AW_MT);
+  const int ntiles = (mend - mbeg + 15) >> 4;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar branches
+  const int i16 = lane & 15, g = lane >> 4;
+  const int W = AW_DC + d_r;
+  const uint32_t wl_base = (uint32_t)(uintptr_t)wl;
+  const uint16_t* wh = w_uk + (size_t)h * d_n * AW_DC;
+
+  // weight rows r0 .. r0+63 into LDS, wave w taking rows r0 + w + 4j; rows
+  // past d_n are zeroed instead (the contraction is padded to 32 NKS rows)
+  auto stage = [&](int r0) {
+#pragma unroll
+    for (int j = 0; j < AW_ROWS / 4; ++j) {
+      const int d = r0 + wave + 4 * j;
+      if (d < d_n)
+        copy16_to_lds(reinterpret_cast<const uint8_t*>(wh + (size_t)d * AW_DC), lane * 16,
+                      wl_base + (d - r0) * AW_LD);
+    }
+  };
+  auto zero_rows = [&](int r0) {
+    const int zb = max(r0, d_n), ze = min(r0 + AW_ROWS, 32 * NKS);
+    const u32x4 z = {0u, 0u, 0u, 0u};
+    for (int i = tid; i < (ze - zb) * (AW_DC / 8); i += PJ_NT)
+      *reinterpret_cast<u32x4*>(wl + (zb - r0 + i / (AW_DC / 8)) * AW_LD + 16 * (i % (AW_DC / 8))) = z;
+  };
+  stage(0);
+
+  // Query rows: staged row r (query row mbeg + r, clamped to mend - 1) holds
+  // its 16-byte chunk c at position c ^ (r & 15), so that the 16 rows of a
+  // tile read at one chunk fall in distinct banks.  A copy fills four rows;
+  // lane l fills position l & 15 of row 4i + (l >> 4) with the chunk that
+  // belongs there (chunks past d_nope re-read the last one: finite values that
+  // meet the zeroed weight rows).
+  {
+    const int nch = d_n >> 3;  // chunks per row
+#pragma unroll
+    for (int i = 0; i < AW_MT / 16; ++i) {
+      const int r = 16 * i + 4 * wave + (lane >> 4);  // this lane's staged row
+      const int c = min((lane & 15) ^ (r & 15), nch - 1);
+      const uint32_t voff = (uint32_t)((((size_t)min(mbeg + r, mend - 1) - mbeg) * H * d_n + 8 * c) * 2);
+      copy16_to_lds(reinterpret_cast<const uint8_t*>(q_nope + ((size_t)mbeg * H + h) * d_n), voff,
+                    wl_base + AW_ROWS * AW_LD + (16 * i + 4 * wave) * AW_QLD);
+    }
+  }
+
+  // The rotary part of the workgroup's rows (d_r <= 64: at most 8 chunks of
+  // 16 bytes per row, 2048 for 256 rows, 8 per thread), carried over
+  // unchanged while the rest is on its way: all loads, then all stores.
+  // Unconditional loads on clamped chunks; only the stores are predicated.
+  {
+    const int rch = d_r >> 3;  // rotary chunks per row
+    const int nrc = (mend - mbeg) * rch;
+    constexpr int RT = AW_MT * 8 / PJ_NT;
+    u32x4 rv[RT];
+#pragma unroll
+    for (int u = 0; u < RT; ++u) {
+      const int i = min(tid + u * PJ_NT, nrc - 1);
+      rv[u] = *reinterpret_cast<const u32x4*>(
+          q_rope + ((size_t)(mbeg + i / rch) * H + h) * d_r + 8 * (i % rch));
+    }
+#pragma unroll
+    for (int u = 0; u < RT; ++u) {
+      const int i = tid + u * PJ_NT;
+      if (i < nrc)
+        *reinterpret_cast<u32x4*>(q_abs + ((size_t)(mbeg + i / rch) * H + h) * W + AW_DC +
+                                  8 * (i % rch)) = rv[u];
+    }
+  }
+
+  // A fragments of k-step ks from the staged round holding weight rows r0 ..
+  bf16x8 a[8][NKS];
+  auto take = [&](int ks, int r0) {
+#pragma unroll
+    for (int ct = 0; ct < 8; ++ct) {
+      const int col = 128 * wave + 16 * ct + 4 * (i16 & 3);
+      const int d = 32 * ks - r0 + 8 * g + (i16 >> 2);
+      const s16x4 v0 = lds_tr16(wl + d * AW_LD + 2 * col);
+      const s16x4 v1 = lds_tr16(wl + (d + 4) * AW_LD + 2 * col);
+      // a plain concatenation: no instruction reads the loaded registers
+      a[ct][ks] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
+    }
+  };
+  // every copy of this wave has landed (and the rotary loads: the stores above
+  // have read them)
+  wait_vmcnt<0>();
+  zero_rows(0);
+  lds_barrier();
+#pragma unroll
+  for (int ks = 0; ks < NKS && ks < 2; ++ks) take(ks, 0);
+  if (NKS > 2) {
+    lds_barrier();  // every wave has its fragments of round 0
+    stage(AW_ROWS);
+    wait_vmcnt<0>();
+    zero_rows(AW_ROWS);
+    lds_barrier();
+#pragma unroll
+    for (int ks = 2; ks < NKS; ++ks) take(ks, AW_ROWS);
+  }
+
+  const int col0 = 128 * wave + 4 * g;  // + 16 ct: this lane's 4 columns
+  // B fragments of tile t (staged row 16t + i16), read one tile ahead
+  auto read_b = [&](int t, bf16x8 (&bq)[NKS]) {
+    const int r = 16 * min(t, ntiles - 1) + i16;
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks)
+      bq[ks] = *reinterpret_cast<const bf16x8*>(ql + r * AW_QLD + 16 * ((4 * ks + g) ^ (r & 15)));
+  };
+  bf16x8 bn[NKS];
+  read_b(0, bn);
+  for (int t = 0; t < ntiles; ++t) {
+    const int r = 16 * t + i16;
+    bf16x8 bq[NKS];
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) bq[ks] = bn[ks];
+    read_b(t + 1, bn);
+    f32x4 acc[8];
+#pragma unroll
+    for (int ct = 0; ct < 8; ++ct) acc[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks)
+#pragma unroll
+      for (int ct = 0; ct < 8; ++ct) acc[ct] = mfma16(a[ct][ks], bq[ks], acc[ct]);
+    const int m = mbeg + r;
+    if (m < mend) {
+      uint16_t* dst = q_abs + ((size_t)m * H + h) * W + col0;
+#pragma unroll
+      for (int ct = 0; ct < 8; ++ct) store_bf16x4(dst + 16 * ct, acc[ct]);
+    }
+  }
+}
+
 // out_proj on MFMA.  Workgroup (h, vb, mz): value columns vb*64 .. +63 of head h
 // for query rows mz*64 .. +63; wave w holds W^UV[h][v][:] for its 16 columns v
 // (the A operand, loaded straight from HBM: both operands are contiguous along
@@ -419,6 +579,34 @@ bool absorb_mfma_fits(int d_n, int d_c, int d_r) {
   return d_c % AB_CT == 0 && d_n % 8 == 0 && d_n > 0 && d_n <= 32 * AB_KS && d_r % 8 == 0;
 }
 
+// the wide absorb kernel: d_c = 512, d_nope <= 128 (A fragments of 128 columns
+// in registers, 256-byte staged query rows), d_rope <= 64
+bool absorb_wide_fits(int M, int H, int d_n, int d_c, int d_r) {
+  // (the query rows a workgroup stages lie within 2^32 bytes of its first)
+  return M > 256 && (M + AW_MT - 1) / AW_MT <= 65535 && d_c == AW_DC && d_n % 8 == 0 &&
+         d_n > 0 && d_n <= 128 && d_r % 8 == 0 && d_r > 0 && d_r <= 64 &&
+         (long long)AW_MT * H * d_n * 2 < (1LL << 32);
+}
+
+hipError_t launch_absorb_wide(const uint16_t* q_nope, const uint16_t* q_rope,
+                              const uint16_t* w_uk, uint16_t* q_abs, int M, int H, int d_n,
+                              int d_r, hipStream_t stream) {
+  const dim3 grid(H, (M + AW_MT - 1) / AW_MT);
+  const size_t shmem = (size_t)AW_ROWS * AW_LD + (size_t)AW_MT * AW_QLD;
+#define AW_LAUNCH(K)                                                                    \
+  hipLaunchKernelGGL((absorb_q_wide_kernel<K>), grid, dim3(PJ_NT), shmem, stream, q_nope, \
+                     q_rope, w_uk, q_abs, M, H, d_n, d_r)
+  switch ((d_n + 31) >> 5) {
+    case 1: AW_LAUNCH(1); break;
+    case 2: AW_LAUNCH(2); break;
+    case 3: AW_LAUNCH(3); break;
+    case 4: AW_LAUNCH(4); break;
+    default: return hipErrorInvalidValue;
+  }
+#undef AW_LAUNCH
+  return hipGetLastError();
+}
+
 bool out_proj_mfma_fits(int d_c, int d_v) {
   return d_c % 32 == 0 && d_c > 0 && d_c <= 32 * OP_KS && d_v % 4 == 0;
 }
@@ -429,6 +617,9 @@ hipError_t launch_absorb_q(int dtype, const void* q_nope, const void* q_rope, co
                            void* q_abs, int M, int H, int d_n, int d_c, int d_r,
                            hipStream_t stream) {
   if (M <= 0) return hipSuccess;
+  if (dtype == 1 && absorb_wide_fits(M, H, d_n, d_c, d_r))
+    return launch_absorb_wide((const uint16_t*)q_nope, (const uint16_t*)q_rope,
+                              (const uint16_t*)w_uk, (uint16_t*)q_abs, M, H, d_n, d_r, stream);
   if (dtype == 1 && absorb_mfma_fits(d_n, d_c, d_r)) {
     const int mt = pj_rows_per_wg(M);
     const dim3 grid(H, d_c / AB_CT, (M + mt - 1) / mt);
@@ -474,7 +665,9 @@ hipError_t launch_absorb_q_append(int dtype, const void* q_nope, const void* q_r
                                   const void* w_uk, void* q_abs, int M, int H, int d_n, int d_c,
                                   int d_r, const AppendArgs& ap, hipStream_t stream) {
   const long long extra = ((long long)ap.rows + PJ_NT / 64 - 1) / (PJ_NT / 64);
-  if (M > 0 && ap.rows > 0 && dtype == 1 && absorb_mfma_fits(d_n, d_c, d_r) &&
+  // a large M takes the wide absorb kernel, then the append on its own
+  if (M > 0 && ap.rows > 0 && dtype == 1 && !absorb_wide_fits(M, H, d_n, d_c, d_r) &&
+      absorb_mfma_fits(d_n, d_c, d_r) &&
       ap.row_bytes % 16 == 0 && (long long)H + extra <= 0x7fffffffLL) {
     const int mt = pj_rows_per_wg(M);
     const dim3 grid((unsigned)(H + extra), d_c / AB_CT, (M + mt - 1) / mt);

@@ -154,9 +154,16 @@ def test_step_parity(name):
 
 # ------------------------------------------------------------------ projections
 
-@pytest.mark.parametrize("name,M", [("v3", 1), ("v3", 150), ("v2_multi", 77),
-                                    ("tiny_f32", 35)])
-def test_projections_elementwise(name, M):
+@pytest.mark.parametrize("name,M,over", [
+    ("v3", 1, {}), ("v3", 150, {}), ("v2_multi", 77, {}), ("tiny_f32", 35, {}),
+    # M > 256: the wide kernels (absorb: one workgroup per head and 64 rows,
+    # weight staged in two rounds; out-proj: 8 waves over all 128 value
+    # columns), ragged against 64-row workgroups, with d_nope that leaves
+    # zero-padded weight rows (104: second round, 40: first round) and value
+    # widths that are not a multiple of 16
+    ("v3", 300, {}), ("v3", 300, {"d_n": 104, "d_v": 100}),
+    ("v3", 290, {"d_n": 40, "d_v": 64}), ("v2_multi", 517, {})])
+def test_projections_elementwise(name, M, over):
     """mla_absorb_q and mla_out_proj alone, with M rows ragged against the
     kernels' 16-row tiles and 64-row workgroups.  Each output element is held
     to what its arithmetic allows, not to the decode tolerance: the fp64
@@ -165,9 +172,9 @@ def test_projections_elementwise(name, M):
     accumulation.  For out_proj the fp32 latent input must enter the product
     with far more than bf16's 8 bits: the absolute slack 1e-4 * max|ref| is
     below what rounding o_lat to bf16 would cost at d_c = 512."""
-    w = REDUCED[name].scaled(B=M, T=1, N=8)
+    w = REDUCED[name].scaled(B=M, T=1, N=8, **over)
     bt = make_inputs(w, with_rows=False)
-    note(f"projections {name} M={M}")
+    note(f"projections {name} M={M} {over}")
     cfg = cfg_of(w)
     dt = torch_dtype(bt)
     q_nope = to_dev(bt.q_nope.reshape(M, w.H, w.d_n), dt, "cuda")
