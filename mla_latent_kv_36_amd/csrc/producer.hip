@@ -21,9 +21,10 @@
 //     v_mfma_f32_16x16x32_bf16.  M is small (a decode step's new tokens), so
 //     the work is the weight stream; the k dimension is split over
 //     workgroups (fp32 partial sums in a workspace) so that enough compute
-//     units stream it.  Each workgroup stages a 64-token x 256 and a
-//     64-column x 256 tile of hidden vectors and weights in LDS and runs 4
-//     waves of 16 tokens x 64 columns.
+//     units stream it.  Each workgroup stages a 64-token and a 64-column
+//     tile of hidden vectors and weights over its k range (at most 512) in
+//     LDS, all of it requested at once, and runs 4 waves of 16 tokens x 64
+//     columns.
 //   * kv_rope_append_kernel: sums the partials in split order (deterministic),
 //     rotates the k^R pairs, rounds to the cache type and writes the row into
 //     its page slot.  The rotation angle is formed and reduced to [-pi, pi]
@@ -37,10 +38,9 @@
 namespace mla {
 namespace {
 
-constexpr int PJ_TM = 64;    // tokens per workgroup tile
-constexpr int PJ_TN = 64;    // output columns per workgroup tile
-constexpr int PJ_KC = 256;   // k per LDS chunk (8 MFMA k-steps)
-constexpr int PJ_LD = PJ_KC + 8;  // bf16 per LDS row: 528 B, 16 rows at one k hit 64 banks once
+constexpr int PJ_TM = 64;     // tokens per workgroup tile
+constexpr int PJ_TN = 64;     // output columns per workgroup tile
+constexpr int PJ_KMAX = 512;  // k per workgroup at most (one staged 1 KiB row)
 
 __device__ __forceinline__ f32x4 mfma16(const bf16x8& a, const bf16x8& b, const f32x4& c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
@@ -48,12 +48,19 @@ __device__ __forceinline__ f32x4 mfma16(const bf16x8& a, const bf16x8& b, const 
 
 // part[z, m, n] = sum over this split's k of hidden[m, k] * Wcat[n, k], with
 // Wcat = [W^DKV ; W^KR] (rows n < d_c from W^DKV, the rest from W^KR).
+// A split covers at most 512 k: the workgroup's 64 hidden rows and 64 weight
+// rows over its k range are all requested at once, as direct-to-LDS copies
+// of 1 KiB (one staged row each), so that the workgroup pays one memory
+// latency; the MFMAs then run from LDS.  16-byte chunk c of staged row r sits
+// at position c ^ (r & 15), so that the 16 rows an MFMA operand reads at one
+// k fall in distinct banks.  Rows past M or N are clamped (their sums are not
+// stored) and k past d within a row re-reads the last chunk (k-steps past the
+// split are not multiplied).
 __global__ __launch_bounds__(256) void kv_proj_mfma_kernel(
     const uint16_t* __restrict__ hidden, const uint16_t* __restrict__ w_dkv,
     const uint16_t* __restrict__ w_kr, float* __restrict__ part, int M, int d, int d_c,
     int d_r, int steps_per_split, int xcds) {
-  __shared__ __align__(16) uint16_t sa[PJ_TM * PJ_LD];
-  __shared__ __align__(16) uint16_t sb[PJ_TN * PJ_LD];
+  __shared__ __align__(16) uint8_t st[(PJ_TM + PJ_TN) * 1024];  // hidden rows, then weight rows
   const int N = d_c + d_r;
   // Workgroup i runs on XCD i % xcds (queried on the host), and each XCD has
   // its own L2.  Tiles are
@@ -73,76 +80,82 @@ __global__ __launch_bounds__(256) void kv_proj_mfma_kernel(
   const int z = t / (ntn * ntm);
   const int nk = d / 32;
   const int s_begin = z * steps_per_split;
-  const int s_end = min(s_begin + steps_per_split, nk);
+  const int steps = min(steps_per_split, nk - s_begin);  // k-steps of 32 (<= 16)
+  const int k0 = 32 * s_begin;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar branches
+
+  // staged row q < 64: hidden row m0 + q; q >= 64: weight row n0 + q - 64
+  const uint32_t st_base = (uint32_t)(uintptr_t)st;
+#pragma unroll
+  for (int j = 0; j < (PJ_TM + PJ_TN) / 4; ++j) {
+    const int q = wave + 4 * j;
+    const int r = q & 63;
+    const uint16_t* src;
+    if (q < PJ_TM) {
+      src = hidden + (size_t)min(m0 + r, M - 1) * d;
+    } else {
+      const int n = min(n0 + r, N - 1);
+      src = n < d_c ? w_dkv + (size_t)n * d : w_kr + (size_t)(n - d_c) * d;
+    }
+    const int c = lane ^ (r & 15);
+    copy16_to_lds(reinterpret_cast<const uint8_t*>(src), 2u * (uint32_t)min(k0 + 8 * c, d - 8),
+                  st_base + q * 1024);
+  }
+  wait_vmcnt<0>();
+  lds_barrier();
 
   f32x4 acc[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  // Staging: 64 rows x (up to) 256 k of both operands in 16-byte pieces (32
-  // per row, 8 per thread and operand); rows past M or N and k past the chunk
-  // are zero.  A chunk's pieces are all loaded into registers before the
-  // first is stored, and the next chunk's loads are issued before this
-  // chunk's MFMAs, so memory latency is paid about once per workgroup.
-  constexpr int PIECES = PJ_KC / 8;
-  constexpr int PER = PJ_TM * PIECES / 256;
-  uint4 va[PER], vb[PER];
-  auto load_chunk = [&](int sc) {
-    const int steps = min(PJ_KC / 32, s_end - sc);
-    const int k0 = sc * 32;
+  // wave w: tokens 16w + (l & 15) (A), columns 16j + (l & 15) (B), k
+  // 32s + 8(l >> 4) .. +7, i.e. chunk 4s + (l >> 4)
+  const int i16 = lane & 15, g = lane >> 4;
+  const uint8_t* arow = st + (16 * wave + i16) * 1024;
+  auto step = [&](int s) __attribute__((always_inline)) {
+    const int pos = ((4 * s + g) ^ i16) * 16;  // every operand row here has (row & 15) == i16
+    const bf16x8 a = *reinterpret_cast<const bf16x8*>(arow + pos);
 #pragma unroll
-    for (int u = 0; u < PER; ++u) {
-      const int q = tid + 256 * u;
-      const int r = q / PIECES, c = q % PIECES;
-      const bool kin = c < steps * 4;
-      const int m = m0 + r, n = n0 + r;
-      va[u] = uint4{0u, 0u, 0u, 0u};
-      vb[u] = uint4{0u, 0u, 0u, 0u};
-      if (kin && m < M) va[u] = *reinterpret_cast<const uint4*>(hidden + (size_t)m * d + k0 + 8 * c);
-      if (kin && n < N) {
-        const uint16_t* w = n < d_c ? w_dkv + (size_t)n * d : w_kr + (size_t)(n - d_c) * d;
-        vb[u] = *reinterpret_cast<const uint4*>(w + k0 + 8 * c);
-      }
+    for (int j = 0; j < 4; ++j) {
+      const bf16x8 b =
+          *reinterpret_cast<const bf16x8*>(st + (PJ_TM + 16 * j + i16) * 1024 + pos);
+      acc[j] = mfma16(a, b, acc[j]);
     }
   };
-  if (s_begin < s_end) load_chunk(s_begin);
-  const int arow = 16 * wave + (lane & 15);
-  const int kq = 8 * (lane >> 4);
-  for (int sc = s_begin; sc < s_end; sc += PJ_KC / 32) {
-    const int steps = min(PJ_KC / 32, s_end - sc);  // k-steps of 32 in this chunk
+  // a full split as straight-line code with its operands read three steps
+  // ahead, so that LDS latency is hidden under the MFMAs of earlier steps
+  if (steps == PJ_KMAX / 32) {
+    constexpr int AH = 3;
+    bf16x8 fa[AH], fb[AH][4];
+    auto read = [&](int s, int k) __attribute__((always_inline)) {
+      const int pos = ((4 * s + g) ^ i16) * 16;
+      fa[k] = *reinterpret_cast<const bf16x8*>(arow + pos);
 #pragma unroll
-    for (int u = 0; u < PER; ++u) {
-      const int q = tid + 256 * u;
-      const int r = q / PIECES, c = q % PIECES;
-      *reinterpret_cast<uint4*>(&sa[r * PJ_LD + 8 * c]) = va[u];
-      *reinterpret_cast<uint4*>(&sb[r * PJ_LD + 8 * c]) = vb[u];
-    }
-    __syncthreads();
-    if (sc + PJ_KC / 32 < s_end) load_chunk(sc + PJ_KC / 32);
-    // wave w: tokens 16w + (l & 15) (A), columns 16j + (l & 15) (B), k
-    // 32s + 8(l >> 4) .. +7
-    for (int s = 0; s < steps; ++s) {
-      const bf16x8 a = *reinterpret_cast<const bf16x8*>(&sa[arow * PJ_LD + 32 * s + kq]);
+      for (int j = 0; j < 4; ++j)
+        fb[k][j] = *reinterpret_cast<const bf16x8*>(st + (PJ_TM + 16 * j + i16) * 1024 + pos);
+    };
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const bf16x8 b =
-            *reinterpret_cast<const bf16x8*>(&sb[(16 * j + (lane & 15)) * PJ_LD + 32 * s + kq]);
-        acc[j] = mfma16(a, b, acc[j]);
-      }
+    for (int s = 0; s < AH; ++s) read(s, s);
+#pragma unroll
+    for (int s = 0; s < PJ_KMAX / 32; ++s) {
+      const int k = s % AH;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[j] = mfma16(fa[k], fb[k][j], acc[j]);
+      if (s + AH < PJ_KMAX / 32) read(s + AH, k);
+      __builtin_amdgcn_sched_barrier(0);
     }
-    __syncthreads();
+  } else {
+    for (int s = 0; s < steps; ++s) step(s);
   }
   // D: lane l holds column 16j + (l & 15), tokens 16w + 4(l >> 4) + i
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    const int n = n0 + 16 * j + (lane & 15);
+    const int n = n0 + 16 * j + i16;
     if (n >= N) continue;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int m = m0 + 16 * wave + 4 * (lane >> 4) + i;
+      const int m = m0 + 16 * wave + 4 * g + i;
       if (m < M) part[((size_t)z * M + m) * N + n] = acc[j][i];
     }
   }
@@ -180,44 +193,60 @@ __device__ __forceinline__ void rope_angle(int pos, int q, int d_r, double log2_
 
 // One workgroup per token m = b * T_new + i; thread t owns the column pairs
 // p = t and p = t + blockDim.x (2p, 2p + 1 < N <= 4 * blockDim.x).  The
-// partial sums are loaded before the page lookup (they do not depend on it),
-// so the two round trips overlap.
+// partial sums of the first 16 splits are requested first, then the page is
+// looked up through the scalar cache (uniform indexes: its waits leave the
+// vector loads in flight), so the round trips overlap.
 template <typename E>
 __global__ __launch_bounds__(1024) void kv_rope_append_kernel(
     const float* __restrict__ part, int ksplit, int M, int d_c, int d_r, void* pool,
     int num_blocks, const int32_t* __restrict__ block_table, int max_blocks,
     const int32_t* __restrict__ seq_lens, int T_new, int block_size, double log2_base) {
+  typedef const int32_t __attribute__((address_space(4)))* cptr;
   const int N = d_c + d_r;
   const int m = blockIdx.x;
   if (m >= M) return;
   const int b = m / T_new;
   const int i = m - b * T_new;
-  const int pos = seq_lens[b] + i;
-  // partial sums in split order, 16 splits' loads in flight at a time (the
-  // loads are unconditional, on clamped indices; splits past the last are
-  // left out by selection)
+  // partial sums in split order, the first 16 splits' loads issued together
+  // (unconditional, on clamped indices; splits past the last are left out by
+  // selection), further splits 16 at a time
+  float2 v[2][16];
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const int pc = min((int)threadIdx.x + u * (int)blockDim.x, N / 2 - 1);
+#pragma unroll
+    for (int k = 0; k < 16; ++k)
+      v[u][k] = *reinterpret_cast<const float2*>(
+          part + ((size_t)min(k, ksplit - 1) * M + m) * N + 2 * pc);
+  }
+  const int pos = ((cptr)seq_lens)[b] + i;
+  const int page = pos / block_size;
+  const bool in_table = pos >= 0 && page < max_blocks;
+  const int blk = in_table ? ((cptr)block_table)[(size_t)b * max_blocks + page] : -1;
   float v0[2] = {0.0f, 0.0f}, v1[2] = {0.0f, 0.0f};
 #pragma unroll
   for (int u = 0; u < 2; ++u) {
     const int p = threadIdx.x + u * blockDim.x;
     if (2 * p >= N) continue;
-    for (int z0 = 0; z0 < ksplit; z0 += 16) {
-      float2 v[16];
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      v0[u] = k < ksplit ? v0[u] + v[u][k].x : v0[u];
+      v1[u] = k < ksplit ? v1[u] + v[u][k].y : v1[u];
+    }
+    for (int z0 = 16; z0 < ksplit; z0 += 16) {
+      float2 w[16];
 #pragma unroll
       for (int k = 0; k < 16; ++k)
-        v[k] = *reinterpret_cast<const float2*>(
+        w[k] = *reinterpret_cast<const float2*>(
             part + ((size_t)min(z0 + k, ksplit - 1) * M + m) * N + 2 * p);
 #pragma unroll
       for (int k = 0; k < 16; ++k) {
-        v0[u] = z0 + k < ksplit ? v0[u] + v[k].x : v0[u];
-        v1[u] = z0 + k < ksplit ? v1[u] + v[k].y : v1[u];
+        v0[u] = z0 + k < ksplit ? v0[u] + w[k].x : v0[u];
+        v1[u] = z0 + k < ksplit ? v1[u] + w[k].y : v1[u];
       }
     }
   }
-  const int page = pos / block_size;
-  if (pos < 0 || page >= max_blocks) return;
-  const int blk = block_table[(size_t)b * max_blocks + page];
-  if (blk < 0 || blk >= num_blocks) return;
+  if (blk < 0 || blk >= num_blocks) return;  // position or page id out of range
   E* row = static_cast<E*>(pool) + ((size_t)blk * block_size + pos % block_size) * N;
 #pragma unroll
   for (int u = 0; u < 2; ++u) {
@@ -267,8 +296,11 @@ int kv_produce_ksplit(int dtype, int M, int d_model, int d_c, int d_r, int cus) 
   const int N = d_c + d_r;
   const long long tiles = (long long)((N + PJ_TN - 1) / PJ_TN) * ((M + PJ_TM - 1) / PJ_TM);
   const int nk = d_model / 32;
-  long long ks = (cus + tiles - 1) / tiles;
-  if (ks < 1) ks = 1;
+  // as many splits as keep the grid within one workgroup per compute unit,
+  // but at least enough for 512 k (16 k-steps) per split
+  long long ks = cus / tiles;
+  const long long ks_min = (nk + PJ_KMAX / 32 - 1) / (PJ_KMAX / 32);
+  if (ks < ks_min) ks = ks_min;
   if (ks > nk) ks = nk;
   const int per = (int)((nk + ks - 1) / ks);
   return (nk + per - 1) / per;
@@ -285,6 +317,7 @@ hipError_t launch_kv_produce(int dtype, const void* hidden, int d_model, const v
   if (kv_proj_mfma_supported(dtype, d_model)) {
     const int nk = d_model / 32;
     const int per = (nk + ksplit - 1) / ksplit;
+    if (ksplit < 1 || per > PJ_KMAX / 32) return hipErrorInvalidValue;  // at most 512 k a split
     const long long tiles =
         (long long)((N + PJ_TN - 1) / PJ_TN) * ((M + PJ_TM - 1) / PJ_TM) * ksplit;
     if (tiles > 0x7fffffffLL) return hipErrorInvalidValue;
