@@ -358,6 +358,21 @@ mla_status mla_validate_block_table(const int32_t* block_table, int32_t B,
                                     int32_t block_size, int32_t num_blocks,
                                     int32_t* err_flag, void* stream);
 
+/*
+ * Measurement helper.
+ *
+ * mla_stream_read: reads `bytes` of device memory at `src` once, as 16-byte
+ * non-temporal loads spread over the whole device, and XORs every 16-byte
+ * chunk into the 16 bytes at `sink` (device, 4 x uint32, updated in place
+ * with atomic XORs: sink becomes sink ^ XOR of all chunks).  It is the
+ * achievable HBM read rate that a roofline of the decode path is set beside
+ * (the pages price the method by the bytes of cache it reads: "Attention,
+ * Part 2: MQA, GQA and MLA", section "Why reading the cache is the real
+ * cost").  src and sink 16-byte aligned and bytes a multiple of 16
+ * (MLA_ERR_ALIGN otherwise); bytes == 0 launches nothing.
+ */
+mla_status mla_stream_read(const void* src, size_t bytes, void* sink, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -516,6 +516,13 @@ mla_status mla_validate_block_table(const int32_t* block_table, int32_t B, int32
                                          num_blocks, err_flag, static_cast<hipStream_t>(stream)));
 }
 
+mla_status mla_stream_read(const void* src, size_t bytes, void* sink, void* stream) {
+  if (bytes == 0) return MLA_OK;
+  if (src == nullptr || sink == nullptr) return MLA_ERR_NULL;
+  if (!aligned16(src) || !aligned16(sink) || bytes % 16 != 0) return MLA_ERR_ALIGN;
+  return hip_status(mla::launch_stream_read(src, bytes, sink, static_cast<hipStream_t>(stream)));
+}
+
 }  // extern "C"
 
 namespace {

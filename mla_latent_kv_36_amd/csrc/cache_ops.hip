@@ -1,4 +1,6 @@
-// Paged latent cache: append, gather (debug) and block-table validation.
+// Paged latent cache: append, gather (debug) and block-table validation; and a
+// streaming read of device memory (the achievable HBM read rate, a
+// measurement helper).
 //
 // Only the latent c and the decoupled rotary key k^R of a token are cached
 // ("Attention, Part 2: MQA, GQA and MLA", section "The MLA equations"), as one
@@ -108,6 +110,51 @@ hipError_t launch_gather(const void* pool, int num_blocks, const int32_t* block_
     hipLaunchKernelGGL(gather_kernel<uint16_t>, grid, dim3(64), 0, stream, (const uint8_t*)pool,
                        num_blocks, block_table, max_blocks, seq_lens, cap, block_size, row_bytes,
                        (uint8_t*)dense);
+  return hipGetLastError();
+}
+
+namespace {
+
+// Streaming read of n 16-byte chunks: thread t of T reads chunks t, t + T,
+// ... eight at a time as non-temporal loads and XORs them together; a
+// workgroup's XOR reaches the sink through the wave's lane swaps, LDS and
+// four atomic XORs.
+constexpr int SR_GRID = 256;  // workgroups: one per compute unit of the chip
+constexpr int SR_NT = 256;
+
+__global__ __launch_bounds__(SR_NT) void stream_read_kernel(const u32x4* __restrict__ x, size_t n,
+                                                            uint32_t* __restrict__ sink) {
+  const size_t T = (size_t)gridDim.x * blockDim.x;
+  size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  u32x4 acc = {0u, 0u, 0u, 0u};
+  for (; i + 7 * T < n; i += 8 * T) {
+    u32x4 v[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) v[k] = __builtin_nontemporal_load(&x[i + k * T]);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) acc ^= v[k];
+  }
+  for (; i < n; i += T) acc ^= __builtin_nontemporal_load(&x[i]);
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1)
+#pragma unroll
+    for (int c = 0; c < 4; ++c) acc[c] ^= (uint32_t)__shfl_xor((int)acc[c], off);
+  __shared__ u32x4 red[SR_NT / 64];
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = acc;
+  __syncthreads();
+  if (threadIdx.x < 4) {
+    uint32_t r = 0u;
+#pragma unroll
+    for (int w = 0; w < SR_NT / 64; ++w) r ^= red[w][threadIdx.x];
+    atomicXor(&sink[threadIdx.x], r);
+  }
+}
+
+}  // namespace
+
+hipError_t launch_stream_read(const void* src, size_t bytes, void* sink, hipStream_t stream) {
+  hipLaunchKernelGGL(stream_read_kernel, dim3(SR_GRID), dim3(SR_NT), 0, stream,
+                     static_cast<const u32x4*>(src), bytes / 16, static_cast<uint32_t*>(sink));
   return hipGetLastError();
 }
 

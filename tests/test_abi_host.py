@@ -280,6 +280,13 @@ def test_debug_helpers_validation(lib):
     assert lib.mla_validate_block_table(FAKE, 2, 4, FAKE, 64, 10, None, None) == NULL
     assert lib.mla_validate_block_table(FAKE, 2, 4, FAKE, 64, 10, FAKE + 2, None) == ALIGN
     assert lib.mla_validate_block_table(FAKE, 2, 0, FAKE, 64, 10, FAKE, None) == DIM
+    # the streaming-read helper: checks only (bytes == 0 launches nothing)
+    assert lib.mla_stream_read(FAKE, 0, FAKE, None) == OK
+    assert lib.mla_stream_read(None, 64, FAKE, None) == NULL
+    assert lib.mla_stream_read(FAKE, 64, None, None) == NULL
+    assert lib.mla_stream_read(FAKE, 72, FAKE, None) == ALIGN
+    assert lib.mla_stream_read(FAKE + 8, 64, FAKE, None) == ALIGN
+    assert lib.mla_stream_read(FAKE, 64, FAKE + 4, None) == ALIGN
 
 
 def test_binding_rejects_wrong_tensor_types(lib):
