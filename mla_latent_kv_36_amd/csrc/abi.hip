@@ -611,9 +611,13 @@ int64_t output_k(const mla_config* c, bool folded) {
   return k > 0x7fffffffLL ? 0 : k;
 }
 
+// the latent outputs are fp32; so are the per-head outputs of an fp32 configuration
+bool output_x_f32(const mla_config* c, bool folded) { return folded || c->dtype == MLA_F32; }
+
 size_t output_workspace(const mla_config* c, int M, int d_model, bool folded) {
   const int64_t K = output_k(c, folded);
-  const int ks = mla::wo_gemm_ksplit(c->dtype, M, d_model, (int)K, output_workgroups());
+  const int ks = mla::wo_gemm_ksplit(c->dtype, output_x_f32(c, folded), M, d_model, (int)K,
+                                     output_workgroups());
   return ks > 1 ? round256((size_t)ks * M * d_model * sizeof(float)) : 0;
 }
 
@@ -636,11 +640,10 @@ mla_status output_call(const mla_config* cfg, bool folded, const void* x, const 
       (workspace != nullptr && !aligned16(workspace)))
     return MLA_ERR_ALIGN;
   const int K = (int)output_k(cfg, folded);
-  const int ks = mla::wo_gemm_ksplit(cfg->dtype, M, d_model, K, output_workgroups());
+  const bool x_f32 = output_x_f32(cfg, folded);
+  const int ks = mla::wo_gemm_ksplit(cfg->dtype, x_f32, M, d_model, K, output_workgroups());
   if (ks > 1 && (workspace == nullptr || workspace_bytes < output_workspace(cfg, M, d_model, folded)))
     return MLA_ERR_WORKSPACE;
-  // the latent outputs are fp32; so are the per-head outputs of an fp32 configuration
-  const bool x_f32 = folded || cfg->dtype == MLA_F32;
   const hipStream_t s = static_cast<hipStream_t>(stream);
   return hip_status(mla::launch_wo_gemm(cfg->dtype, x_f32, x, w, y, static_cast<float*>(workspace),
                                         ks, M, d_model, K, device_shape(s, true).xcds, s));

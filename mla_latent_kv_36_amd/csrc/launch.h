@@ -91,7 +91,7 @@ hipError_t launch_rope(int dtype, void* x, const int32_t* positions, int M, int 
 // count (1 for the generic kernel).  xcds: the device's XCD count (workgroup
 // placement).
 bool wo_gemm_mfma_supported(int dtype, int N, int K);
-int wo_gemm_ksplit(int dtype, int M, int N, int K, int target_workgroups);
+int wo_gemm_ksplit(int dtype, bool x_f32, int M, int N, int K, int target_workgroups);
 hipError_t launch_wo_gemm(int dtype, bool x_f32, const void* x, const void* w, void* y,
                           float* part, int ksplit, int M, int N, int K, int xcds,
                           hipStream_t stream);

@@ -27,7 +27,11 @@
 //     and share its L2;
 //   * the k dimension is split over workgroups when the tiles alone would
 //     leave compute units idle; the splits' fp32 partial sums are then added
-//     in split order by a second kernel (deterministic).
+//     in split order by a second kernel (deterministic);
+//   * 17 to 128 bf16 token rows take a streaming form instead: all tokens in
+//     one tile and 256 weight rows per workgroup, both operands brought in by
+//     direct-to-LDS copies through a ring several chunks deep (below);
+//     up to 16 tokens take a form with no LDS (below).
 // fp32 token rows are rounded to bf16 when staged (the product is bf16 x bf16
 // with fp32 accumulation either way).  fp32 weights and other shapes take a
 // one-thread-per-output kernel.  The fold is a one-time weight preparation and
@@ -246,6 +250,128 @@ __global__ __launch_bounds__(WO_NT) void wo_stream_direct_kernel(
   }
 }
 
+// The same product for 16 < M <= 128 bf16 token rows: every token in one
+// tile, so the weight is streamed once, and 256 weight rows per workgroup, so
+// that the token rows (read again by every workgroup) are a third of the
+// bytes moved.  Workgroup (256 weight rows, k split): the k range is cut into
+// chunks of one MFMA k-step (32 k); each chunk's 256 weight rows and 128
+// token rows (clamped to M - 1) reach LDS as direct-to-LDS copies (sixteen
+// 64-byte rows per copy; 16-byte chunk c of row r at position
+// c ^ ((r >> 2) & 3), so that the 16 rows an operand reads at one k fall in
+// distinct banks) through a ring of WS_SLOTS slots, WS_SLOTS - 1 chunks ahead
+// of the MFMAs: the bytes in flight per compute unit, which bound its rate
+// at this latency, fill most of the LDS.  Wave w takes weight rows
+// 64w .. 64w+63 (4 A tiles) against the 8 token tiles (B).  Copies past the
+// split's k range re-read clamped, finite values that are not multiplied.
+constexpr int WS_TN = 256;      // weight rows per workgroup
+constexpr int WS_TM = 128;      // token rows (all of them)
+constexpr int WS_SLOTS = 6;
+constexpr int WS_ROW = 64;                              // bytes per staged row (32 k)
+constexpr int WS_SLOT = (WS_TM + WS_TN) * WS_ROW;       // 24 KiB
+constexpr int WS_COPIES = (WS_TM + WS_TN) / 16 / 4;     // copies per wave per chunk (6)
+
+template <int N_>
+__device__ __forceinline__ void wait_copies_ahead(int ahead) {
+  // this wave's copies of all but the `ahead` most recent chunks have landed
+  if (ahead >= 5) wait_vmcnt<5 * N_>();
+  else if (ahead == 4) wait_vmcnt<4 * N_>();
+  else if (ahead == 3) wait_vmcnt<3 * N_>();
+  else if (ahead == 2) wait_vmcnt<2 * N_>();
+  else if (ahead == 1) wait_vmcnt<N_>();
+  else wait_vmcnt<0>();
+}
+
+__global__ __launch_bounds__(256) void wo_stream_lds_kernel(
+    const uint16_t* __restrict__ x, const uint16_t* __restrict__ w, uint16_t* __restrict__ y,
+    float* __restrict__ part, int M, int N, int K, int steps_per_split, int xcds) {
+  extern __shared__ __align__(16) uint8_t ring[];  // [WS_SLOTS][token rows, then weight rows][64 B]
+  const int ntn = (N + WS_TN - 1) / WS_TN;
+  const int total = (int)gridDim.x;
+  const int full = total - total % xcds;
+  const int i = blockIdx.x;
+  const int t = i < full ? (i % xcds) * (full / xcds) + i / xcds : i;
+  const int n0 = (t % ntn) * WS_TN;
+  const int z = t / ntn;
+  const int nk = K / 32;
+  const int s_begin = z * steps_per_split;
+  const int nchunks = min(steps_per_split, nk - s_begin);  // one k-step per chunk
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: scalar branches
+  const int l16 = lane & 15, g = lane >> 4;
+  const uint32_t ring_base = (uint32_t)(uintptr_t)ring;
+
+  // copies of chunk c into slot c % WS_SLOTS: staged row q < 128 is token row
+  // q, q >= 128 weight row n0 + q - 128; copy j of wave w fills rows
+  // 16(w + 4j) .. +15, lane l row 16(w + 4j) + (l >> 2), position l & 3
+  const uint8_t* xb = reinterpret_cast<const uint8_t*>(x);
+  const uint8_t* wb = reinterpret_cast<const uint8_t*>(w + (size_t)n0 * K);
+  auto issue = [&](int c) {
+    const int kbase = 32 * (s_begin + c);
+    const uint32_t slot = ring_base + (c % WS_SLOTS) * WS_SLOT;
+#pragma unroll
+    for (int j = 0; j < WS_COPIES; ++j) {
+      const int q0 = 16 * (wave + 4 * j);       // first staged row of this copy (uniform)
+      const int q = q0 + (lane >> 2);           // this lane's row
+      const int ch = (lane & 3) ^ ((q >> 2) & 3);  // the chunk that belongs at its position
+      const int k = kbase + 8 * ch;
+      if (q0 < WS_TM) {
+        const uint32_t voff = (uint32_t)(((size_t)min(q, M - 1) * K + k) * 2);
+        copy16_to_lds(xb, voff, slot + q0 * WS_ROW);
+      } else {
+        const uint32_t voff = (uint32_t)(((size_t)min(q - WS_TM, N - 1 - n0) * K + k) * 2);
+        copy16_to_lds(wb, voff, slot + q0 * WS_ROW);
+      }
+    }
+  };
+
+  f32x4 acc[4][WS_TM / 16];
+#pragma unroll
+  for (int at = 0; at < 4; ++at)
+#pragma unroll
+    for (int j = 0; j < WS_TM / 16; ++j) acc[at][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+#pragma unroll
+  for (int c = 0; c < WS_SLOTS - 1; ++c)
+    if (c < nchunks) issue(c);
+  for (int c = 0; c < nchunks; ++c) {
+    wait_copies_ahead<WS_COPIES>(min(WS_SLOTS - 2, nchunks - 1 - c));
+    lds_barrier();  // every wave's copies of chunk c; every wave done with chunk c-1
+    if (c + WS_SLOTS - 1 < nchunks) issue(c + WS_SLOTS - 1);  // into chunk c-1's slot
+    const uint8_t* sl = ring + (c % WS_SLOTS) * WS_SLOT;
+    // operand rows R read here have (R >> 2) & 3 == (l16 >> 2) & 3 (R = 16 k + l16)
+    const int off = 16 * (g ^ ((l16 >> 2) & 3));
+    bf16x8 a[4];
+#pragma unroll
+    for (int at = 0; at < 4; ++at)
+      a[at] = *reinterpret_cast<const bf16x8*>(sl + (WS_TM + 64 * wave + 16 * at + l16) * WS_ROW + off);
+#pragma unroll
+    for (int j = 0; j < WS_TM / 16; ++j) {
+      const bf16x8 b = *reinterpret_cast<const bf16x8*>(sl + (16 * j + l16) * WS_ROW + off);
+#pragma unroll
+      for (int at = 0; at < 4; ++at) acc[at][j] = mfma16(a[at], b, acc[at][j]);
+    }
+  }
+  // D: lane l holds token 16j + (l & 15), outputs 64w + 16at + 4(l >> 4) .. +3
+#pragma unroll
+  for (int at = 0; at < 4; ++at) {
+    const int n = n0 + 64 * wave + 16 * at + 4 * g;
+    if (n >= N) continue;
+#pragma unroll
+    for (int j = 0; j < WS_TM / 16; ++j) {
+      const int m = 16 * j + l16;
+      if (m >= M) continue;
+      if (y != nullptr) {
+        u16x4 h;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) h[e] = f32_to_bf16(acc[at][j][e]);
+        *reinterpret_cast<u16x4*>(y + (size_t)m * N + n) = h;
+      } else {
+        *reinterpret_cast<f32x4*>(part + ((size_t)z * M + m) * N + n) = acc[at][j];
+      }
+    }
+  }
+}
+
 // y[m, n .. n+3] = sum over splits z (in order) of part[z, m, n .. n+3],
 // rounded to bf16; one thread per 4 outputs.  The loads of up to 16 splits
 // are issued (on clamped indices) before the first is added.
@@ -341,10 +467,30 @@ bool wo_gemm_mfma_supported(int dtype, int N, int K) {
   return dtype == 1 && K > 0 && K % 32 == 0 && N > 0 && N % 4 == 0;
 }
 
-int wo_gemm_ksplit(int dtype, int M, int N, int K, int target_workgroups) {
+// bf16 token rows, 16 < M <= 128: the weight-streaming kernel with every token
+// in one tile (its 144 KiB of LDS allow one workgroup per compute unit, and a
+// compute unit streams at the rate its bytes in flight allow: measured, half
+// as many workgroups with twice the k range each run slower; the staged rows
+// of a workgroup lie within 2^32 bytes of its first)
+static bool wo_stream_lds_fits(int dtype, bool x_f32, int M, int N, int K) {
+  return wo_gemm_mfma_supported(dtype, N, K) && !x_f32 && M > 16 && M <= WS_TM &&
+         (long long)WS_TM * K * 2 < (1LL << 32) && (long long)WS_TN * K * 2 < (1LL << 32);
+}
+
+int wo_gemm_ksplit(int dtype, bool x_f32, int M, int N, int K, int target_workgroups) {
   if (!wo_gemm_mfma_supported(dtype, N, K) || M <= 0) return 1;
   // up to 16 tokens: the direct kernel, WO_DC chunks of 4 k steps per split
   if (M <= 16) return (K / 32 + 4 * WO_DC - 1) / (4 * WO_DC);
+  if (wo_stream_lds_fits(dtype, x_f32, M, N, K)) {
+    // one workgroup per compute unit (target_workgroups counts two)
+    const long long tiles = (N + WS_TN - 1) / WS_TN;
+    const int nk = K / 32;
+    long long ks = (target_workgroups / 2) / tiles;
+    if (ks < 1) ks = 1;
+    if (ks > nk) ks = nk;
+    const int per = (int)((nk + ks - 1) / ks);
+    return (nk + per - 1) / per;
+  }
   const long long tiles = (long long)((N + WO_TN - 1) / WO_TN) * ((M + WO_TM - 1) / WO_TM);
   const int nk = K / 32;
   long long ks = (target_workgroups + tiles - 1) / tiles;
@@ -374,6 +520,23 @@ hipError_t launch_wo_gemm(int dtype, bool x_f32, const void* x, const void* w, v
       hipLaunchKernelGGL(wo_stream_direct_kernel<uint16_t>, dim3((unsigned)tiles), dim3(WO_NT), 0,
                          stream, static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(w),
                          yd, part, M, N, K, 4 * WO_DC, xcds);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || ksplit == 1) return e;
+    const size_t quads = (size_t)M * N / 4;
+    hipLaunchKernelGGL(wo_finish_kernel, dim3((unsigned)((quads + 255) / 256)), dim3(256), 0,
+                       stream, part, static_cast<uint16_t*>(y), M, N, ksplit);
+    return hipGetLastError();
+  }
+  if (wo_stream_lds_fits(dtype, x_f32, M, N, K)) {
+    const int nk = K / 32;
+    const int per = (nk + ksplit - 1) / ksplit;
+    const long long tiles = (long long)((N + WS_TN - 1) / WS_TN) * ksplit;
+    if (tiles > 0x7fffffffLL) return hipErrorInvalidValue;
+    if (ksplit > 1 && part == nullptr) return hipErrorInvalidValue;
+    uint16_t* yd = ksplit == 1 ? static_cast<uint16_t*>(y) : nullptr;
+    hipLaunchKernelGGL(wo_stream_lds_kernel, dim3((unsigned)tiles), dim3(256),
+                       (size_t)WS_SLOTS * WS_SLOT, stream, static_cast<const uint16_t*>(x),
+                       static_cast<const uint16_t*>(w), yd, part, M, N, K, per, xcds);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || ksplit == 1) return e;
     const size_t quads = (size_t)M * N / 4;

@@ -7,8 +7,10 @@ on the same seeded inputs:
 * mla_fold_uv_o (W^UV folded into W^O): per element, the same bound;
 * mla_o_proj_folded (the folded matrix on the fp32 latent outputs, rounded to
   bf16 as they are read): within 2e-2 of max|y|, the bound of the bf16 path;
-* MFMA kernel with and without a k split, ragged token and output tiles, the
-  generic kernel (widths that are not a multiple of 32 or 4) and fp32;
+* MFMA kernels with and without a k split (up to 16 tokens; 17 to 128
+  tokens, streamed with every token in one tile), ragged token and output
+  tiles, a chunk shorter than its k-steps, the generic kernel (widths that are
+  not a multiple of 32 or 4) and fp32;
 * the k-split partial sums are added in a fixed order: reruns are bit-exact;
 * at the V2-scale widths and full size, with the launch configuration the
   benchmark times: every output of W^O, sampled rows of the folded matrix and
@@ -31,8 +33,12 @@ TDT = {"bf16": torch.bfloat16, "f32": torch.float32}
 CASES = {
     # MFMA kernel, k split: 12 tokens, the V2-scale heads, d = 5120
     "v2_reduced": V2_MULTI.scaled(B=3, T=4),
-    # two token tiles, the second ragged (70 tokens), output tile ragged
+    # the weight-streaming kernel (16 < M <= 128 bf16 tokens, every token in
+    # one tile): 70 tokens, the output tile ragged (200 = 3 x 64 + 8)
     "v2_many_tokens": V2_MULTI.scaled(B=70, T=1, d_model=200),
+    # the same kernel at its smallest M, k = 288 (9 k-steps: splits of one
+    # step, a chunk shorter than its 4 k-steps), output tile ragged
+    "v2_stream_17": V2_MULTI.scaled(B=17, T=1, H=3, d_v=96, d_model=136),
     # generic kernel: an output width that is not a multiple of 4
     "bf16_odd_width": V2_MULTI.scaled(B=2, T=2, d_model=198),
     # generic kernel: k = H * d_v = 30 is not a multiple of 32
@@ -155,6 +161,14 @@ def test_o_proj_rerun_bit_exact():
     assert mla.mla_o_proj_workspace_size(cfg, w.B * w.T, w.d_model) > 0   # k is split
     oi = make_output_inputs(w)
     note("o_proj rerun")
+    a, b = _o_proj(w, oi), _o_proj(w, oi)
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+def test_o_proj_stream_rerun_bit_exact():
+    w = CASES["v2_many_tokens"]
+    oi = make_output_inputs(w)
+    note("o_proj stream rerun")
     a, b = _o_proj(w, oi), _o_proj(w, oi)
     assert torch.equal(a.view(torch.int16), b.view(torch.int16))
 
