@@ -178,12 +178,14 @@ def streaming_read(torch, mla, mib: int = 2048, reps: int = 20) -> dict:
         torch.cuda.synchronize()
         return sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(reps))[reps // 2]
 
-    ms_hip = timed(lambda: mla.mla_stream_read(x, sink))
+    ms_hip = timed(lambda: mla.mla_stream_read(x, sink, 0))
+    ms_lds = timed(lambda: mla.mla_stream_read(x, sink, 1))
     ms_read = timed(lambda: x.sum())
     ms_copy = timed(lambda: y.copy_(x))
     del x, y, sink
     return {"read_GBps": (mib << 20) / (ms_hip * 1e-3) / 1e9,
-            "read_kernel": "mla_stream_read (16-byte non-temporal loads, 256 x 256 threads)",
+            "read_kernel": "mla_stream_read mode 0 (16-byte non-temporal loads, 256 x 256 threads)",
+            "read_direct_to_lds_GBps": (mib << 20) / (ms_lds * 1e-3) / 1e9,
             "torch_sum_GBps": (mib << 20) / (ms_read * 1e-3) / 1e9,
             "copy_GBps": 2 * (mib << 20) / (ms_copy * 1e-3) / 1e9,
             "bytes": mib << 20, "copy_kernel": "torch copy_ (fp32), read + written bytes",
@@ -435,8 +437,9 @@ def main() -> int:
     ap.add_argument("--no-extra", action="store_true",
                     help="skip the other workloads' mla_decode timings")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
-                    help="only run a plain device copy of this many MiB five times "
-                         "(the known-size reference for HBM byte counters) and exit")
+                    help="only run a plain device copy of this many MiB and the "
+                         "library's streaming read of it in both modes, five times "
+                         "each (known-size references for HBM byte counters), and exit")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -451,15 +454,23 @@ def main() -> int:
     import torch
 
     if args.copy_probe_mib > 0:
-        # One elementwise kernel per call that reads n bytes and writes n bytes.
+        # Kernels of known bytes for the HBM byte counters: one elementwise
+        # kernel per call that reads n bytes and writes n bytes, then the
+        # library's streaming read of n bytes through registers (mode 0) and
+        # through direct-to-LDS copies (mode 1, the decode kernel's path).
         n = args.copy_probe_mib << 20
         src = torch.ones(n // 4, dtype=torch.float32, device="cuda")
         dst = torch.empty_like(src)
         for _ in range(5):
             torch.mul(src, 1.0, out=dst)
+        from mla_latent_kv_36_amd import binding as mla
+        sink = torch.zeros(4, dtype=torch.int32, device="cuda")
+        for mode in (0, 1):
+            for _ in range(5):
+                mla.mla_stream_read(src, sink, mode)
         torch.cuda.synchronize()
         print(json.dumps({"copy_probe_bytes_read": n, "copy_probe_bytes_written": n,
-                          "launches": 5}))
+                          "stream_read_bytes": n, "launches": 5}))
         return 0
 
     from mla_latent_kv_36_amd import binding as mla

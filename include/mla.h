@@ -361,17 +361,23 @@ mla_status mla_validate_block_table(const int32_t* block_table, int32_t B,
 /*
  * Measurement helper.
  *
- * mla_stream_read: reads `bytes` of device memory at `src` once, as 16-byte
- * non-temporal loads spread over the whole device, and XORs every 16-byte
- * chunk into the 16 bytes at `sink` (device, 4 x uint32, updated in place
- * with atomic XORs: sink becomes sink ^ XOR of all chunks).  It is the
- * achievable HBM read rate that a roofline of the decode path is set beside
- * (the pages price the method by the bytes of cache it reads: "Attention,
- * Part 2: MQA, GQA and MLA", section "Why reading the cache is the real
- * cost").  src and sink 16-byte aligned and bytes a multiple of 16
- * (MLA_ERR_ALIGN otherwise); bytes == 0 launches nothing.
+ * mla_stream_read: reads `bytes` of device memory at `src` once and XORs every
+ * 16-byte chunk into the 16 bytes at `sink` (device, 4 x uint32, updated in
+ * place with atomic XORs: sink becomes sink ^ XOR of all chunks).  It gives
+ * the achievable HBM read rate that a roofline of the decode path is set
+ * beside (the pages price the method by the bytes of cache it reads:
+ * "Attention, Part 2: MQA, GQA and MLA", section "Why reading the cache is
+ * the real cost"), and a kernel of known bytes to calibrate memory-traffic
+ * counters against.  mode 0: 16-byte non-temporal loads into registers from
+ * 256 x 256 threads striding over the buffer.  mode 1: direct-to-LDS copies,
+ * the path the decode kernel streams the cache through: each of 256
+ * workgroups streams a contiguous range in 1 KiB copies through a ring in
+ * LDS (a tail under 1 KiB is read with plain loads).  src and sink 16-byte
+ * aligned and bytes a multiple of 16 (MLA_ERR_ALIGN otherwise), mode 0 or 1
+ * (MLA_ERR_DIM otherwise); bytes == 0 launches nothing.
  */
-mla_status mla_stream_read(const void* src, size_t bytes, void* sink, void* stream);
+mla_status mla_stream_read(const void* src, size_t bytes, void* sink, int32_t mode,
+                           void* stream);
 
 #ifdef __cplusplus
 }

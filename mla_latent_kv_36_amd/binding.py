@@ -63,7 +63,7 @@ _SIGNATURES = {
     "mla_out_proj": (_I, [_CFG, _P, _P, _P, _I, _P]),
     "mla_gather_rows": (_I, [_CFG, _P, _I, _P, _I, _P, _I, _I, _P, _P]),
     "mla_validate_block_table": (_I, [_P, _I, _I, _P, _I, _I, _P, _P]),
-    "mla_stream_read": (_I, [_P, ctypes.c_size_t, _P, _P]),
+    "mla_stream_read": (_I, [_P, ctypes.c_size_t, _P, _I, _P]),
     "mla_kv_produce_workspace_size": (ctypes.c_size_t, [_CFG, _I, _I]),
     "mla_kv_produce": (_I, [_CFG, _P, _I, _P, _P, ctypes.c_float, _P, _I, _P, _I, _P, _I, _I,
                             _I, _P, ctypes.c_size_t, _P]),
@@ -260,15 +260,16 @@ def mla_validate_block_table(block_table: torch.Tensor, seq_lens: torch.Tensor,
                                            num_blocks, _ptr(err_flag), _stream(stream)))
 
 
-def mla_stream_read(src: torch.Tensor, sink: torch.Tensor, stream=None) -> None:
+def mla_stream_read(src: torch.Tensor, sink: torch.Tensor, mode: int = 0, stream=None) -> None:
     """Read every byte of the contiguous device tensor src once and XOR its
-    16-byte chunks into sink (a device tensor of 16 bytes, updated in place)."""
+    16-byte chunks into sink (a device tensor of 16 bytes, updated in place);
+    mode 0: loads into registers, 1: direct-to-LDS copies."""
     if not (src.is_cuda and sink.is_cuda and src.is_contiguous() and sink.is_contiguous()):
         raise ValueError("mla_stream_read: contiguous device tensors expected")
     if sink.numel() * sink.element_size() < 16:
         raise ValueError("mla_stream_read: sink must hold 16 bytes")
     _check(load().mla_stream_read(_ptr(src), src.numel() * src.element_size(), _ptr(sink),
-                                  _stream(stream)))
+                                  mode, _stream(stream)))
 
 
 def mla_kv_produce_workspace_size(cfg: MlaConfig, M: int, d_model: int) -> int:

@@ -90,8 +90,12 @@ int64_t groups_of(const mla_config* c, int T) { return (int64_t)T * ((c->n_heads
 // MFMA kernel, plain plan: units of work are (64-row query group, 32-row unit
 // of the cache).  The kernel's LDS ring fits one workgroup per compute unit,
 // so aim for one wave of workgroups over the chip, but keep at least 8 units
-// per workgroup so the partial outputs (128 KiB per workgroup) stay well below
-// the cache bytes read.
+// per workgroup.  A (sequence, split) range of U units is read from HBM once
+// (36,864 U bytes) while each of its T*H query rows writes a bf16 partial
+// that the merge reads back: 2 * T*H * 1,024 bytes of round trip.  At the
+// minimum U = 8 and T*H = 128 that is 0.89 of the range's cache bytes; at
+// the V3 shape (U = 17) 0.42, which the counters confirm (16.8 MB written,
+// then read, against 75.5 MB of cache).
 int mfma_splits(const mla_config* c, int T, int gran_max, int64_t gran_total, int cus) {
   const int64_t work = gran_total * groups_of(c, T);
   int64_t chunk = (work + cus - 1) / cus;
@@ -516,11 +520,14 @@ mla_status mla_validate_block_table(const int32_t* block_table, int32_t B, int32
                                          num_blocks, err_flag, static_cast<hipStream_t>(stream)));
 }
 
-mla_status mla_stream_read(const void* src, size_t bytes, void* sink, void* stream) {
+mla_status mla_stream_read(const void* src, size_t bytes, void* sink, int32_t mode,
+                           void* stream) {
+  if (mode != 0 && mode != 1) return MLA_ERR_DIM;
   if (bytes == 0) return MLA_OK;
   if (src == nullptr || sink == nullptr) return MLA_ERR_NULL;
   if (!aligned16(src) || !aligned16(sink) || bytes % 16 != 0) return MLA_ERR_ALIGN;
-  return hip_status(mla::launch_stream_read(src, bytes, sink, static_cast<hipStream_t>(stream)));
+  return hip_status(
+      mla::launch_stream_read(src, bytes, sink, mode == 1, static_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

@@ -150,11 +150,81 @@ __global__ __launch_bounds__(SR_NT) void stream_read_kernel(const u32x4* __restr
   }
 }
 
+// The same read through direct-to-LDS copies: workgroup i streams the 1 KiB
+// pieces [P i / G, P (i+1) / G) of the buffer's P whole pieces, wave w taking
+// every fourth; each wave keeps SR_RING copies in flight through its own ring
+// of SR_RING 1 KiB slots, and XORs a slot's 16 bytes per lane once it has
+// landed, before the slot takes the next copy.  Workgroup 0 reads the tail
+// under 1 KiB with plain loads.
+constexpr int SR_RING = 8;
+
+template <int N>
+__device__ __forceinline__ void sr_wait(int ahead) {
+  // this wave's copies have landed except the `ahead` most recent (< N)
+  if (ahead >= N - 1) wait_vmcnt<N - 1>();
+  else if (ahead == 6) wait_vmcnt<6>();
+  else if (ahead == 5) wait_vmcnt<5>();
+  else if (ahead == 4) wait_vmcnt<4>();
+  else if (ahead == 3) wait_vmcnt<3>();
+  else if (ahead == 2) wait_vmcnt<2>();
+  else if (ahead == 1) wait_vmcnt<1>();
+  else wait_vmcnt<0>();
+}
+
+__global__ __launch_bounds__(SR_NT) void stream_read_lds_kernel(const uint8_t* __restrict__ x,
+                                                                size_t bytes,
+                                                                uint32_t* __restrict__ sink) {
+  __shared__ __align__(16) uint8_t ring[SR_NT / 64][SR_RING][1024];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform
+  const size_t P = bytes >> 10;
+  const size_t p0 = P * blockIdx.x / gridDim.x, p1 = P * (blockIdx.x + 1) / gridDim.x;
+  // this wave's pieces: p0 + wave + 4k, k < n
+  const long long n = p1 > p0 + wave ? (long long)((p1 - p0 - wave + 3) / 4) : 0;
+  const uint32_t base = (uint32_t)(uintptr_t)&ring[wave][0][0];
+  auto issue = [&](long long k) {
+    copy16_to_lds(x + ((p0 + wave + 4 * k) << 10), (uint32_t)lane * 16,
+                  base + (uint32_t)(k % SR_RING) * 1024);
+  };
+  u32x4 acc = {0u, 0u, 0u, 0u};
+  for (long long k = 0; k < SR_RING && k < n; ++k) issue(k);
+  for (long long k = 0; k < n; ++k) {
+    sr_wait<SR_RING>((int)min((long long)SR_RING - 1, n - 1 - k));
+    acc ^= *reinterpret_cast<const u32x4*>(&ring[wave][k % SR_RING][16 * lane]);
+    // the read has completed before the slot takes its next copy
+    __builtin_amdgcn_s_waitcnt((0x7 << 4) | 0xF | (3 << 14));  // lgkmcnt(0)
+    if (k + SR_RING < n) issue(k + SR_RING);
+  }
+  if (blockIdx.x == 0) {
+    const size_t t0 = P << 6, tn = bytes >> 4;  // 16-byte chunks of the tail
+    const u32x4* xc = reinterpret_cast<const u32x4*>(x);
+    for (size_t c = t0 + threadIdx.x; c < tn; c += SR_NT) acc ^= xc[c];
+  }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1)
+#pragma unroll
+    for (int c = 0; c < 4; ++c) acc[c] ^= (uint32_t)__shfl_xor((int)acc[c], off);
+  __shared__ u32x4 red[SR_NT / 64];
+  if (lane == 0) red[wave] = acc;
+  __syncthreads();
+  if (threadIdx.x < 4) {
+    uint32_t r = 0u;
+#pragma unroll
+    for (int w = 0; w < SR_NT / 64; ++w) r ^= red[w][threadIdx.x];
+    atomicXor(&sink[threadIdx.x], r);
+  }
+}
+
 }  // namespace
 
-hipError_t launch_stream_read(const void* src, size_t bytes, void* sink, hipStream_t stream) {
-  hipLaunchKernelGGL(stream_read_kernel, dim3(SR_GRID), dim3(SR_NT), 0, stream,
-                     static_cast<const u32x4*>(src), bytes / 16, static_cast<uint32_t*>(sink));
+hipError_t launch_stream_read(const void* src, size_t bytes, void* sink, bool lds,
+                              hipStream_t stream) {
+  if (lds)
+    hipLaunchKernelGGL(stream_read_lds_kernel, dim3(SR_GRID), dim3(SR_NT), 0, stream,
+                       static_cast<const uint8_t*>(src), bytes, static_cast<uint32_t*>(sink));
+  else
+    hipLaunchKernelGGL(stream_read_kernel, dim3(SR_GRID), dim3(SR_NT), 0, stream,
+                       static_cast<const u32x4*>(src), bytes / 16, static_cast<uint32_t*>(sink));
   return hipGetLastError();
 }
 

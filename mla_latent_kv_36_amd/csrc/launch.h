@@ -100,8 +100,9 @@ bool fold_uv_o_supported(int d_v);
 hipError_t launch_fold_uv_o(int dtype, const void* w_uv, const void* w_o, void* w_fold, int H,
                             int d_v, int d_c, int d, hipStream_t stream);
 // Reads bytes (a multiple of 16) at src once and XORs the 16-byte chunks into
-// the 4 x uint32 at sink (atomically).
-hipError_t launch_stream_read(const void* src, size_t bytes, void* sink, hipStream_t stream);
+// the 4 x uint32 at sink (atomically); lds: through direct-to-LDS copies.
+hipError_t launch_stream_read(const void* src, size_t bytes, void* sink, bool lds,
+                              hipStream_t stream);
 hipError_t launch_validate(const int32_t* block_table, int B, int max_blocks,
                            const int32_t* seq_lens, int block_size, int num_blocks,
                            int32_t* err_flag, hipStream_t stream);

@@ -281,12 +281,15 @@ def test_debug_helpers_validation(lib):
     assert lib.mla_validate_block_table(FAKE, 2, 4, FAKE, 64, 10, FAKE + 2, None) == ALIGN
     assert lib.mla_validate_block_table(FAKE, 2, 0, FAKE, 64, 10, FAKE, None) == DIM
     # the streaming-read helper: checks only (bytes == 0 launches nothing)
-    assert lib.mla_stream_read(FAKE, 0, FAKE, None) == OK
-    assert lib.mla_stream_read(None, 64, FAKE, None) == NULL
-    assert lib.mla_stream_read(FAKE, 64, None, None) == NULL
-    assert lib.mla_stream_read(FAKE, 72, FAKE, None) == ALIGN
-    assert lib.mla_stream_read(FAKE + 8, 64, FAKE, None) == ALIGN
-    assert lib.mla_stream_read(FAKE, 64, FAKE + 4, None) == ALIGN
+    for mode in (0, 1):
+        assert lib.mla_stream_read(FAKE, 0, FAKE, mode, None) == OK
+        assert lib.mla_stream_read(None, 64, FAKE, mode, None) == NULL
+        assert lib.mla_stream_read(FAKE, 64, None, mode, None) == NULL
+        assert lib.mla_stream_read(FAKE, 72, FAKE, mode, None) == ALIGN
+        assert lib.mla_stream_read(FAKE + 8, 64, FAKE, mode, None) == ALIGN
+        assert lib.mla_stream_read(FAKE, 64, FAKE + 4, mode, None) == ALIGN
+    assert lib.mla_stream_read(FAKE, 64, FAKE, 2, None) == DIM
+    assert lib.mla_stream_read(FAKE, 64, FAKE, -1, None) == DIM
 
 
 def test_binding_rejects_wrong_tensor_types(lib):
