@@ -99,6 +99,10 @@ CASES = {
                         table="permuted"), None),
     # causal multi-token queries (G = 8 groups, K = 32 items per group)
     "multi_token": (V2_MULTI.scaled(name="bal_multi", seed=9102, B=6, N=900, var_len=True), None),
+    # 80 heads and 3 causal tokens: each token's second 64-row group is
+    # partial (G = 6 groups, K = 42 items per group)
+    "partial_groups": (V3.scaled(name="bal_h80", seed=9103, B=7, T=3, H=80, N=1100,
+                                 var_len=True, causal=True, table="permuted"), None),
 }
 
 
@@ -114,7 +118,7 @@ def test_balanced_plan_matches_oracle_and_table(name):
     cfg = cfg_of(w)
     B, T = bt.q_abs.shape[:2]
     cap = int(seq_lens.max())
-    K = 256 // (T * w.H // 64)
+    K = 256 // (T * -(-w.H // 64))  # 64-row groups: ceil(H / 64) per new token
     assert K > B and mla.mla_decode_num_splits(cfg, B, T, cap, 0) == K
     o, lse, ws = _run(w, bt, pool_after, seq_lens)
     # the table in the workspace tail, after the bf16 partial outputs and the

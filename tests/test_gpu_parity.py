@@ -162,7 +162,10 @@ def test_step_parity(name):
     # zero-padded weight rows (104: second round, 40: first round) and value
     # widths that are not a multiple of 16
     ("v3", 300, {}), ("v3", 300, {"d_n": 104, "d_v": 100}),
-    ("v3", 290, {"d_n": 40, "d_v": 64}), ("v2_multi", 517, {})])
+    ("v3", 290, {"d_n": 40, "d_v": 64}), ("v2_multi", 517, {}),
+    # just past the wide kernel's threshold: 257 rows (one 256-row workgroup
+    # and one of a single row), 20 heads, a 32-wide rotary part
+    ("v3", 257, {"H": 20, "d_r": 32, "d_n": 64})])
 def test_projections_elementwise(name, M, over):
     """mla_absorb_q and mla_out_proj alone, with M rows ragged against the
     kernels' 16-row tiles and 64-row workgroups.  Each output element is held
