@@ -228,6 +228,45 @@ mla_status mla_decode_noalloc(const mla_config* cfg, const void* q_abs, const vo
 size_t mla_decode_noalloc_scratch_bytes(void);
 
 /*
+ * mla_decode_fused -- mla_decode's split-KV attention and its log-sum-exp
+ * merge in ONE kernel launch, for batches of variable-length sequences
+ * ("Research on MLA": the fused, variable-length and megakernel decoders it
+ * lists; "Attention, Part 2: MQA, GQA and MLA", section "Does a smaller cache
+ * make writing faster?": once the cache is small, the fixed cost of each step
+ * counts).  Persistent workgroups (at most one per compute unit) take work
+ * items -- a 64-row query group against one split of one sequence, under the
+ * same plain or balanced plan as mla_decode -- from an on-device queue; the
+ * split that arrives last in its group hands the group's merge to whichever
+ * workgroups run out of work items.  A sequence whose rows fit one split is
+ * written directly.  Same arguments and results as mla_decode (rounding
+ * aside: partials are merged in split order, as there) for the bf16 shape
+ * with d_c = 512, d_rope = 64 and 64-row pages; any other config gives
+ * MLA_ERR_DIM, as does a batch with more than 3,840 (sequence, 64-row group)
+ * pairs, where mla_decode_fused_workspace_size returns (size_t)-1.
+ *
+ * workspace: device memory of at least mla_decode_fused_workspace_size(...)
+ * bytes for the same arguments (MLA_ERR_WORKSPACE otherwise; never 0).  Its
+ * first mla_decode_fused_counter_bytes() bytes (256 KiB) hold the queue's
+ * counters and must be zero when a call starts: fill them with zeros once,
+ * after allocating the workspace; every completed call leaves them zero, so
+ * calls ordered on one stream can reuse the workspace for any shape.  Calls
+ * that overlap in time on one workspace race.  The rest of the workspace is
+ * scratch.  The 32-bit word at byte offset 512 is an error word: bit 0 set
+ * means a merge waited past its bound (only a device that stalls could cause
+ * it) and some rows were not written; zero the counters again after that.
+ */
+size_t mla_decode_fused_workspace_size(const mla_config* cfg, int32_t B, int32_t T,
+                                       int32_t max_seq_len_host, int64_t total_tokens_host,
+                                       int32_t num_splits);
+size_t mla_decode_fused_counter_bytes(void);
+mla_status mla_decode_fused(const mla_config* cfg, const void* q_abs, const void* pool,
+                            int32_t num_blocks, const int32_t* block_table, int32_t max_blocks,
+                            const int32_t* seq_lens, int32_t max_seq_len_host, int32_t B,
+                            int32_t T, int32_t causal, int32_t num_splits,
+                            int64_t total_tokens_host, void* workspace, size_t workspace_bytes,
+                            float* o_lat, float* lse, void* stream);
+
+/*
  * mla_out_proj -- output-side up-projection, applied once per head after the
  * latent-space sum ("Attention, Part 2", section "The trick that makes it fast":
  * W_uv(h) is applied just once at the end).

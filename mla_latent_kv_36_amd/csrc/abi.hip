@@ -442,6 +442,90 @@ mla_status mla_decode(const mla_config* cfg, const void* q_abs, const void* pool
 
 size_t mla_decode_noalloc_scratch_bytes(void) { return kScratchBytes; }
 
+// Workspace of the one-launch decode: the counter region (zero on entry), the
+// per-group merge records, the balanced plan's table, then the partials as
+// for mla_decode; each region rounded up to 256 bytes.
+struct FusedLayout {
+  size_t rec, table, part_o, part_lse, total;
+};
+static bool fused_layout(const mla_config* cfg, int B, int T, const Plan& pl, FusedLayout* L) {
+  const int64_t BG = (int64_t)B * groups_of(cfg, T);
+  if (BG > mla::kQueueMaxGroups) return false;
+  L->rec = mla::kQueueCounterBytes;
+  L->table = L->rec + round256((size_t)BG * 2 * sizeof(int32_t));
+  L->part_o = L->table + round256((size_t)B * 4 * sizeof(int32_t));
+  size_t lse_off = 0;
+  const size_t pb = pl.splits > 1 ? partial_bytes(cfg, B, T, pl, &lse_off, nullptr) : 0;
+  L->part_lse = L->part_o + lse_off;
+  L->total = L->part_o + pb;
+  return true;
+}
+
+size_t mla_decode_fused_workspace_size(const mla_config* cfg, int32_t B, int32_t T,
+                                       int32_t max_seq_len_host, int64_t total_tokens_host,
+                                       int32_t num_splits) {
+  if (check_cfg(cfg) != MLA_OK || B < 0 || T < 1 || max_seq_len_host < 0 || num_splits < 0 ||
+      !use_mfma(cfg, T))
+    return (size_t)-1;
+  const Plan pl = make_plan(cfg, B, T, max_seq_len_host, total_tokens_host, num_splits,
+                            device_shape(nullptr, false));
+  FusedLayout L;
+  if (!fused_layout(cfg, B, T, pl, &L)) return (size_t)-1;
+  return L.total;
+}
+
+size_t mla_decode_fused_counter_bytes(void) { return mla::kQueueCounterBytes; }
+
+mla_status mla_decode_fused(const mla_config* cfg, const void* q_abs, const void* pool,
+                            int32_t num_blocks, const int32_t* block_table, int32_t max_blocks,
+                            const int32_t* seq_lens, int32_t max_seq_len_host, int32_t B,
+                            int32_t T, int32_t causal, int32_t num_splits,
+                            int64_t total_tokens_host, void* workspace, size_t workspace_bytes,
+                            float* o_lat, float* lse, void* stream) {
+  bool work;
+  mla_status st = check_decode(cfg, q_abs, pool, num_blocks, block_table, max_blocks, seq_lens,
+                               max_seq_len_host, B, T, causal, num_splits, o_lat, lse, &work);
+  if (st != MLA_OK) return st;
+  if (!use_mfma(cfg, T)) return MLA_ERR_DIM;
+  if (!work) return MLA_OK;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const DeviceShape dev = device_shape(s, true);
+  const Plan pl = make_plan(cfg, B, T, max_seq_len_host, total_tokens_host, num_splits, dev);
+  FusedLayout L;
+  if (!fused_layout(cfg, B, T, pl, &L)) return MLA_ERR_DIM;
+  if (workspace == nullptr || workspace_bytes < L.total) return MLA_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return MLA_ERR_ALIGN;
+  char* ws = static_cast<char*>(workspace);
+
+  mla::DecodeParams p{};
+  p.q_abs = q_abs;
+  p.pool = pool;
+  p.block_table = block_table;
+  p.seq_lens = seq_lens;
+  p.o_lat = o_lat;
+  p.lse = lse;
+  p.part_o = pl.splits > 1 ? ws + L.part_o : nullptr;
+  p.part_lse = pl.splits > 1 ? reinterpret_cast<float*>(ws + L.part_lse) : nullptr;
+  p.part_bf16 = 1;
+  p.B = B;
+  p.T = T;
+  p.H = cfg->n_heads;
+  p.d_c = cfg->d_c;
+  p.d_r = cfg->d_rope;
+  p.block_size = cfg->block_size;
+  p.num_blocks = num_blocks;
+  p.max_blocks = max_blocks;
+  p.cap = max_seq_len_host;
+  p.causal = causal;
+  p.num_splits = pl.splits;
+  p.chunk_rows = pl.chunk;
+  p.xcds = dev.xcds;
+  p.scale_log2 = softmax_scale(cfg) * 1.4426950408889634f;
+  p.plan = pl.balanced ? reinterpret_cast<int32_t*>(ws + L.table) : nullptr;
+  p.counters = reinterpret_cast<uint32_t*>(ws);  // the group records follow at L.rec
+  return hip_status(mla::launch_decode_queue(p, dev.cus, s));
+}
+
 mla_status mla_decode_noalloc(const mla_config* cfg, const void* q_abs, const void* pool,
                               int32_t num_blocks, const int32_t* block_table,
                               int32_t max_blocks, const int32_t* seq_lens,

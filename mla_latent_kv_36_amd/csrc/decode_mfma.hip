@@ -52,6 +52,7 @@
 
 #include "common.h"
 #include "launch.h"
+#include "merge.h"
 
 namespace mla {
 namespace {
@@ -180,7 +181,9 @@ __device__ __forceinline__ void softmax_unit(Smem& sm, int u, int valid, int grp
 
 // After the last unit: the rows' sums (the four lanes' shares added), the
 // reciprocals of those for the normalisation, and the rows' log-sum-exp
-// (natural log) to the output or to the split's partial.
+// (natural log) to the output or to the split's partial (kDev: with a
+// device-scope store, for a merge in the same launch).
+template <bool kDev>
 __device__ __forceinline__ void softmax_finish(Smem& sm, const DecodeParams& p, int grp, int lane,
                                                float m_run, float l_lane, bool direct, int b,
                                                int pidx, int TH, int rb, int rows_here) {
@@ -192,6 +195,9 @@ __device__ __forceinline__ void softmax_finish(Smem& sm, const DecodeParams& p, 
   if (srow >= rows_here) return;  // past the token's last head: not stored
   if (direct) {
     if (p.lse != nullptr) p.lse[(size_t)b * TH + rb + srow] = lse;
+  } else if constexpr (kDev) {
+    __hip_atomic_store(&p.part_lse[(size_t)pidx * TH + rb + srow], lse, __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
   } else {
     p.part_lse[(size_t)pidx * TH + rb + srow] = lse;
   }
@@ -206,13 +212,16 @@ __device__ __forceinline__ void softmax_finish(Smem& sm, const DecodeParams& p, 
 // item k is split k - P_b of the sequence with P_b <= k < P_b + S_b, or no
 // work past the last.  Computed by one wave (64 lanes, sequences
 // lane + 64c); with `table`, every sequence's (P_b, S_b, ch_b) is written
-// there for the merge.  Returns {b, s, S_b, ch_b, P_b}, b = -1 for no work.
+// there for the merge.  With min_one, a sequence with no visible row gets one
+// (empty) split as well, whose work item writes its zero output.  Returns
+// {b, s, S_b, ch_b, P_b, multi}, b = -1 for no work, multi = the number of
+// sequences with more than one split.
 constexpr int kMinUnits = 8;
 struct PlanItem {
-  int b, s, S_b, ch_b, P_b;
+  int b, s, S_b, ch_b, P_b, multi;
 };
 __device__ __forceinline__ PlanItem balanced_item(const DecodeParams& p, int k, int lane,
-                                                  int32_t* table) {
+                                                  int32_t* table, bool min_one = false) {
   const int B = p.B;
   const int K = p.num_splits;
   auto units = [&](int b) {
@@ -230,8 +239,12 @@ __device__ __forceinline__ PlanItem balanced_item(const DecodeParams& p, int k, 
     for (int off = 32; off >= 1; off >>= 1) x = max(x, __shfl_xor(x, off));
     return x;
   };
-  // the splits sequence b gets for a bound of C units per split
-  auto splits_of = [](int U, int C) { return U == 0 ? 0 : (U + C - 1) / C; };
+  // the splits sequence b gets for a bound of C units per split (none for the
+  // lanes past the last sequence)
+  auto splits_of = [B, min_one](int b, int U, int C) {
+    if (b >= B) return 0;
+    return U == 0 ? (min_one ? 1 : 0) : (U + C - 1) / C;
+  };
   long long total = 0;
   int umax = 0;
   for (int c0 = 0; c0 < B; c0 += 64) {
@@ -246,15 +259,15 @@ __device__ __forceinline__ PlanItem balanced_item(const DecodeParams& p, int k, 
   while (lo < hi) {
     const int mid = lo + (hi - lo) / 2;
     int cnt = 0;
-    for (int c0 = 0; c0 < B; c0 += 64) cnt += wave_sum(splits_of(units(c0 + lane), mid));
+    for (int c0 = 0; c0 < B; c0 += 64) cnt += wave_sum(splits_of(c0 + lane, units(c0 + lane), mid));
     if (cnt <= K) hi = mid; else lo = mid + 1;
   }
   const int C = lo;
-  PlanItem it{-1, 0, 0, 0, 0};
+  PlanItem it{-1, 0, 0, 0, 0, 0};
   int base = 0;  // splits of the sequences before this chunk
   for (int c0 = 0; c0 < B; c0 += 64) {
     const int U = units(c0 + lane);
-    const int S_b = splits_of(U, C);
+    const int S_b = splits_of(c0 + lane, U, C);
     const int ch_b = S_b > 0 ? (U + S_b - 1) / S_b : 0;
     int incl = S_b;  // inclusive prefix sum over the lanes
 #pragma unroll
@@ -263,6 +276,7 @@ __device__ __forceinline__ PlanItem balanced_item(const DecodeParams& p, int k, 
       if (lane >= off) incl += y;
     }
     const int P_b = base + incl - S_b;
+    it.multi += wave_sum(S_b > 1 ? 1 : 0);
     if (table != nullptr && c0 + lane < B) {
       table[4 * (c0 + lane) + 0] = P_b;
       table[4 * (c0 + lane) + 1] = S_b;
@@ -282,75 +296,32 @@ __device__ __forceinline__ PlanItem balanced_item(const DecodeParams& p, int k, 
   return it;
 }
 
-__global__ __launch_bounds__(NT, 1) void decode_mfma_kernel(const DecodeParams p) {
-  __shared__ Smem sm;
-
-  const int tid = threadIdx.x;
+// One work item: the 64 query rows of group g (ceil(H / 64) groups per new
+// token) of sequence b against cache rows s * chunk_rows .. (s + 1) *
+// chunk_rows - 1 (cut at the rows the group's token sees), written as the
+// final output (direct) or as partial pidx.  kDev: partials with device-scope
+// stores.
+template <bool kDev>
+__device__ __forceinline__ void attend_range(Smem& sm, const DecodeParams& p, int g, int b, int s,
+                                            int pidx, int chunk_rows, bool direct) {
+  // The thread index through an opaque copy: inside the one-launch kernel's
+  // item loop, the lane-dependent offsets of all three roles would otherwise
+  // be hoisted out of the loop and held in registers across every role.
+  int tid = threadIdx.x;
+  if constexpr (kDev) asm volatile("" : "+v"(tid));
   const int lane = tid & 63;
   // Wave index as a scalar: the role branches below are uniform (scalar)
   // branches, so a wave never steps through the other role's barriers.
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31;
   const int lhi = lane >> 5;
-
-  // 64-row groups: ceil(H / 64) per new token, the last one partial when H
-  // is not a multiple of 64
   const int gpt = (p.H + ROWS - 1) / ROWS;
-  const int G = p.T * gpt;
-  const int S = p.num_splits;
-  // Workgroup i is dispatched to XCD i % X (X XCDs, queried on the host), and
-  // each XCD has its own L2.  XCD x gets a contiguous block of (sequence,
-  // split) pairs, and all G 64-row groups of each: the pages of a pair and the
-  // absorbed queries of a sequence then come from HBM once per XCD and from L2
-  // for the other workgroups that read them.  Ids past the last full set of
-  // X G keep the plain order.
-  const int XCDS = p.xcds;
-  const int i = blockIdx.x;
-  const int full = (int)gridDim.x - (int)gridDim.x % (XCDS * G);
-  int g, pair;
-  if (i < full) {
-    const int r = i / XCDS;
-    g = r % G;
-    pair = (i % XCDS) * (full / G / XCDS) + r / G;
-  } else {
-    g = i % G;
-    pair = i / G;
-  }
-  // (sequence b, split s) of this workgroup, its partial's index and the cache
-  // rows per split: the plain plan cuts every sequence at the same rows; a
-  // balanced plan is computed here, by wave 0, from the sequence lengths
-  int b, s, pidx, chunk_rows;
-  if (p.plan == nullptr) {
-    s = pair % S;
-    b = pair / S;
-    pidx = pair;
-    chunk_rows = p.chunk_rows;
-  } else {
-    if (wave == 0) {
-      const PlanItem it = balanced_item(p, pair, lane, g == 0 && pair == 0 ? p.plan : nullptr);
-      if (lane == 0) {
-        sm.item[0] = it.b;
-        sm.item[1] = it.s;
-        sm.item[2] = it.P_b + it.s;
-        sm.item[3] = it.ch_b * UNIT;
-      }
-    }
-    __syncthreads();
-    b = __builtin_amdgcn_readfirstlane(sm.item[0]);
-    if (b < 0) return;  // no work item: the whole workgroup
-    s = __builtin_amdgcn_readfirstlane(sm.item[1]);
-    pidx = __builtin_amdgcn_readfirstlane(sm.item[2]);
-    chunk_rows = __builtin_amdgcn_readfirstlane(sm.item[3]);
-  }
-
   const int TH = p.T * p.H;
   const int t = g / gpt;                                   // the group's new token
   const int rb = t * p.H + (g - t * gpt) * ROWS;           // its first query row (t*H + h)
   const int rows_here = min(ROWS, (t + 1) * p.H - rb);     // 64, or fewer in a token's last group
   // this range starts at cache row tok0 (a multiple of UNIT)
   const int tok0 = s * chunk_rows;
-  // one split and the plain plan: the final output directly
-  const bool direct = S == 1 && p.plan == nullptr;
 
   // The sequence length fixes where the range ends.  Each role first requests
   // what does not depend on it -- the score waves their queries and unit 0's
@@ -611,13 +582,17 @@ __global__ __launch_bounds__(NT, 1) void decode_mfma_kernel(const DecodeParams p
       lds_barrier();                       // E(j)
     }
     wait_vmcnt<0>();  // a unit 1 copied past a one-unit range
-    softmax_finish(sm, p, grp, lane, m_run, l_lane, direct, b, pidx, TH, rb, rows_here);
+    softmax_finish<kDev>(sm, p, grp, lane, m_run, l_lane, direct, b, pidx, TH, rb, rows_here);
     lds_barrier();                         // F
   } else {
     // =============================== value waves ===============================
     // Value wave v owns latent columns 128v .. 128v+127 of O for all 64 rows,
     // and the softmax of query rows 16v .. 16v+15.
     const int v = (wave & 1) + 2 * (wave >> 2);
+    // the softmax scale in a register of its own for the whole range (the
+    // one-launch kernel would otherwise re-load it in every step)
+    float c_log2 = p.scale_log2;
+    if constexpr (kDev) asm volatile("" : "+s"(c_log2));
     const int tok_end = range_end();
     if (tok0 >= tok_end) {
       empty_range();
@@ -743,7 +718,7 @@ __global__ __launch_bounds__(NT, 1) void decode_mfma_kernel(const DecodeParams p
         if (j >= 0) pv(j, next ? j + 1 : -1);
         else if (next) load_v(j + 1);
       } else {
-        if (next) softmax_unit(sm, j + 1, unit_valid(j + 1), v, lane, p.scale_log2, m_run, l_lane);
+        if (next) softmax_unit(sm, j + 1, unit_valid(j + 1), v, lane, c_log2, m_run, l_lane);
         if (j >= 0) pv(j, next ? j + 1 : -1);
         else if (next) load_v(j + 1);
       }
@@ -756,14 +731,16 @@ __global__ __launch_bounds__(NT, 1) void decode_mfma_kernel(const DecodeParams p
       for (int j = -2; j < U; ++j) step(j, std::false_type{});
     }
 
-    if (v < 2) softmax_finish(sm, p, v, lane, m_run, l_lane, direct, b, pidx, TH, rb, rows_here);
+    if (v < 2) softmax_finish<kDev>(sm, p, v, lane, m_run, l_lane, direct, b, pidx, TH, rb, rows_here);
     lds_barrier();                         // F
     // Streaming (non-temporal) stores: the rows are read by the next kernel,
     // not by this one, and lines left dirty in L2 would all be written back
     // at the end of the launch, which delays the next kernel's start.  A
     // split's partial is stored as bf16: it is a normalised average of cached
     // rows, so bf16 keeps 8 significant bits of every element whatever its
-    // range, and the merge reads half the bytes.
+    // range, and the merge reads half the bytes.  kDev: partials are merged
+    // in the same launch, possibly on another XCD, so they are stored with
+    // device-scope stores, which do not stay in this XCD's L2.
     auto store_rows = [&](auto* dst, auto cvt) __attribute__((always_inline)) {
 #pragma unroll
       for (int rt = 0; rt < 2; ++rt) {
@@ -773,9 +750,14 @@ __global__ __launch_bounds__(NT, 1) void decode_mfma_kernel(const DecodeParams p
           const float inv = sm.lrow[row];
           if (row < rows_here) {  // past the token's last head: not stored
 #pragma unroll
-            for (int dt = 0; dt < 4; ++dt)
-              __builtin_nontemporal_store(cvt(o[rt][dt][r] * inv),
-                                          &dst[(size_t)row * DC + 128 * v + 32 * dt + l32]);
+            for (int dt = 0; dt < 4; ++dt) {
+              auto* at = &dst[(size_t)row * DC + 128 * v + 32 * dt + l32];
+              if (kDev && !direct)
+                __hip_atomic_store(at, cvt(o[rt][dt][r] * inv), __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
+              else
+                __builtin_nontemporal_store(cvt(o[rt][dt][r] * inv), at);
+            }
           }
         }
       }
@@ -785,6 +767,334 @@ __global__ __launch_bounds__(NT, 1) void decode_mfma_kernel(const DecodeParams p
     else
       store_rows(static_cast<uint16_t*>(p.part_o) + ((size_t)pidx * TH + rb) * DC,
                  [](float x) { return f32_to_bf16(x); });
+  }
+}
+
+__global__ __launch_bounds__(NT, 1) void decode_mfma_kernel(const DecodeParams p) {
+  __shared__ Smem sm;
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+
+  // 64-row groups: ceil(H / 64) per new token, the last one partial when H
+  // is not a multiple of 64
+  const int gpt = (p.H + ROWS - 1) / ROWS;
+  const int G = p.T * gpt;
+  const int S = p.num_splits;
+  // Workgroup i is dispatched to XCD i % X (X XCDs, queried on the host), and
+  // each XCD has its own L2.  XCD x gets a contiguous block of (sequence,
+  // split) pairs, and all G 64-row groups of each: the pages of a pair and the
+  // absorbed queries of a sequence then come from HBM once per XCD and from L2
+  // for the other workgroups that read them.  Ids past the last full set of
+  // X G keep the plain order.
+  const int XCDS = p.xcds;
+  const int i = blockIdx.x;
+  const int full = (int)gridDim.x - (int)gridDim.x % (XCDS * G);
+  int g, pair;
+  if (i < full) {
+    const int r = i / XCDS;
+    g = r % G;
+    pair = (i % XCDS) * (full / G / XCDS) + r / G;
+  } else {
+    g = i % G;
+    pair = i / G;
+  }
+  // (sequence b, split s) of this workgroup, its partial's index and the cache
+  // rows per split: the plain plan cuts every sequence at the same rows; a
+  // balanced plan is computed here, by wave 0, from the sequence lengths
+  int b, s, pidx, chunk_rows;
+  if (p.plan == nullptr) {
+    s = pair % S;
+    b = pair / S;
+    pidx = pair;
+    chunk_rows = p.chunk_rows;
+  } else {
+    if (wave == 0) {
+      const PlanItem it = balanced_item(p, pair, lane, g == 0 && pair == 0 ? p.plan : nullptr);
+      if (lane == 0) {
+        sm.item[0] = it.b;
+        sm.item[1] = it.s;
+        sm.item[2] = it.P_b + it.s;
+        sm.item[3] = it.ch_b * UNIT;
+      }
+    }
+    __syncthreads();
+    b = __builtin_amdgcn_readfirstlane(sm.item[0]);
+    if (b < 0) return;  // no work item: the whole workgroup
+    s = __builtin_amdgcn_readfirstlane(sm.item[1]);
+    pidx = __builtin_amdgcn_readfirstlane(sm.item[2]);
+    chunk_rows = __builtin_amdgcn_readfirstlane(sm.item[3]);
+  }
+
+  attend_range<false>(sm, p, g, b, s, pidx, chunk_rows, S == 1 && p.plan == nullptr);
+}
+
+// ---------------------------------------------------------------- one launch
+// Split-KV decode and its log-sum-exp merge in a single launch of persistent
+// workgroups (one per compute unit), in the manner of the fused and
+// megakernel decoders that "Research on MLA" lists for variable-length
+// serving.
+//  * Work items (query group, split) of the plain or balanced plan: workgroup
+//    i takes item i first, then further items from a queue counter, so that a
+//    workgroup that finishes early takes more.  A sequence whose rows all fit
+//    one split writes its final output directly.
+//  * Publishing: a split's partial rows and log-sum-exps are written with
+//    device-scope stores; every wave waits for its stores to complete, then
+//    one thread counts the split into its group (arrival count).
+//  * Last arrival: the split that completes its group's count pushes the
+//    group's kQueueSlices merge slices (8 query rows each, with the group's
+//    split count) onto a ring, after the group's record (first partial, rows
+//    per split) under a balanced plan; a plain plan's record follows from
+//    the parameters.
+//  * Merges: a workgroup that finds the item queue empty takes ring tickets,
+//    waits for its ticket's entry to be pushed, and merges the slice (one row
+//    per wave) with device-scope loads.  A ticket is only taken after every
+//    work item has been taken by a running workgroup, and no work item waits
+//    on anything, so every awaited entry is pushed; the wait is bounded all
+//    the same (kSpinLimit polls; a miss sets bit 0 of the error word and
+//    leaves the slice unmerged).
+//  * Every counter is left zero for the next launch: the arrival count by its
+//    last arrival, a ring entry by its consumer, the queue counters by the
+//    last workgroup to leave.
+// Device-scope stores write past the XCD's L2 and device-scope loads do not
+// take lines from it, so partials written on one XCD are seen on another
+// once the stores have completed (the AMDGPU memory model's agent scope).
+constexpr int kCtrItems = 0, kCtrHead = 32, kCtrTail = 64, kCtrExit = 96, kCtrErr = 128;
+constexpr int kCtrRing = 256;  // first word of the merge ring (8-byte entries)
+constexpr unsigned kSpinLimit = 1u << 20;
+
+__device__ __forceinline__ void st_dev(uint32_t* a, uint32_t v) {
+  __hip_atomic_store(a, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint32_t add_dev(uint32_t* a, uint32_t v) {
+  return __hip_atomic_fetch_add(a, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint64_t ld_dev64(const uint64_t* a) {
+  return __hip_atomic_load(a, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_dev64(uint64_t* a, uint64_t v) {
+  __hip_atomic_store(a, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// Counter region (32-bit words from p.counters): the queue counters and the
+// error word in the first 1 KiB, then kQueueSlices ring entries per (sequence,
+// 64-row group) -- 8 bytes each: the slice + 1 and the group's split count --
+// then an arrival count per group.  The group records follow the region: 8
+// bytes per group, its first partial and its rows per split.
+__device__ __forceinline__ uint64_t* ring_of(const DecodeParams& p) {
+  return reinterpret_cast<uint64_t*>(p.counters + kCtrRing);
+}
+__device__ __forceinline__ uint32_t* arrive_of(const DecodeParams& p, int G) {
+  return p.counters + kCtrRing + 2 * kQueueSlices * p.B * G;
+}
+__device__ __forceinline__ uint64_t* rec_of(const DecodeParams& p) {
+  return reinterpret_cast<uint64_t*>(p.counters + kQueueCounterBytes / 4);
+}
+
+// The launch's parameters through an opaque copy of their address (the
+// kernel argument block holds them at offset 0).  Inside the one-launch
+// kernel's item loop, every value derived from the parameters alone would
+// otherwise be hoisted out of the loop and held in scalar registers across the
+// whole item, which the item's own code needs: beyond the register file, the
+// compiler re-loads values inside the per-unit loops, and each such load makes
+// the LDS waits there wait for it too.
+typedef const __attribute__((address_space(4))) DecodeParams* ParamsPtr;
+__device__ __forceinline__ const DecodeParams& params() {
+  ParamsPtr kp = (ParamsPtr)__builtin_amdgcn_kernarg_segment_ptr();
+  asm volatile("" : "+s"(kp));
+  return *(const DecodeParams*)kp;
+}
+
+__global__ __launch_bounds__(NT, 1) void decode_queue_kernel(const DecodeParams) {
+  __shared__ Smem sm;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  // The queue's state lives in sm.item (LDS) and is read back after each
+  // item rather than held in registers across it.  sm.item: [0] sequence
+  // (-1: none), [1] group, [2] split, [3] the sequence's splits, [4] its
+  // first partial, [5] rows per split, [6] the sequences with more than one
+  // split (-1: not known yet), [7] the workgroups of the launch.
+  //
+  // Work item `ticket` into sm.item (wave 0).
+  auto take = [&](int ticket) {
+    const DecodeParams& p = params();
+    const int G = p.T * ((p.H + ROWS - 1) / ROWS);
+    const int S = p.num_splits;
+    const bool balanced = p.plan != nullptr;
+    const int n_items = (balanced ? 1 : p.B) * S * G;
+    int b = -1, g = 0, s = 0, S_b = 0, P_b = 0, ch = 0, mu = -1;
+    if (ticket < n_items) {
+      // item = k G + g.  The first tickets (one per workgroup) are placed as
+      // in the split kernel: XCD x runs all G groups of a contiguous block of
+      // (sequence, split) pairs, so that their pages come from HBM once per
+      // XCD; the tickets past them are handed out in item order.
+      const int grid = sm.item[7];
+      const int XCDS = p.xcds;
+      const int full = grid - grid % (XCDS * G);
+      int k;
+      if (ticket < full) {
+        const int r = ticket / XCDS;
+        g = r % G;
+        k = (ticket % XCDS) * (full / G / XCDS) + r / G;
+      } else {
+        g = ticket % G;
+        k = ticket / G;
+      }
+      if (balanced) {
+        const PlanItem pi = balanced_item(p, k, lane, ticket == 0 ? p.plan : nullptr, true);
+        b = pi.b;
+        s = pi.s;
+        S_b = pi.S_b;
+        P_b = pi.P_b;
+        ch = pi.ch_b * UNIT;
+        mu = pi.multi;
+      } else {
+        b = k / S;
+        s = k % S;
+        S_b = S;
+        P_b = b * S;
+        ch = p.chunk_rows;
+        mu = S > 1 ? p.B : 0;
+      }
+    }
+    if (lane == 0) {
+      sm.item[0] = b;
+      sm.item[1] = g;
+      sm.item[2] = s;
+      sm.item[3] = S_b;
+      sm.item[4] = P_b;
+      sm.item[5] = ch;
+      if (mu >= 0) sm.item[6] = mu;
+    }
+  };
+
+  // ---- work items: the first by workgroup id, the others from the queue
+  if (tid == 0) {
+    sm.item[6] = -1;
+    sm.item[7] = (int)gridDim.x;
+  }
+  __syncthreads();
+  if (wave == 0) take(blockIdx.x);
+  __syncthreads();
+  for (;;) {
+    {
+      const DecodeParams& p = params();
+      const int b = __builtin_amdgcn_readfirstlane(sm.item[0]);
+      // no item left (tickets past the last, or a balanced plan's spare
+      // items, which all come after its last real one)
+      if (b < 0 || b >= p.B) break;
+      const int S_b = __builtin_amdgcn_readfirstlane(sm.item[3]);
+      const int s = __builtin_amdgcn_readfirstlane(sm.item[2]);
+      attend_range<true>(sm, p, __builtin_amdgcn_readfirstlane(sm.item[1]), b, s,
+                         __builtin_amdgcn_readfirstlane(sm.item[4]) + s,
+                         __builtin_amdgcn_readfirstlane(sm.item[5]), S_b == 1);
+    }
+    const int S_b = __builtin_amdgcn_readfirstlane(sm.item[3]);
+    if (S_b > 1) {
+      wait_vmcnt<0>();  // this wave's partial stores have completed
+      __syncthreads();
+      if (tid == 0) {
+        const DecodeParams& p = params();
+        const int G = p.T * ((p.H + ROWS - 1) / ROWS);
+        const int bg = sm.item[0] * G + sm.item[1];
+        uint32_t* const arrive = arrive_of(p, G) + bg;
+        if (add_dev(arrive, 1u) + 1 == (uint32_t)S_b) {
+          // the group's last split: nothing else reads its count in this launch
+          st_dev(arrive, 0u);
+          if (p.plan != nullptr) {  // a plain plan's record is known to all
+            st_dev64(rec_of(p) + bg,
+                     (uint64_t)(uint32_t)sm.item[4] | ((uint64_t)(uint32_t)sm.item[5] << 32));
+            wait_vmcnt<0>();  // the record before the ring entries
+          }
+          const uint32_t pos = add_dev(p.counters + kCtrTail, (uint32_t)kQueueSlices);
+          for (int j = 0; j < kQueueSlices; ++j)
+            st_dev64(ring_of(p) + pos + j,
+                     (uint64_t)(bg * kQueueSlices + j + 1) | ((uint64_t)(uint32_t)S_b << 32));
+        }
+      }
+    }
+    __syncthreads();  // the LDS and sm.item are free for the next item
+    if (wave == 0) {
+      uint32_t t0 = 0;
+      if (lane == 0) t0 = add_dev(params().counters + kCtrItems, 1u);
+      take(sm.item[7] + (int)__shfl(t0, 0));
+    }
+    __syncthreads();
+  }
+
+  // ---- merges
+  const DecodeParams& p = params();
+  const int gpt = (p.H + ROWS - 1) / ROWS;
+  const int G = p.T * gpt;
+  int multi = __builtin_amdgcn_readfirstlane(sm.item[6]);
+  if (multi < 0) {  // a balanced plan whose item this workgroup never computed
+    if (wave == 0) {
+      const PlanItem pi = balanced_item(p, 0, lane, nullptr, true);
+      if (lane == 0) sm.item[6] = pi.multi;
+    }
+    __syncthreads();
+    multi = __builtin_amdgcn_readfirstlane(sm.item[6]);
+  }
+  const int n_slices = multi * G * kQueueSlices;
+  uint32_t* const ctr = p.counters;
+  uint64_t* const ring = ring_of(p);
+  const int TH = p.T * p.H;
+  for (;;) {
+    __syncthreads();  // sm.item is free
+    if (tid == 0) {
+      int task = -1;  // -1: no ticket left; -2: the entry never came
+      const uint32_t t = add_dev(ctr + kCtrHead, 1u);
+      if (t < (uint32_t)n_slices) {
+        uint64_t e = ld_dev64(ring + t);
+        for (unsigned n = 0; e == 0 && n < kSpinLimit; ++n) {
+          __builtin_amdgcn_s_sleep(2);
+          e = ld_dev64(ring + t);
+        }
+        if (e == 0) {
+          __hip_atomic_fetch_or(ctr + kCtrErr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          task = -2;
+        } else {
+          st_dev64(ring + t, 0ull);
+          task = (int)(uint32_t)e - 1;
+          const int bg = task / kQueueSlices;
+          const int b = bg / G;
+          uint64_t r;  // first partial | rows per split << 32
+          if (p.plan != nullptr)
+            r = ld_dev64(rec_of(p) + bg);
+          else
+            r = (uint64_t)(uint32_t)(b * p.num_splits) | ((uint64_t)(uint32_t)p.chunk_rows << 32);
+          sm.item[1] = (int)(uint32_t)r;
+          sm.item[2] = (int)(uint32_t)(e >> 32);
+          sm.item[3] = (int)(uint32_t)(r >> 32);
+        }
+      }
+      sm.item[0] = task;
+    }
+    __syncthreads();
+    const int task = __builtin_amdgcn_readfirstlane(sm.item[0]);
+    if (task == -1) break;
+    if (task < 0) continue;
+    const int bg = task / kQueueSlices;
+    const int sl = task - bg * kQueueSlices;
+    const int b = bg / G;
+    const int g = bg - b * G;
+    const int t = g / gpt;
+    const int rb = t * p.H + (g - t * gpt) * ROWS;
+    const int rows_here = min(ROWS, (t + 1) * p.H - rb);
+    const int r = sl * (ROWS / kQueueSlices) + wave;  // one query row per wave
+    if (r < rows_here)
+      merge_row_splits<uint16_t, true>(p, (long long)b * TH + rb + r, lane,
+                                       __builtin_amdgcn_readfirstlane(sm.item[1]),
+                                       __builtin_amdgcn_readfirstlane(sm.item[2]),
+                                       __builtin_amdgcn_readfirstlane(sm.item[3]));
+  }
+
+  // ---- leave: the last workgroup out resets the queue counters
+  if (tid == 0 && add_dev(ctr + kCtrExit, 1u) + 1 == gridDim.x) {
+    st_dev(ctr + kCtrItems, 0u);
+    st_dev(ctr + kCtrHead, 0u);
+    st_dev(ctr + kCtrTail, 0u);
+    st_dev(ctr + kCtrExit, 0u);
   }
 }
 
@@ -805,6 +1115,18 @@ hipError_t launch_decode_mfma(const DecodeParams& p, hipStream_t stream) {
   if (grid <= 0) return hipSuccess;
   if (grid > 0x7fffffffLL) return hipErrorInvalidValue;
   hipLaunchKernelGGL(decode_mfma_kernel, dim3((unsigned)grid), dim3(NT), 0, stream, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_decode_queue(const DecodeParams& p, int workgroups, hipStream_t stream) {
+  const int G = p.T * ((p.H + ROWS - 1) / ROWS);
+  const long long items = (p.plan != nullptr ? 1LL : (long long)p.B) * p.num_splits * G;
+  if (items <= 0) return hipSuccess;
+  if (p.counters == nullptr || items > 0x7fffffffLL ||
+      (long long)p.B * G > kQueueMaxGroups || workgroups < 1)
+    return hipErrorInvalidValue;
+  const long long grid = items < workgroups ? items : workgroups;
+  hipLaunchKernelGGL(decode_queue_kernel, dim3((unsigned)grid), dim3(NT), 0, stream, p);
   return hipGetLastError();
 }
 

@@ -32,12 +32,28 @@ struct DecodeParams {
   // split count and units per split for the merge.  Partials are then
   // indexed by work item: part_o [K, T*H, d_c], part_lse [K, T*H].
   int32_t* plan;
+  // One-launch decode (decode_queue_kernel) only: the counters of its work
+  // queue and merge ring (kQueueCounterBytes, zero before the launch and left
+  // zero after it), followed at once by 8 bytes per (sequence, 64-row group)
+  // for the merge.
+  uint32_t* counters;
 };
+
+// The one-launch decode's counter region: a 1 KiB header, then per (sequence,
+// 64-row group) kQueueSlices 8-byte merge-ring entries and an arrival count.
+constexpr size_t kQueueCounterBytes = (size_t)256 << 10;
+constexpr int kQueueSlices = 8;
+constexpr int64_t kQueueMaxGroups =
+    ((int64_t)kQueueCounterBytes / 4 - 256) / (1 + 2 * kQueueSlices);
 
 // The MFMA kernel covers bf16, d_c = 512, d_rope = 64 and 64-token pages, any
 // H and T (ceil(H / 64) query groups of 64 rows per new token).
 bool decode_mfma_supported(int dtype, int d_c, int d_r, int block_size, int T, int H);
 hipError_t launch_decode_mfma(const DecodeParams& p, hipStream_t stream);
+// The same decode and its merge in one launch of at most `workgroups`
+// persistent workgroups (one per compute unit fits): work items from a queue,
+// merges of a group's partials taken up once its last split has arrived.
+hipError_t launch_decode_queue(const DecodeParams& p, int workgroups, hipStream_t stream);
 hipError_t launch_decode_generic(const DecodeParams& p, int dtype, hipStream_t stream);
 hipError_t launch_combine(const DecodeParams& p, hipStream_t stream);
 

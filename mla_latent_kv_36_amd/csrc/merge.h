@@ -20,10 +20,22 @@ namespace mla {
 // and 256 + 4l .. +3 (two 16-byte loads); bf16 partials, columns 8l .. 8l+7
 // (one 16-byte load).  Raw loads first (`raw`), converted after every load of
 // the row is in flight (`lo`, `hi`: the lane's first and last 4 columns).
+//
+// kDev: the partials were stored by other workgroups of the running launch
+// with device-scope stores, and are read with device-scope loads (which do not
+// take stale lines from this XCD's L2); bf16 partials only.
+template <bool kDev>
+__device__ __forceinline__ float ld_lse(const float* p) {
+  if constexpr (kDev) return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  else return *p;
+}
+
 template <typename PT> struct Part8;
 template <> struct Part8<float> {
   struct Raw { f32x4 a, b; };
+  template <bool kDev = false>
   __device__ __forceinline__ static Raw load(const float* row, int lane) {
+    static_assert(!kDev, "device-scope merges read bf16 partials");
     return {*reinterpret_cast<const f32x4*>(row + 4 * lane),
             *reinterpret_cast<const f32x4*>(row + 256 + 4 * lane)};
   }
@@ -35,8 +47,18 @@ template <> struct Part8<float> {
 };
 template <> struct Part8<uint16_t> {
   using Raw = u16x8;
+  template <bool kDev = false>
   __device__ __forceinline__ static Raw load(const uint16_t* row, int lane) {
-    return *reinterpret_cast<const u16x8*>(row + 8 * lane);
+    if constexpr (kDev) {
+      // two 8-byte device-scope loads (atomic loads are at most 8 bytes)
+      const uint64_t* w = reinterpret_cast<const uint64_t*>(row + 8 * lane);
+      typedef __attribute__((__vector_size__(2 * sizeof(uint64_t)))) uint64_t u64x2;
+      const u64x2 v = {__hip_atomic_load(w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT),
+                       __hip_atomic_load(w + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)};
+      return __builtin_bit_cast(u16x8, v);
+    } else {
+      return *reinterpret_cast<const u16x8*>(row + 8 * lane);
+    }
   }
   __device__ __forceinline__ static void hold(const Raw& r) { asm volatile("" ::"v"(r)); }
   __device__ __forceinline__ static f32x4 lo(const Raw& r) {
@@ -52,7 +74,7 @@ template <> struct Part8<uint16_t> {
 // Merges query row `row` (sequence b = row / (T H)) from the S partials
 // P0 .. P0+S-1 of its sequence, which cover `chunk` cache rows each, with one
 // wave; lane is the lane index.
-template <typename PT>
+template <typename PT, bool kDev = false>
 __device__ void merge_row_splits(const DecodeParams& p, long long row, int lane, int P0, int S,
                                  int chunk) {
   using P8 = Part8<PT>;
@@ -71,11 +93,11 @@ __device__ void merge_row_splits(const DecodeParams& p, long long row, int lane,
     const PT* po_b = part + ((size_t)P0 * TH + rr) * 512;
     const size_t sstride = (size_t)TH * 512;
     const int len = p.seq_lens[b];
-    const float lse_l = lse_b[(size_t)min(lane, S - 1) * TH];
+    const float lse_l = ld_lse<kDev>(lse_b + (size_t)min(lane, S - 1) * TH);
     typename P8::Raw v[8];
 #pragma unroll
     for (int k = 0; k < 8; ++k)
-      v[k] = P8::load(po_b + (size_t)min(k, S - 1) * sstride, lane);
+      v[k] = P8::template load<kDev>(po_b + (size_t)min(k, S - 1) * sstride, lane);
     // every value above is consumed here, so all the loads are issued before
     // the first wait (the compiler would otherwise interleave waits and loads)
     __builtin_amdgcn_sched_barrier(0);
@@ -124,15 +146,26 @@ __device__ void merge_row_splits(const DecodeParams& p, long long row, int lane,
     return;
   }
   // split s's log-sum-exp is read by lane s % 64 (all loads of a pass in
-  // flight at once), then reduced across the wave in a fixed order
+  // flight at once), then reduced across the wave in a fixed order; with at
+  // most 64 splits each lane keeps its split's weight, and the weights below
+  // are taken from the lanes rather than read again
   float M = -INFINITY;
+  float lse_l = -INFINITY;  // lane's split (ns <= 64)
   for (int c = 0; c < ns; c += 64)
-    if (c + lane < ns) M = fmaxf(M, lse_b[(size_t)(c + lane) * TH]);
+    if (c + lane < ns) {
+      lse_l = ld_lse<kDev>(lse_b + (size_t)(c + lane) * TH);
+      M = fmaxf(M, lse_l);
+    }
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
   float den = 0.0f;
-  for (int c = 0; c < ns; c += 64)
-    if (c + lane < ns) den += exp2f((lse_b[(size_t)(c + lane) * TH] - M) * kLog2e);
+  const float e_l = lane < ns ? exp2f((lse_l - M) * kLog2e) : 0.0f;
+  if (ns <= 64) {
+    den = e_l;
+  } else {
+    for (int c = 0; c < ns; c += 64)
+      if (c + lane < ns) den += exp2f((ld_lse<kDev>(lse_b + (size_t)(c + lane) * TH) - M) * kLog2e);
+  }
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) den += __shfl_xor(den, off);
   const float inv = 1.0f / den;
@@ -149,13 +182,15 @@ __device__ void merge_row_splits(const DecodeParams& p, long long row, int lane,
         float w[8];
 #pragma unroll
         for (int k = 0; k < 8; ++k) {
-          const float e = exp2f((lse_b[(size_t)min(s0 + k, ns - 1) * TH] - M) * kLog2e);
+          const float e = ns <= 64
+              ? __shfl(e_l, min(s0 + k, ns - 1))
+              : exp2f((ld_lse<kDev>(lse_b + (size_t)min(s0 + k, ns - 1) * TH) - M) * kLog2e);
           w[k] = s0 + k < ns ? e : 0.0f;
         }
         typename P8::Raw v[8];
 #pragma unroll
         for (int k = 0; k < 8; ++k)
-          v[k] = P8::load(po_b + (size_t)min(s0 + k, ns - 1) * sstride + d0, lane);
+          v[k] = P8::template load<kDev>(po_b + (size_t)min(s0 + k, ns - 1) * sstride + d0, lane);
 #pragma unroll
         for (int k = 0; k < 8; ++k) {
           a0 += w[k] * P8::lo(v[k]);
@@ -165,7 +200,7 @@ __device__ void merge_row_splits(const DecodeParams& p, long long row, int lane,
       *reinterpret_cast<f32x4*>(P8::col_lo(out + d0, lane)) = a0 * inv;
       *reinterpret_cast<f32x4*>(P8::col_hi(out + d0, lane)) = a1 * inv;
     }
-  } else if constexpr (sizeof(PT) == 4) {
+  } else if constexpr (sizeof(PT) == 4 && !kDev) {
     const float* pf = reinterpret_cast<const float*>(po_b);
     if ((p.d_c & 3) == 0) {
       for (int d = 4 * lane; d < p.d_c; d += 256) {

@@ -113,6 +113,45 @@ def test_decode_noalloc_validation(lib):
     assert _decode_noalloc(lib, cfg, B=B, T=T, mb=512, cap=cap, ns=64, tot=B * cap) == WS
 
 
+def _decode_fused(lib, cfg, q=FAKE, pool=FAKE, nb=10, bt=FAKE, mb=4, sl=FAKE, cap=256, B=2,
+                  T=1, causal=1, ns=0, tot=0, ws=None, wsb=0, o=FAKE, lse=None):
+    return lib.mla_decode_fused(ctypes.byref(cfg) if cfg is not None else None, q, pool, nb, bt,
+                                mb, sl, cap, B, T, causal, ns, tot, ws, wsb, o, lse, None)
+
+
+def test_decode_fused_validation(lib):
+    cfg = v3_cfg()
+    ctr = binding.mla_decode_fused_counter_bytes()
+    assert ctr == 256 << 10
+    # the same argument checks as mla_decode
+    assert _decode_fused(lib, None) == NULL
+    assert _decode_fused(lib, v3_cfg(dtype=7)) == DTYPE
+    assert _decode_fused(lib, cfg, T=0) == DIM
+    assert _decode_fused(lib, cfg, causal=2) == DIM
+    assert _decode_fused(lib, cfg, cap=4 * 64 + 1) == CAP
+    assert _decode_fused(lib, cfg, q=None) == NULL
+    assert _decode_fused(lib, cfg, q=FAKE_MIS) == ALIGN
+    # only the bf16 MFMA shape (d_c 512, d_rope 64, 64-row pages)
+    for bad in (v3_cfg(dtype="f32"), v3_cfg(d_c=256), v3_cfg(d_rope=32), v3_cfg(block_size=16)):
+        assert _decode_fused(lib, bad, cap=64) == DIM
+        with pytest.raises(RuntimeError):
+            binding.mla_decode_fused_workspace_size(bad, 2, 1, 256, 0, 0)
+    # the workspace always holds the counter region, then the partials
+    need = binding.mla_decode_fused_workspace_size(cfg, 2, 1, 256, 0, 1)
+    assert need >= ctr
+    need4 = binding.mla_decode_fused_workspace_size(cfg, 2, 1, 256, 0, 4)
+    assert need4 == need + mla.mla_decode_workspace_size(cfg, 2, 1, 256, 0, 4)
+    assert _decode_fused(lib, cfg, ns=4) == WS
+    assert _decode_fused(lib, cfg, ns=4, ws=FAKE, wsb=need4 - 1) == WS
+    assert _decode_fused(lib, cfg, ns=4, ws=FAKE_MIS, wsb=need4) == ALIGN
+    # (sequence, 64-row group) pairs beyond what the counter region holds
+    B_big = 4000
+    with pytest.raises(RuntimeError):
+        binding.mla_decode_fused_workspace_size(cfg, B_big, 1, 256, 0, 1)
+    assert _decode_fused(lib, cfg, B=B_big, ws=FAKE, wsb=1 << 40) == DIM
+    assert _decode_fused(lib, cfg, B=0) == OK
+
+
 def test_workspace_and_split_plan(lib):
     cfg = v3_cfg()
     # one split needs no workspace
