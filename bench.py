@@ -380,6 +380,34 @@ def capture(torch, steps, fn):
     return g
 
 
+def fused_phase(torch, mla, steps, reps, us_two_kernel, cache_bytes, flops) -> dict:
+    """mla_decode_fused (split-KV attention and merge in one launch) on the
+    same rotated copies: per-call time, its roofline, and whether it left the
+    same o_lat / lse bits as mla_decode (it does whenever the plan is plain;
+    a balanced plan writes its one-split sequences directly, without the
+    bf16 partial round trip)."""
+    st0 = steps[0]
+    st0.decode()
+    torch.cuda.synchronize()
+    o_ref, lse_ref = st0.o_lat.clone(), st0.lse.clone()
+    for st in steps:              # workspaces allocated (zeroed) outside the graph
+        st.decode_fused()
+    torch.cuda.synchronize()
+    same = bool(torch.equal(st0.o_lat.view(torch.int32), o_ref.view(torch.int32)) and
+                torch.equal(st0.lse.view(torch.int32), lse_ref.view(torch.int32)))
+    rel = float((st0.o_lat - o_ref).abs().max() / o_ref.abs().max().clamp_min(1e-30))
+    g = capture(torch, steps, lambda st: st.decode_fused())
+    dec = replay_stats(torch, g, len(steps), reps)
+    del g
+    ctr = mla.mla_decode_fused_counter_bytes()
+    zero = all(int(torch.count_nonzero(st.fused_workspace[:ctr])) == 0 for st in steps)
+    rl = roofline(cache_bytes, flops, dec["median"])
+    return {"call_us": dec, "vs_two_kernel": us_two_kernel / dec["median"],
+            "roofline": {k: rl[k] for k in ("bound", "achieved", "peak", "unit", "frac")},
+            "bitwise_equal_to_mla_decode": same, "max_rel_diff_to_mla_decode": rel,
+            "counters_left_zero": zero}
+
+
 def extra_workload(name, args, torch, mla, DecodeStep, reps) -> dict:
     """mla_decode of another workload, timed the same way as the main one
     (rotated copies, per-replay events), with its own roofline; the
@@ -407,6 +435,8 @@ def extra_workload(name, args, torch, mla, DecodeStep, reps) -> dict:
            "algorithmic_flops_per_launch": flops,
            "roofline": roofline(cache_bytes, flops, dec["median"]),
            "rotated_copies": len(steps)}
+    log(f"{name}: one-launch decode")
+    out["decode_fused"] = fused_phase(torch, mla, steps, reps, dec["median"], cache_bytes, flops)
     if w.T > 1:
         gs = capture(torch, steps, lambda st: st.run())
         stp = replay_stats(torch, gs, len(steps), reps)
@@ -568,6 +598,9 @@ def main() -> int:
                    "gcn_arch": getattr(props, "gcnArchName", "")},
     }
     del step_graphs
+    log("one-launch decode")
+    line["decode_fused"] = fused_phase(torch, mla, steps, args.phase_reps, us_decode,
+                                       cache_bytes, decode_flops)
     line["achievable_hbm"] = streaming_read(torch, mla)
     if line["roofline"]["unit"] == "GB/s":  # the measured read rate beside the published peak
         ach = line["achievable_hbm"]["read_GBps"]

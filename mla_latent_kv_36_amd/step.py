@@ -67,6 +67,22 @@ class DecodeStep:
                        num_splits=self.num_splits, total_tokens_host=self.total_tokens,
                        workspace=self.workspace, stream=stream)
 
+    def decode_fused(self, stream=None):
+        """decode in one launch (mla_decode_fused) into the same outputs; its
+        workspace is allocated zeroed on first use and left zeroed by every
+        call."""
+        if getattr(self, "fused_workspace", None) is None:
+            nbytes = mla.mla_decode_fused_workspace_size(self.cfg, self.B, self.T,
+                                                         self.max_len_after, self.total_tokens,
+                                                         self.num_splits)
+            self.fused_workspace = torch.zeros(nbytes, dtype=torch.uint8,
+                                               device=self.q_abs.device)
+        mla.mla_decode_fused(self.cfg, self.q_abs, self.pool, self.block_table, self.seq_lens,
+                             self.max_len_after, self.o_lat, self.lse,
+                             workspace=self.fused_workspace, causal=self.causal,
+                             num_splits=self.num_splits, total_tokens_host=self.total_tokens,
+                             stream=stream)
+
     def out_proj(self, stream=None):
         mla.mla_out_proj(self.cfg, self.o_lat.view(self.M, self.H, -1), self.w_uv, self.out,
                          stream)
