@@ -522,9 +522,10 @@ def main() -> int:
         if args.num_splits == 0 else args.num_splits
     stream = torch.cuda.current_stream()
 
-    # The step: one graph per rotated copy (absorb + append, decode,
-    # out-projection), replayed in turn: `warmup` untimed steps, then exactly
-    # `steps` timed ones between two synchronisations.
+    # The step: one graph per rotated copy (absorb + append, then decode +
+    # out-projection: mla_absorb_q_append and mla_decode_out_proj), replayed
+    # in turn: `warmup` untimed steps, then exactly `steps` timed ones between
+    # two synchronisations.
     step_graphs = [capture(torch, [st], lambda x: x.run()) for st in steps]
     for i in range(args.warmup):
         step_graphs[i % len(step_graphs)].replay()
@@ -545,7 +546,8 @@ def main() -> int:
     phase_fns = {"decode": lambda st: st.decode(), "absorb_q": lambda st: st.absorb(),
                  "cache_append": lambda st: st.append(),
                  "absorb_q_append": lambda st: st.absorb_append(),
-                 "out_proj": lambda st: st.out_proj()}
+                 "out_proj": lambda st: st.out_proj(),
+                 "decode_out_proj": lambda st: st.decode_out_proj()}
     phases = {}
     for name, fn in phase_fns.items():
         g = capture(torch, steps, fn)

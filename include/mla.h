@@ -228,6 +228,29 @@ mla_status mla_decode_noalloc(const mla_config* cfg, const void* q_abs, const vo
 size_t mla_decode_noalloc_scratch_bytes(void);
 
 /*
+ * mla_decode_out_proj -- mla_decode followed by mla_out_proj on its o_lat
+ * (out[b, t, h, :] = W^UV[h] o_lat[b, t, h, :]: "Attention, Part 2", section
+ * "The trick that makes it fast", W^UV applied once per head after the sum in
+ * latent space), with the log-sum-exp merge of the split partials and the
+ * up-projection in one launch where they can share it (bf16, d_c = 512,
+ * d_rope = 64, 64-row pages, d_v a multiple of 4, and a plan with more than
+ * one split): each head's merged rows go from the partials straight into the
+ * projection's operand tiles.  Otherwise the calls' own launches run in turn.
+ * Arguments as mla_decode's (same workspace, mla_decode_workspace_size), plus
+ * w_uv [H, d_v, d_c] and out [B*T, H, d_v] (cfg->dtype) as mla_out_proj's;
+ * o_lat and lse are written as mla_decode writes them, and out equals what
+ * mla_out_proj computes from that o_lat, bit for bit.  Every check of both
+ * calls runs before any launch.
+ */
+mla_status mla_decode_out_proj(const mla_config* cfg, const void* q_abs, const void* pool,
+                               int32_t num_blocks, const int32_t* block_table,
+                               int32_t max_blocks, const int32_t* seq_lens,
+                               int32_t max_seq_len_host, int32_t B, int32_t T, int32_t causal,
+                               int32_t num_splits, int64_t total_tokens_host, const void* w_uv,
+                               void* workspace, size_t workspace_bytes, float* o_lat, float* lse,
+                               void* out, void* stream);
+
+/*
  * mla_decode_fused -- mla_decode's split-KV attention and its log-sum-exp
  * merge in ONE kernel launch, for batches of variable-length sequences
  * ("Research on MLA": the fused, variable-length and megakernel decoders it

@@ -60,6 +60,8 @@ _SIGNATURES = {
     "mla_decode_noalloc": (_I, [_CFG, _P, _P, _I, _P, _I, _P, _I, _I, _I, _I, _I,
                                 ctypes.c_int64, _P, _P, _P]),
     "mla_decode_noalloc_scratch_bytes": (ctypes.c_size_t, []),
+    "mla_decode_out_proj": (_I, [_CFG, _P, _P, _I, _P, _I, _P, _I, _I, _I, _I, _I,
+                                 ctypes.c_int64, _P, _P, ctypes.c_size_t, _P, _P, _P, _P]),
     "mla_decode_fused_workspace_size": (ctypes.c_size_t, [_CFG, _I, _I, _I, ctypes.c_int64,
                                                           _I]),
     "mla_decode_fused_counter_bytes": (ctypes.c_size_t, []),
@@ -232,6 +234,32 @@ def mla_decode_noalloc(cfg: MlaConfig, q_abs: torch.Tensor, pool: torch.Tensor,
 
 def mla_decode_noalloc_scratch_bytes() -> int:
     return int(load().mla_decode_noalloc_scratch_bytes())
+
+
+def mla_decode_out_proj(cfg: MlaConfig, q_abs: torch.Tensor, pool: torch.Tensor,
+                        block_table: torch.Tensor, seq_lens: torch.Tensor, max_seq_len_host: int,
+                        w_uv: torch.Tensor, o_lat: torch.Tensor, out: torch.Tensor,
+                        lse: Optional[torch.Tensor] = None, *, causal: bool = True,
+                        num_splits: int = 0, total_tokens_host: int = 0,
+                        workspace: Optional[torch.Tensor] = None, stream=None) -> None:
+    """mla_decode then mla_out_proj on its o_lat, the merge and the projection
+    sharing a launch where they can."""
+    dt = _TORCH_DTYPE[cfg.dtype]
+    _dev(q_abs, dt, "q_abs"), _dev(pool, dt, "pool"), _dev(o_lat, torch.float32, "o_lat")
+    _dev(block_table, torch.int32, "block_table"), _dev(seq_lens, torch.int32, "seq_lens")
+    _dev(w_uv, dt, "w_uv"), _dev(out, dt, "out")
+    if lse is not None:
+        _dev(lse, torch.float32, "lse")
+    B, T = q_abs.shape[0], q_abs.shape[1]
+    ws_bytes = 0
+    if workspace is not None:
+        ws_bytes = workspace.numel() * workspace.element_size()
+    _check(load().mla_decode_out_proj(ctypes.byref(cfg), _ptr(q_abs), _ptr(pool), pool.shape[0],
+                                      _ptr(block_table), block_table.shape[1], _ptr(seq_lens),
+                                      int(max_seq_len_host), B, T, 1 if causal else 0,
+                                      int(num_splits), int(total_tokens_host), _ptr(w_uv),
+                                      _ptr(workspace), ws_bytes, _ptr(o_lat), _ptr(lse),
+                                      _ptr(out), _stream(stream)))
 
 
 def mla_decode_fused_workspace_size(cfg: MlaConfig, B: int, T: int, max_seq_len_host: int,

@@ -370,13 +370,16 @@ static mla_status check_decode(const mla_config* cfg, const void* q_abs, const v
 
 // Launches a checked decode under plan pl with its partials in `workspace`
 // (at least partial_bytes(pl) bytes when pl needs a merge).
+// With w_uv, out_proj follows (out = W^UV o_lat): in the merge's launch where
+// the MFMA kernels apply and the plan has splits, else as a launch of its own.
 static mla_status launch_decode_plan(const mla_config* cfg, const Plan& pl,
                                      const DeviceShape& dev, const void* q_abs,
                                      const void* pool, int32_t num_blocks,
                                      const int32_t* block_table, int32_t max_blocks,
                                      const int32_t* seq_lens, int32_t max_seq_len_host,
                                      int32_t B, int32_t T, int32_t causal, void* workspace,
-                                     float* o_lat, float* lse, hipStream_t s) {
+                                     float* o_lat, float* lse, hipStream_t s,
+                                     const void* w_uv = nullptr, void* out = nullptr) {
   size_t lse_off = 0;
   size_t plan_off = 0;
   const bool merge = pl.splits > 1;
@@ -413,10 +416,17 @@ static mla_status launch_decode_plan(const mla_config* cfg, const Plan& pl,
   hipError_t e = use_mfma(cfg, T) ? mla::launch_decode_mfma(p, s)
                                   : mla::launch_decode_generic(p, cfg->dtype, s);
   if (e != hipSuccess) return MLA_ERR_HIP;
+  const bool proj = w_uv != nullptr;
+  if (merge && proj && p.part_bf16 &&
+      mla::merge_out_proj_supported(cfg->dtype, cfg->d_c, cfg->d_v))
+    return hip_status(mla::launch_merge_out_proj(p, w_uv, out, cfg->d_v, s));
   if (merge) {
     e = mla::launch_combine(p, s);
     if (e != hipSuccess) return MLA_ERR_HIP;
   }
+  if (proj)
+    return hip_status(mla::launch_out_proj(cfg->dtype, o_lat, w_uv, out, B * T, cfg->n_heads,
+                                           cfg->d_c, cfg->d_v, s));
   return MLA_OK;
 }
 
@@ -441,6 +451,36 @@ mla_status mla_decode(const mla_config* cfg, const void* q_abs, const void* pool
 }
 
 size_t mla_decode_noalloc_scratch_bytes(void) { return kScratchBytes; }
+
+mla_status mla_decode_out_proj(const mla_config* cfg, const void* q_abs, const void* pool,
+                               int32_t num_blocks, const int32_t* block_table,
+                               int32_t max_blocks, const int32_t* seq_lens,
+                               int32_t max_seq_len_host, int32_t B, int32_t T, int32_t causal,
+                               int32_t num_splits, int64_t total_tokens_host, const void* w_uv,
+                               void* workspace, size_t workspace_bytes, float* o_lat, float* lse,
+                               void* out, void* stream) {
+  bool work;
+  mla_status st = check_decode(cfg, q_abs, pool, num_blocks, block_table, max_blocks, seq_lens,
+                               max_seq_len_host, B, T, causal, num_splits, o_lat, lse, &work);
+  if (st != MLA_OK) return st;
+  // mla_out_proj's checks, also before anything is launched
+  if (cfg->d_v <= 0) return MLA_ERR_DIM;
+  if ((int64_t)B * T > 0x7fffffffLL || ((int64_t)B * T + 15) / 16 > 65535 ||
+      ((int64_t)cfg->d_v + 15) / 16 > 65535)
+    return MLA_ERR_DIM;
+  if (!work) return MLA_OK;
+  if (w_uv == nullptr || out == nullptr) return MLA_ERR_NULL;
+  if (!aligned16(w_uv) || !aligned16(out)) return MLA_ERR_ALIGN;
+  if (workspace != nullptr && !aligned16(workspace)) return MLA_ERR_ALIGN;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const DeviceShape dev = device_shape(s, true);
+  const Plan pl = make_plan(cfg, B, T, max_seq_len_host, total_tokens_host, num_splits, dev);
+  const size_t need = pl.splits > 1 ? partial_bytes(cfg, B, T, pl, nullptr, nullptr) : 0;
+  if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return MLA_ERR_WORKSPACE;
+  return launch_decode_plan(cfg, pl, dev, q_abs, pool, num_blocks, block_table, max_blocks,
+                            seq_lens, max_seq_len_host, B, T, causal, workspace, o_lat, lse, s,
+                            w_uv, out);
+}
 
 // Workspace of the one-launch decode: the counter region (zero on entry), the
 // per-group merge records, the balanced plan's table, then the partials as

@@ -62,6 +62,12 @@ hipError_t launch_absorb_q(int dtype, const void* q_nope, const void* q_rope,
                            int d_r, hipStream_t stream);
 hipError_t launch_out_proj(int dtype, const float* o_lat, const void* w_uv, void* out,
                            int M, int H, int d_c, int d_v, hipStream_t stream);
+// The merge of bf16 split partials (p as for launch_combine, with o_lat) and
+// out_proj in one launch: out[m, h, :] = W^UV[h] o_lat[m, h, :], o_lat and lse
+// written as the merge kernel would.  bf16, d_c = 512.
+bool merge_out_proj_supported(int dtype, int d_c, int d_v);
+hipError_t launch_merge_out_proj(const DecodeParams& p, const void* w_uv, void* out, int d_v,
+                                 hipStream_t stream);
 // The cache append's arguments, for a kernel that carries the append along
 // with its own work (rows == 0: no append).
 struct AppendArgs {

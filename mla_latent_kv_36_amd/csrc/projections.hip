@@ -21,6 +21,7 @@
 // B column l & 15, the same k; D column l & 15, rows 4(l >> 4) .. +3.
 #include "common.h"
 #include "launch.h"
+#include "merge.h"
 
 namespace mla {
 namespace {
@@ -546,6 +547,154 @@ __global__ __launch_bounds__(PJ_NT) void out_proj_mfma_kernel(
   for (int m0 = mbeg + 16; m0 < mend; m0 += 16) tile(m0);
 }
 
+// The log-sum-exp merge of the split partials and out_proj in one launch.
+// Workgroup (h, vb, mz): value columns vb*128 .. +127 of head h for query
+// rows mz*mt .. +mt-1, in tiles of MO_TR rows; 8 waves, wave w holding
+// W^UV[h][v][:] for its 16 columns v (the A operand, as in
+// out_proj_mfma_kernel).  Each tile of o_lat is not read but merged from the
+// bf16 split partials (the merge kernel's per-row arithmetic, lane l taking
+// latent columns 8l .. 8l+7) straight into the LDS staging, MO_TR / 8 query
+// rows per wave with all of their loads in flight together; with d_v <= 128
+// every partial is read once.  The
+// staged values are the ones the merge kernel would have written to o_lat, so
+// `out` equals the two launches' bit for bit.  Workgroups of vb = 0 write
+// o_lat and lse as well (o_lat: streaming stores).
+constexpr int MO_NT = 512;                  // 8 waves
+constexpr int MO_VT = 16 * (MO_NT / 64);    // value columns per workgroup
+
+// MO_TR: query rows per tile, 16 or 8 (the MFMA's 16 columns, half used): at
+// 16 rows or fewer, tiles of 8 make two workgroups per head, so that the
+// whole chip streams the partials and W^UV (each CU's share of the memory
+// bandwidth is the limit, and the pair, 128 workgroups apart, shares an XCD's
+// L2 for W^UV); with more rows, tiles of 16 keep the re-reads of W^UV down.
+template <int MO_TR>
+__global__ __launch_bounds__(MO_NT) void merge_out_proj_kernel(const DecodeParams p,
+                                                               const uint16_t* __restrict__ w_uv,
+                                                               uint16_t* __restrict__ out,
+                                                               int d_v, int mt) {
+  __shared__ __align__(16) uint8_t st[2][16 * OP_LD];  // hi, lo
+  const int H = p.H, T = p.T;
+  const int M = p.B * T;
+  const int h = blockIdx.x, vb = blockIdx.y;
+  const int mbeg = blockIdx.z * mt, mend = min(M, mbeg + mt);
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int i16 = lane & 15, g = lane >> 4;
+  const int vrow = vb * MO_VT + 16 * wave + i16;  // A row of this lane
+  constexpr int MO_RW = MO_TR / (MO_NT / 64);     // query rows each wave merges per tile
+
+  // W^UV fragments first (clamped row: rows past d_v feed outputs that are
+  // not stored), so that they are in flight with the first tile's partials
+  bf16x8 a[OP_KS];
+  const uint16_t* wrow = w_uv + ((size_t)h * d_v + min(vrow, d_v - 1)) * 512 + 8 * g;
+#pragma unroll
+  for (int ks = 0; ks < OP_KS; ++ks) a[ks] = load_bf16x8(wrow + 32 * ks);
+
+  const int v0 = vb * MO_VT + 16 * wave + 4 * g;  // this lane's 4 output columns
+  if constexpr (MO_TR < 16) {  // the staged rows past the tile's stay zero
+    const u16x8 z = {0, 0, 0, 0, 0, 0, 0, 0};
+    for (int r = MO_TR + wave; r < 16; r += MO_NT / 64) {
+      *reinterpret_cast<u16x8*>(st[0] + r * OP_LD + 16 * lane) = z;
+      *reinterpret_cast<u16x8*>(st[1] + r * OP_LD + 16 * lane) = z;
+    }
+  }
+  for (int m0 = mbeg; m0 < mend; m0 += MO_TR) {
+    // query rows m0 + MO_RW wave + i (clamped to the last row: rows past mend
+    // are merged again and staged as zeros); the sequence's splits from the
+    // plan, as the merge kernel takes them
+    int bq[MO_RW], tq[MO_RW], P0[MO_RW], S[MO_RW], ch[MO_RW];
+    bool few = true;  // at most 8 splits in each of the rows
+#pragma unroll
+    for (int i = 0; i < MO_RW; ++i) {
+      const int m = min(m0 + MO_RW * wave + i, mend - 1);
+      bq[i] = m / T;
+      tq[i] = m - bq[i] * T;
+      if (p.plan != nullptr) {
+        // scalar loads (the index is uniform): their wait leaves the vector
+        // loads in flight
+        const int32_t __attribute__((address_space(4)))* e =
+            (const int32_t __attribute__((address_space(4)))*)p.plan + 4 * (size_t)bq[i];
+        P0[i] = e[0];
+        S[i] = e[1];
+        ch[i] = e[2] * 32;
+      } else {
+        P0[i] = bq[i] * p.num_splits;
+        S[i] = p.num_splits;
+        ch[i] = p.chunk_rows;
+      }
+      // a sequence without splits has no visible row: its loads go to split
+      // 0 with a count of 1, which then merges no split (o = 0, lse = -inf)
+      if (S[i] == 0) {
+        P0[i] = 0;
+        S[i] = 1;
+        ch[i] = 32;
+      }
+      few = few && S[i] <= 8;
+    }
+    f32x4 lo[MO_RW], hi[MO_RW];
+    float lse[MO_RW];
+    if (few) {
+      Row8Loads L[MO_RW];
+#pragma unroll
+      for (int i = 0; i < MO_RW; ++i)
+        row8_issue<false>(p, bq[i], tq[i] * H + h, lane, P0[i], S[i], L[i]);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int i = 0; i < MO_RW; ++i) row8_hold(L[i]);
+#pragma unroll
+      for (int i = 0; i < MO_RW; ++i)
+        row8_finish(p, L[i], tq[i], lane, S[i], ch[i], lo[i], hi[i], lse[i]);
+    } else {
+      for (int i = 0; i < MO_RW; ++i)
+        row_merge512<false>(p, bq[i], tq[i] * H + h, tq[i], lane, P0[i], S[i], ch[i], lo[i],
+                            hi[i], lse[i]);
+    }
+    // stage as bf16 hi / lo (out_proj's split of an fp32 o_lat value)
+#pragma unroll
+    for (int i = 0; i < MO_RW; ++i) {
+      const int r = MO_RW * wave + i, m = m0 + r;
+      const bool live = m < mend;
+      if (live && vb == 0) {
+        float* ol = p.o_lat + ((size_t)m * H + h) * 512 + 8 * lane;
+        __builtin_nontemporal_store(lo[i], reinterpret_cast<f32x4*>(ol));
+        __builtin_nontemporal_store(hi[i], reinterpret_cast<f32x4*>(ol + 4));
+        if (lane == 0 && p.lse != nullptr) p.lse[(size_t)m * H + h] = lse[i];
+      }
+      u16x8 hb, lb;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float x = live ? (e < 4 ? lo[i][e] : hi[i][e - 4]) : 0.0f;
+        hb[e] = f32_to_bf16(x);
+        lb[e] = f32_to_bf16(x - bf16_to_f32(hb[e]));
+      }
+      *reinterpret_cast<u16x8*>(st[0] + r * OP_LD + 16 * lane) = hb;
+      *reinterpret_cast<u16x8*>(st[1] + r * OP_LD + 16 * lane) = lb;
+    }
+    __syncthreads();
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    const int boff = i16 * OP_LD + 16 * g;
+#pragma unroll
+    for (int ks = 0; ks < OP_KS; ++ks) {
+      const bf16x8 bh = *reinterpret_cast<const bf16x8*>(st[0] + boff + 64 * ks);
+      const bf16x8 bl = *reinterpret_cast<const bf16x8*>(st[1] + boff + 64 * ks);
+      acc = mfma16(a[ks], bh, acc);
+      acc = mfma16(a[ks], bl, acc);
+    }
+    const int m = m0 + i16;
+    if (i16 < MO_TR && m < mend && v0 < d_v) {
+      uint16_t* dst = out + ((size_t)m * H + h) * d_v + v0;
+      if (v0 + 3 < d_v) {
+        store_bf16x4(dst, acc);
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (v0 + i < d_v) dst[i] = f32_to_bf16(acc[i]);
+      }
+    }
+    __syncthreads();  // the next tile overwrites the staging buffer
+  }
+}
+
 // absorb_q_mfma_kernel for ceil(d_n / 32) k-steps (1 .. AB_KS)
 hipError_t launch_absorb_kernel(dim3 grid, size_t shmem, hipStream_t stream,
                                 const uint16_t* q_nope, const uint16_t* q_rope,
@@ -658,6 +807,27 @@ hipError_t launch_out_proj(int dtype, const float* o_lat, const void* w_uv, void
   else
     hipLaunchKernelGGL(out_proj_kernel<uint16_t>, grid, dim3(256), 0, stream, o_lat,
                        (const uint16_t*)w_uv, (uint16_t*)out, M, H, d_c, d_v);
+  return hipGetLastError();
+}
+
+bool merge_out_proj_supported(int dtype, int d_c, int d_v) {
+  return dtype == 1 && d_c == 512 && out_proj_mfma_fits(d_c, d_v);
+}
+
+hipError_t launch_merge_out_proj(const DecodeParams& p, const void* w_uv, void* out, int d_v,
+                                 hipStream_t stream) {
+  const int M = p.B * p.T;
+  if (M <= 0) return hipSuccess;
+  if (!p.part_bf16 || p.d_c != 512 || !out_proj_mfma_fits(512, d_v) || p.o_lat == nullptr)
+    return hipErrorInvalidValue;
+  const int mt = M <= 16 ? 8 : pj_rows_per_wg(M);
+  const dim3 grid(p.H, (d_v + MO_VT - 1) / MO_VT, (M + mt - 1) / mt);
+  if (M <= 16)
+    hipLaunchKernelGGL(merge_out_proj_kernel<8>, grid, dim3(MO_NT), 0, stream, p,
+                       (const uint16_t*)w_uv, (uint16_t*)out, d_v, mt);
+  else
+    hipLaunchKernelGGL(merge_out_proj_kernel<16>, grid, dim3(MO_NT), 0, stream, p,
+                       (const uint16_t*)w_uv, (uint16_t*)out, d_v, mt);
   return hipGetLastError();
 }
 

@@ -1,8 +1,9 @@
 """One MLA decode step as the four library calls, on device buffers.
 
 ``DecodeStep`` owns the outputs and the workspace of one step and runs
-absorb -> append -> decode -> out-projection on the current stream.  It is
-plumbing around the C ABI (allocation through torch, then four calls); all of
+absorb -> append -> decode -> out-projection on the current stream (the step
+as two calls: absorb with append, decode with out-projection).  It is
+plumbing around the C ABI (allocation through torch, then the library calls); all of
 the arithmetic happens in libmla's kernels.
 """
 from __future__ import annotations
@@ -87,7 +88,15 @@ class DecodeStep:
         mla.mla_out_proj(self.cfg, self.o_lat.view(self.M, self.H, -1), self.w_uv, self.out,
                          stream)
 
+    def decode_out_proj(self, stream=None):
+        """decode and out_proj in one call (the merge and the projection share
+        a launch where they can)."""
+        mla.mla_decode_out_proj(self.cfg, self.q_abs, self.pool, self.block_table, self.seq_lens,
+                                self.max_len_after, self.w_uv, self.o_lat, self.out, self.lse,
+                                causal=self.causal, num_splits=self.num_splits,
+                                total_tokens_host=self.total_tokens, workspace=self.workspace,
+                                stream=stream)
+
     def run(self, stream=None):
         self.absorb_append(stream)
-        self.decode(stream)
-        self.out_proj(stream)
+        self.decode_out_proj(stream)

@@ -113,6 +113,36 @@ def test_decode_noalloc_validation(lib):
     assert _decode_noalloc(lib, cfg, B=B, T=T, mb=512, cap=cap, ns=64, tot=B * cap) == WS
 
 
+def _decode_out_proj(lib, cfg, q=FAKE, pool=FAKE, nb=10, bt=FAKE, mb=4, sl=FAKE, cap=256, B=2,
+                     T=1, causal=1, ns=0, tot=0, w_uv=FAKE, ws=None, wsb=0, o=FAKE, lse=None,
+                     out=FAKE):
+    return lib.mla_decode_out_proj(ctypes.byref(cfg) if cfg is not None else None, q, pool, nb,
+                                   bt, mb, sl, cap, B, T, causal, ns, tot, w_uv, ws, wsb, o, lse,
+                                   out, None)
+
+
+def test_decode_out_proj_validation(lib):
+    cfg = v3_cfg()
+    # mla_decode's checks
+    assert _decode_out_proj(lib, None) == NULL
+    assert _decode_out_proj(lib, v3_cfg(dtype=7)) == DTYPE
+    assert _decode_out_proj(lib, cfg, T=0) == DIM
+    assert _decode_out_proj(lib, cfg, cap=4 * 64 + 1) == CAP
+    assert _decode_out_proj(lib, cfg, q=None) == NULL
+    assert _decode_out_proj(lib, cfg, o=None) == NULL
+    # mla_out_proj's
+    assert _decode_out_proj(lib, v3_cfg(d_v=0)) == DIM
+    assert _decode_out_proj(lib, cfg, w_uv=None) == NULL
+    assert _decode_out_proj(lib, cfg, out=None) == NULL
+    assert _decode_out_proj(lib, cfg, out=FAKE_MIS) == ALIGN
+    assert _decode_out_proj(lib, cfg, w_uv=FAKE_MIS) == ALIGN
+    # mla_decode's workspace
+    need = mla.mla_decode_workspace_size(cfg, 2, 1, 256, 0, 4)
+    assert _decode_out_proj(lib, cfg, ns=4) == WS
+    assert _decode_out_proj(lib, cfg, ns=4, ws=FAKE, wsb=need - 1) == WS
+    assert _decode_out_proj(lib, cfg, B=0) == OK
+
+
 def _decode_fused(lib, cfg, q=FAKE, pool=FAKE, nb=10, bt=FAKE, mb=4, sl=FAKE, cap=256, B=2,
                   T=1, causal=1, ns=0, tot=0, ws=None, wsb=0, o=FAKE, lse=None):
     return lib.mla_decode_fused(ctypes.byref(cfg) if cfg is not None else None, q, pool, nb, bt,
