@@ -387,6 +387,11 @@ def fused_phase(torch, mla, steps, reps, us_two_kernel, cache_bytes, flops) -> d
     a balanced plan writes its one-split sequences directly, without the
     bf16 partial round trip)."""
     st0 = steps[0]
+    try:
+        mla.mla_decode_fused_workspace_size(st0.cfg, st0.B, st0.T, st0.max_len_after,
+                                            st0.total_tokens, st0.num_splits)
+    except RuntimeError as e:  # a shape the one-launch decode does not take
+        return {"supported": False, "reason": str(e)}
     st0.decode()
     torch.cuda.synchronize()
     o_ref, lse_ref = st0.o_lat.clone(), st0.lse.clone()
