@@ -107,8 +107,10 @@ int heuristic_splits(const mla_config* c, int B, int T, int gran_max, int64_t gr
                      int cus) {
   if (gran_max <= 1) return 1;
   if (use_mfma(c, T)) return mfma_splits(c, T, gran_max, gran_total, cus);
-  const int64_t qrows = (int64_t)B * T * c->n_heads;
-  int64_t s = (4 * (int64_t)cus + qrows - 1) / qrows;
+  // generic kernel: a workgroup per group of heads of one new token and split
+  const int64_t groups =
+      (int64_t)B * T * ((c->n_heads + mla::kGenericHeads - 1) / mla::kGenericHeads);
+  int64_t s = (4 * (int64_t)cus + groups - 1) / groups;
   if (s > gran_max) s = gran_max;
   return (int)(s < 1 ? 1 : s);
 }

@@ -1,15 +1,23 @@
 // Split-KV latent-attention decode for any shape and element type (fp32 or
 // bf16): the path for shapes the MFMA kernel does not cover (for example fp32
-// caches or latent widths other than 512).  It is a plain flash-decoding loop:
-// one workgroup = one query row (b, t, h) x one split, 256 rows of the cache
-// per step, fp32 throughout.
+// caches or latent widths other than 512).  A flash-decoding loop, fp32
+// throughout: one workgroup = GH heads of one new token (b, t) x one split,
+// GR cached rows per step, so that each cached row is read once for GH heads
+// instead of once per head.
 //
-// Per step: each thread scores one cached row against the absorbed query held
-// in LDS (content and rotary terms in one dot product, "Attention, Part 2: MQA,
-// GQA and MLA", section "Why position needs its own key"), the block takes the
-// step maximum, rescales its running sum and accumulator, and accumulates the
-// weighted latents (the first d_c columns of each row, "How DeepSeek Rewrote
-// the Transformer", section "Absorbed projections", point 3).
+// Per step:
+//  * scores: wave w takes rows w, w + 4, ... of the step; its lanes split the
+//    row's columns (coalesced loads), each loaded element feeds the GH dot
+//    products against the absorbed queries held in LDS (content and rotary
+//    terms in one dot product, "Attention, Part 2: MQA, GQA and MLA", section
+//    "Why position needs its own key");
+//  * softmax: thread (head, row) takes one score; each head's GR scores sit in
+//    one half-wave, which forms the step maximum and sum; a head's running
+//    maximum and sum live in LDS;
+//  * values: thread d accumulates latent column d of every head from the
+//    weighted rows (the first d_c columns of each row, "How DeepSeek Rewrote
+//    the Transformer", section "Absorbed projections", point 3), each loaded
+//    element feeding GH accumulators.
 #include "common.h"
 #include "launch.h"
 #include "merge.h"
@@ -19,7 +27,160 @@ namespace {
 
 constexpr int NT = 256;
 constexpr int MAX_DC_PER_THREAD = 8;  // d_c <= 2048
+constexpr int GH = kGenericHeads;     // heads per workgroup
+constexpr int GR = NT / GH;           // cached rows per step (32: a half-wave per head)
 
+template <typename E>
+__global__ __launch_bounds__(NT) void decode_generic_kernel(const DecodeParams p) {
+  extern __shared__ float smem[];
+  const int W = p.d_c + p.d_r;
+  float* sq = smem;              // [GH][W] queries
+  float* sp = sq + GH * W;       // [GH][GR] scores, then probabilities, of the step
+  float* sal = sp + GH * GR;     // [GH] rescale factor of the step
+  float* sm_m = sal + GH;        // [GH] running maximum (log2 domain)
+  float* sm_l = sm_m + GH;       // [GH] running sum
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int TH = p.T * p.H;
+  const int gpt = (p.H + GH - 1) / GH;  // head groups per new token
+  const int bt = blockIdx.x / gpt;
+  const int h0 = (blockIdx.x - bt * gpt) * GH;
+  const int b = bt / p.T, t = bt - b * p.T;
+  const int nh = min(GH, p.H - h0);     // heads of this group
+  const int s = blockIdx.y;
+  const int bs = p.block_size;
+  const int n_valid = visible_rows(p.seq_lens[b], p.T, t, p.causal, p.cap);
+  const int j0 = s * p.chunk_rows;
+  const int j1 = min(j0 + p.chunk_rows, n_valid);
+  const bool direct = (p.num_splits == 1);
+  auto dst_of = [&](int hh) {
+    const size_t rr = (size_t)t * p.H + h0 + hh;
+    return direct ? p.o_lat + ((size_t)b * TH + rr) * p.d_c
+                  : static_cast<float*>(p.part_o) + (((size_t)b * p.num_splits + s) * TH + rr) * p.d_c;
+  };
+
+  if (j0 >= j1) {
+    if (direct) {
+      for (int i = tid; i < nh * p.d_c; i += NT) dst_of(i / p.d_c)[i % p.d_c] = 0.0f;
+      if (tid < nh && p.lse != nullptr) p.lse[(size_t)b * TH + (size_t)t * p.H + h0 + tid] = -INFINITY;
+    }
+    return;
+  }
+
+  const E* qb = static_cast<const E*>(p.q_abs) + ((size_t)b * TH + (size_t)t * p.H + h0) * W;
+  for (int i = tid; i < GH * W; i += NT) {
+    const int hh = i / W;  // heads past the group's last take its last one (not stored)
+    sq[i] = Elem<E>::load(qb + (size_t)min(hh, nh - 1) * W, i - hh * W);
+  }
+  if (tid < GH) {
+    sm_m[tid] = -INFINITY;
+    sm_l[tid] = 0.0f;
+  }
+  __syncthreads();
+
+  const E* pool = static_cast<const E*>(p.pool);
+  const int32_t* table = p.block_table + (size_t)b * p.max_blocks;
+  auto row_ptr = [&](int j) {
+    const int blk = clamp_block(table[j / bs], p.num_blocks);
+    return pool + ((size_t)blk * bs + (j % bs)) * W;
+  };
+
+  float acc[GH][MAX_DC_PER_THREAD];
+#pragma unroll
+  for (int hh = 0; hh < GH; ++hh)
+#pragma unroll
+    for (int i = 0; i < MAX_DC_PER_THREAD; ++i) acc[hh][i] = 0.0f;
+
+  for (int jb = j0; jb < j1; jb += GR) {
+    const int n = min(GR, j1 - jb);
+    // scores of the step's rows for every head of the group
+    for (int r = wave; r < GR; r += NT / 64) {
+      float dot[GH];
+#pragma unroll
+      for (int hh = 0; hh < GH; ++hh) dot[hh] = 0.0f;
+      if (r < n) {
+        const E* row = row_ptr(jb + r);
+        for (int k = lane; k < W; k += 64) {
+          const float x = Elem<E>::load(row, k);
+#pragma unroll
+          for (int hh = 0; hh < GH; ++hh) dot[hh] += sq[hh * W + k] * x;
+        }
+      }
+#pragma unroll
+      for (int hh = 0; hh < GH; ++hh) {
+        float v = dot[hh];
+        for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+        if (lane == 0) sp[hh * GR + r] = r < n ? v * p.scale_log2 : -INFINITY;
+      }
+    }
+    __syncthreads();
+    // online softmax: thread (hh, r), the GR scores of a head in one half-wave
+    {
+      const int hh = tid / GR, r = tid - hh * GR;
+      const float v = sp[hh * GR + r];
+      float mx = v;
+      for (int o = GR / 2; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
+      const float m_old = sm_m[hh];
+      const float m_new = fmaxf(m_old, mx);  // finite: every step holds a row
+      const float e = exp2f(v - m_new);      // 0 for rows past the range
+      float sum = e;
+      for (int o = GR / 2; o > 0; o >>= 1) sum += __shfl_xor(sum, o);
+      sp[hh * GR + r] = e;
+      __syncthreads();  // every thread has read sm_m before it changes
+      if (r == 0) {
+        const float alpha = exp2f(m_old - m_new);  // 0 on the first step
+        sal[hh] = alpha;
+        sm_l[hh] = sm_l[hh] * alpha + sum;
+        sm_m[hh] = m_new;
+      }
+    }
+    __syncthreads();
+    // values: latent column d of every head from the weighted rows
+#pragma unroll
+    for (int i = 0; i < MAX_DC_PER_THREAD; ++i) {
+      const int d = tid + i * NT;
+      if (d < p.d_c) {
+        float a[GH];
+#pragma unroll
+        for (int hh = 0; hh < GH; ++hh) a[hh] = acc[hh][i] * sal[hh];
+        for (int jj = 0; jj < n; ++jj) {
+          const float x = Elem<E>::load(row_ptr(jb + jj), d);
+#pragma unroll
+          for (int hh = 0; hh < GH; ++hh) a[hh] += sp[hh * GR + jj] * x;
+        }
+#pragma unroll
+        for (int hh = 0; hh < GH; ++hh) acc[hh][i] = a[hh];
+      }
+    }
+    __syncthreads();  // sp and sal are rewritten by the next step
+  }
+
+#pragma unroll
+  for (int hh = 0; hh < GH; ++hh) {
+    if (hh >= nh) break;
+    const float inv = 1.0f / sm_l[hh];
+    float* dst = dst_of(hh);
+#pragma unroll
+    for (int i = 0; i < MAX_DC_PER_THREAD; ++i) {
+      const int d = tid + i * NT;
+      if (d < p.d_c) dst[d] = acc[hh][i] * inv;
+    }
+  }
+  if (tid < nh) {
+    const float v = (sm_m[tid] + log2f(sm_l[tid])) * kLn2;
+    const size_t rr = (size_t)t * p.H + h0 + tid;
+    if (direct) {
+      if (p.lse != nullptr) p.lse[(size_t)b * TH + rr] = v;
+    } else {
+      p.part_lse[((size_t)b * p.num_splits + s) * TH + rr] = v;
+    }
+  }
+}
+
+// For launches too small to fill the chip with head groups: one workgroup per
+// query row (b, t, h) x split, NT cached rows per step -- each thread scores
+// one row against the query held in LDS, the block takes the step maximum and
+// sum, and each thread accumulates latent columns of the weighted rows.
 __device__ __forceinline__ float block_max(float v, float* red) {
   for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
   const int w = threadIdx.x >> 6;
@@ -43,7 +204,7 @@ __device__ __forceinline__ float block_sum(float v, float* red) {
 }
 
 template <typename E>
-__global__ __launch_bounds__(NT) void decode_generic_kernel(const DecodeParams p) {
+__global__ __launch_bounds__(NT) void decode_generic_head_kernel(const DecodeParams p) {
   extern __shared__ float smem[];
   const int W = p.d_c + p.d_r;
   float* sq = smem;          // [W] query
@@ -148,10 +309,22 @@ __global__ __launch_bounds__(64 * CMB_ROWS) void combine_kernel(const DecodePara
 }  // namespace
 
 hipError_t launch_decode_generic(const DecodeParams& p, int dtype, hipStream_t stream) {
-  const long long rows = (long long)p.B * p.T * p.H;
-  if (rows <= 0) return hipSuccess;
-  const size_t shmem = (size_t)(p.d_c + p.d_r + NT + NT / 64) * sizeof(float);
-  const dim3 grid((unsigned)rows, (unsigned)p.num_splits);
+  const long long groups = (long long)p.B * p.T * ((p.H + GH - 1) / GH);
+  if (groups <= 0) return hipSuccess;
+  if (groups > 0x7fffffffLL) return hipErrorInvalidValue;
+  if (groups * p.num_splits < 128) {
+    // too few head groups to fill half the chip: a workgroup per query row
+    const long long rows = (long long)p.B * p.T * p.H;
+    const size_t shmem = (size_t)(p.d_c + p.d_r + NT + NT / 64) * sizeof(float);
+    const dim3 grid((unsigned)rows, (unsigned)p.num_splits);
+    if (dtype == 0)
+      hipLaunchKernelGGL(decode_generic_head_kernel<float>, grid, dim3(NT), shmem, stream, p);
+    else
+      hipLaunchKernelGGL(decode_generic_head_kernel<uint16_t>, grid, dim3(NT), shmem, stream, p);
+    return hipGetLastError();
+  }
+  const size_t shmem = (size_t)(GH * (p.d_c + p.d_r) + GH * GR + 3 * GH) * sizeof(float);
+  const dim3 grid((unsigned)groups, (unsigned)p.num_splits);
   if (dtype == 0)
     hipLaunchKernelGGL(decode_generic_kernel<float>, grid, dim3(NT), shmem, stream, p);
   else

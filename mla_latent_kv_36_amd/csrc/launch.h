@@ -54,6 +54,9 @@ hipError_t launch_decode_mfma(const DecodeParams& p, hipStream_t stream);
 // persistent workgroups (one per compute unit fits): work items from a queue,
 // merges of a group's partials taken up once its last split has arrived.
 hipError_t launch_decode_queue(const DecodeParams& p, int workgroups, hipStream_t stream);
+// The generic kernel: a workgroup per (kGenericHeads heads of one new token,
+// split).
+constexpr int kGenericHeads = 8;
 hipError_t launch_decode_generic(const DecodeParams& p, int dtype, hipStream_t stream);
 hipError_t launch_combine(const DecodeParams& p, hipStream_t stream);
 

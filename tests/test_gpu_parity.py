@@ -43,6 +43,12 @@ REDUCED = {
     "bf16_h80_t3": V3.scaled(B=3, T=3, H=80, N=250),
     # bf16 with a latent width the MFMA kernel does not take: the generic kernel
     "bf16_dc256_generic": V3.scaled(B=2, d_c=256, N=200),
+    # generic kernel launches large enough for its head-group form (8 heads per
+    # workgroup sharing each cached row): fp32, bf16 with d_c = 256, and 20
+    # heads (groups of 8, 8 and 4); one split falls back to a workgroup per head
+    "f32_groups": V3.scaled(B=6, H=64, N=300, dtype="f32"),
+    "bf16_dc256_groups": V3.scaled(B=6, H=64, d_c=256, N=300),
+    "f32_h20_groups": V3.scaled(B=16, H=20, N=300, dtype="f32"),
     # a prefill chunk: 64 causal queries per sequence over a ragged cache
     "prefill": PREFILL.scaled(B=2, T=64, N=200),
 }
