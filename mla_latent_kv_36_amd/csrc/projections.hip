@@ -212,6 +212,19 @@ __global__ __launch_bounds__(PJ_NT) void absorb_q_mfma_kernel(
 #pragma unroll
   for (int t = 0; t < NT; ++t) load_q(mbeg + 16 * t, bq[t]);  // rows past mend: clamped
 
+  // The rotary part is carried over unchanged (by the workgroups cb == 0),
+  // 16 bytes at a time.  Its first pass of pieces is requested here, with the
+  // other loads, so that the copy at the end costs no memory round trip of
+  // its own (every workgroup requests it; it is a few KiB, mostly from L2).
+  const int chunks = d_r / 8;
+  const int nrope = (mend - mbeg) * chunks;
+  u32x4 rv0 = {0u, 0u, 0u, 0u};
+  if (chunks > 0) {  // q_rope may be absent when d_r = 0
+    const int i = min(tid, nrope - 1);
+    const int m = mbeg + i / chunks, r = 8 * (i % chunks);
+    rv0 = *reinterpret_cast<const u32x4*>(q_rope + ((size_t)m * H + h) * d_r + r);
+  }
+
   // the weight slice: every piece is loaded (unconditional) before the first
   // is stored, so staging costs one memory latency; nks * 32 rows of 16
   // pieces make exactly 2 * nks pieces per thread
@@ -271,9 +284,12 @@ __global__ __launch_bounds__(PJ_NT) void absorb_q_mfma_kernel(
   for (int t = 0; t < NT; ++t)
     if (mbeg + 16 * t < mend) tile(mbeg + 16 * t, bq[t]);
 
-  if (cb == 0) {  // the rotary part is carried over unchanged, 16 bytes at a time
-    const int chunks = d_r / 8;
-    for (int i = tid; i < (mend - mbeg) * chunks; i += PJ_NT) {
+  if (cb == 0) {  // the rotary part: the first pass from registers, any further ones direct
+    if (tid < nrope) {
+      const int m = mbeg + tid / chunks, r = 8 * (tid % chunks);
+      *reinterpret_cast<u32x4*>(q_abs + ((size_t)m * H + h) * W + d_c + r) = rv0;
+    }
+    for (int i = tid + PJ_NT; i < nrope; i += PJ_NT) {
       const int m = mbeg + i / chunks, r = 8 * (i % chunks);
       *reinterpret_cast<u32x4*>(q_abs + ((size_t)m * H + h) * W + d_c + r) =
           *reinterpret_cast<const u32x4*>(q_rope + ((size_t)m * H + h) * d_r + r);
