@@ -28,6 +28,10 @@ CASES = {
     "v2_reduced": V2_MULTI.scaled(B=3, N=300),
     # more tokens than one 64-row tile, T = 1
     "v2_many_tokens": V2_MULTI.scaled(B=70, T=1, N=100),
+    # a ragged 64-column tile (d_c + d_r = 560) and a k range of 33 steps
+    "ragged_cols": V2_MULTI.scaled(B=25, T=3, N=70, d_r=48, d_model=1056),
+    # five 64-token tiles
+    "v2_300_tokens": V2_MULTI.scaled(B=75, T=4, N=40),
     # generic kernel: a width that is not a multiple of 32
     "bf16_odd_width": V2_MULTI.scaled(B=2, N=90, d_model=200),
     # fp32 cache: the generic kernel
