@@ -280,7 +280,11 @@ def output_side_phase(w, torch, mla, reps) -> dict:
     st_o = replay_stats(torch, g, copies, reps)
     us = st_o["median"]
     algo = wo_bytes + M * K * elem + M * d * elem
-    out = {"o_proj": {"call": "mla_o_proj", "kernels": "wo_gemm_mfma_kernel + wo_finish_kernel",
+    # the library's kernel for these token rows: up to 16 the register-streaming
+    # kernel, up to 128 bf16 rows the LDS-streaming kernel, more the tiled GEMM
+    o_kernel = ("wo_stream_direct_kernel" if M <= 16 else
+                "wo_stream_lds_kernel" if M <= 128 and w.dtype == "bf16" else "wo_gemm_mfma_kernel")
+    out = {"o_proj": {"call": "mla_o_proj", "kernels": o_kernel + " + wo_finish_kernel",
                       "tokens": M, "k": K, "d_model": d, "us": us, "bound": "hbm",
                       "algorithmic_bytes": algo, "GBps": algo / (us * 1e-6) / 1e9,
                       "frac": algo / (us * 1e-6) / 1e9 / HBM_PEAK_GBPS, "us_stats": st_o,

@@ -29,7 +29,7 @@
 //     leave compute units idle; the splits' fp32 partial sums are then added
 //     in split order by a second kernel (deterministic);
 //   * 17 to 128 bf16 token rows take a streaming form instead: all tokens in
-//     one tile and 256 weight rows per workgroup, both operands brought in by
+//     one tile and 128 weight rows per workgroup, both operands brought in by
 //     direct-to-LDS copies through a ring several chunks deep (below);
 //     up to 16 tokens take a form with no LDS (below).
 // fp32 token rows are rounded to bf16 when staged (the product is bf16 x bf16
@@ -251,24 +251,31 @@ __global__ __launch_bounds__(WO_NT) void wo_stream_direct_kernel(
 }
 
 // The same product for 16 < M <= 128 bf16 token rows: every token in one
-// tile, so the weight is streamed once, and 256 weight rows per workgroup, so
-// that the token rows (read again by every workgroup) are a third of the
-// bytes moved.  Workgroup (256 weight rows, k split): the k range is cut into
-// chunks of one MFMA k-step (32 k); each chunk's 256 weight rows and 128
-// token rows (clamped to M - 1) reach LDS as direct-to-LDS copies (sixteen
+// tile, so the weight is streamed once, and 128 weight rows per workgroup.
+// The token rows are read again by every workgroup (from L2), half of the
+// bytes a workgroup moves; in exchange the k range needs half as many splits
+// for the same number of workgroups, which halves the fp32 partial sums
+// written and read back (at 128 tokens and a 5,120 x 5,120 weight: 15.7 MB
+// instead of 31.5 MB for 256 rows; measured 26.8 against 30.0 us, while 64
+// rows, 7.9 MB of partials, took 31.7 us).  Workgroup (128 weight rows, k
+// split): the k range is cut into chunks of one MFMA k-step (32 k); each
+// chunk's 128 weight rows and 128 token rows (clamped to M - 1) reach LDS as
+// direct-to-LDS copies (sixteen
 // 64-byte rows per copy; 16-byte chunk c of row r at position
 // c ^ ((r >> 2) & 3), so that the 16 rows an operand reads at one k fall in
 // distinct banks) through a ring of WS_SLOTS slots, WS_SLOTS - 1 chunks ahead
 // of the MFMAs: the bytes in flight per compute unit, which bound its rate
-// at this latency, fill most of the LDS.  Wave w takes weight rows
-// 64w .. 64w+63 (4 A tiles) against the 8 token tiles (B).  Copies past the
+// at this latency (a deeper ring, 8 or 9 slots, was slower).  Wave w takes
+// weight rows 32w .. 32w+31 (2 A tiles) against the 8 token tiles (B).
+// Copies past the
 // split's k range re-read clamped, finite values that are not multiplied.
-constexpr int WS_TN = 256;      // weight rows per workgroup
+constexpr int WS_AT_ = 2;                // 16-row weight tiles per wave
+constexpr int WS_TN = 64 * WS_AT_;       // weight rows per workgroup (128)
 constexpr int WS_TM = 128;      // token rows (all of them)
 constexpr int WS_SLOTS = 6;
 constexpr int WS_ROW = 64;                              // bytes per staged row (32 k)
-constexpr int WS_SLOT = (WS_TM + WS_TN) * WS_ROW;       // 24 KiB
-constexpr int WS_COPIES = (WS_TM + WS_TN) / 16 / 4;     // copies per wave per chunk (6)
+constexpr int WS_SLOT = (WS_TM + WS_TN) * WS_ROW;       // 16 KiB
+constexpr int WS_COPIES = (WS_TM + WS_TN) / 16 / 4;     // copies per wave per chunk (4)
 
 template <int N_>
 __device__ __forceinline__ void wait_copies_ahead(int ahead) {
@@ -324,9 +331,9 @@ __global__ __launch_bounds__(256) void wo_stream_lds_kernel(
     }
   };
 
-  f32x4 acc[4][WS_TM / 16];
+  f32x4 acc[WS_AT_][WS_TM / 16];
 #pragma unroll
-  for (int at = 0; at < 4; ++at)
+  for (int at = 0; at < WS_AT_; ++at)
 #pragma unroll
     for (int j = 0; j < WS_TM / 16; ++j) acc[at][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
@@ -340,21 +347,22 @@ __global__ __launch_bounds__(256) void wo_stream_lds_kernel(
     const uint8_t* sl = ring + (c % WS_SLOTS) * WS_SLOT;
     // operand rows R read here have (R >> 2) & 3 == (l16 >> 2) & 3 (R = 16 k + l16)
     const int off = 16 * (g ^ ((l16 >> 2) & 3));
-    bf16x8 a[4];
+    bf16x8 a[WS_AT_];
 #pragma unroll
-    for (int at = 0; at < 4; ++at)
-      a[at] = *reinterpret_cast<const bf16x8*>(sl + (WS_TM + 64 * wave + 16 * at + l16) * WS_ROW + off);
+    for (int at = 0; at < WS_AT_; ++at)
+      a[at] = *reinterpret_cast<const bf16x8*>(
+          sl + (WS_TM + 16 * WS_AT_ * wave + 16 * at + l16) * WS_ROW + off);
 #pragma unroll
     for (int j = 0; j < WS_TM / 16; ++j) {
       const bf16x8 b = *reinterpret_cast<const bf16x8*>(sl + (16 * j + l16) * WS_ROW + off);
 #pragma unroll
-      for (int at = 0; at < 4; ++at) acc[at][j] = mfma16(a[at], b, acc[at][j]);
+      for (int at = 0; at < WS_AT_; ++at) acc[at][j] = mfma16(a[at], b, acc[at][j]);
     }
   }
-  // D: lane l holds token 16j + (l & 15), outputs 64w + 16at + 4(l >> 4) .. +3
+  // D: lane l holds token 16j + (l & 15), outputs 32w + 16at + 4(l >> 4) .. +3
 #pragma unroll
-  for (int at = 0; at < 4; ++at) {
-    const int n = n0 + 64 * wave + 16 * at + 4 * g;
+  for (int at = 0; at < WS_AT_; ++at) {
+    const int n = n0 + 16 * WS_AT_ * wave + 16 * at + 4 * g;
     if (n >= N) continue;
 #pragma unroll
     for (int j = 0; j < WS_TM / 16; ++j) {
