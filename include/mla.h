@@ -381,7 +381,9 @@ mla_status mla_rope(const mla_config* cfg, void* x, int32_t heads, const int32_t
  *
  * Both products accumulate in fp32 and round once.  When the k dimension is
  * split over workgroups, the partial sums go to `workspace` (device) and are
- * added in a fixed order (reruns are bit-exact): it must hold
+ * added in a fixed order (reruns are bit-exact); for 17 to 128 fp32 rows
+ * (mla_o_proj_folded) the workspace also takes their bf16 copy, rounded in a
+ * first launch and then streamed like bf16 rows.  It must hold
  * mla_o_proj_workspace_size(cfg, M, d_model, folded) bytes (0: none needed, NULL
  * allowed), else MLA_ERR_WORKSPACE; its contents on entry do not matter.
  * mla_o_proj_workspace_size returns (size_t)-1 for invalid arguments.  M == 0

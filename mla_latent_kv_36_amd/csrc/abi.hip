@@ -749,9 +749,9 @@ bool output_x_f32(const mla_config* c, bool folded) { return folded || c->dtype 
 
 size_t output_workspace(const mla_config* c, int M, int d_model, bool folded) {
   const int64_t K = output_k(c, folded);
-  const int ks = mla::wo_gemm_ksplit(c->dtype, output_x_f32(c, folded), M, d_model, (int)K,
-                                     output_workgroups());
-  return ks > 1 ? round256((size_t)ks * M * d_model * sizeof(float)) : 0;
+  const bool x_f32 = output_x_f32(c, folded);
+  const int ks = mla::wo_gemm_ksplit(c->dtype, x_f32, M, d_model, (int)K, output_workgroups());
+  return mla::wo_gemm_workspace_bytes(c->dtype, x_f32, M, d_model, (int)K, ks);
 }
 
 mla_status output_args(const mla_config* cfg, int32_t M, int32_t d_model, bool folded) {
@@ -775,8 +775,8 @@ mla_status output_call(const mla_config* cfg, bool folded, const void* x, const 
   const int K = (int)output_k(cfg, folded);
   const bool x_f32 = output_x_f32(cfg, folded);
   const int ks = mla::wo_gemm_ksplit(cfg->dtype, x_f32, M, d_model, K, output_workgroups());
-  if (ks > 1 && (workspace == nullptr || workspace_bytes < output_workspace(cfg, M, d_model, folded)))
-    return MLA_ERR_WORKSPACE;
+  const size_t need = output_workspace(cfg, M, d_model, folded);
+  if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return MLA_ERR_WORKSPACE;
   const hipStream_t s = static_cast<hipStream_t>(stream);
   return hip_status(mla::launch_wo_gemm(cfg->dtype, x_f32, x, w, y, static_cast<float*>(workspace),
                                         ks, M, d_model, K, device_shape(s, true).xcds, s));

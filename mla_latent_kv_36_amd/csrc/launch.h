@@ -117,6 +117,9 @@ hipError_t launch_rope(int dtype, void* x, const int32_t* positions, int M, int 
 // placement).
 bool wo_gemm_mfma_supported(int dtype, int N, int K);
 int wo_gemm_ksplit(int dtype, bool x_f32, int M, int N, int K, int target_workgroups);
+// Workspace of one product: a bf16 copy of fp32 token rows where the
+// streaming kernel takes them (first), then the split partial sums.
+size_t wo_gemm_workspace_bytes(int dtype, bool x_f32, int M, int N, int K, int ksplit);
 hipError_t launch_wo_gemm(int dtype, bool x_f32, const void* x, const void* w, void* y,
                           float* part, int ksplit, int M, int N, int K, int xcds,
                           hipStream_t stream);

@@ -28,7 +28,8 @@
 //   * the k dimension is split over workgroups when the tiles alone would
 //     leave compute units idle; the splits' fp32 partial sums are then added
 //     in split order by a second kernel (deterministic);
-//   * 17 to 128 bf16 token rows take a streaming form instead: all tokens in
+//   * 17 to 128 token rows (fp32 ones rounded to bf16 first, in a launch of
+//     their own) take a streaming form instead: all tokens in
 //     one tile and 128 weight rows per workgroup, both operands brought in by
 //     direct-to-LDS copies through a ring several chunks deep (below);
 //     up to 16 tokens take a form with no LDS (below).
@@ -380,6 +381,24 @@ __global__ __launch_bounds__(256) void wo_stream_lds_kernel(
   }
 }
 
+// fp32 token rows rounded to bf16 (round to nearest even, as the tiled
+// kernel rounds them when it stages them): 8 values per thread, n8 = n / 8.
+__global__ __launch_bounds__(256) void wo_round_x_kernel(const float* __restrict__ x,
+                                                         uint16_t* __restrict__ x16,
+                                                         size_t n8) {
+  const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n8) return;
+  const f32x4 a = *reinterpret_cast<const f32x4*>(x + 8 * i);
+  const f32x4 b = *reinterpret_cast<const f32x4*>(x + 8 * i + 4);
+  u16x8 h;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    h[e] = f32_to_bf16(a[e]);
+    h[e + 4] = f32_to_bf16(b[e]);
+  }
+  *reinterpret_cast<u16x8*>(x16 + 8 * i) = h;
+}
+
 // y[m, n .. n+3] = sum over splits z (in order) of part[z, m, n .. n+3],
 // rounded to bf16; one thread per 4 outputs.  The loads of up to 16 splits
 // are issued (on clamped indices) before the first is added.
@@ -481,8 +500,19 @@ bool wo_gemm_mfma_supported(int dtype, int N, int K) {
 // as many workgroups with twice the k range each run slower; the staged rows
 // of a workgroup lie within 2^32 bytes of its first)
 static bool wo_stream_lds_fits(int dtype, bool x_f32, int M, int N, int K) {
-  return wo_gemm_mfma_supported(dtype, N, K) && !x_f32 && M > 16 && M <= WS_TM &&
+  (void)x_f32;  // fp32 token rows are rounded to bf16 first, into the workspace
+  return wo_gemm_mfma_supported(dtype, N, K) && M > 16 && M <= WS_TM &&
          (long long)WS_TM * K * 2 < (1LL << 32) && (long long)WS_TN * K * 2 < (1LL << 32);
+}
+
+// Bytes of the bf16 copy of fp32 token rows that the streaming kernel reads
+// (placed first in the workspace, the split partial sums after it), or 0.
+// Rounding once up front lets every workgroup stream the rows as 64-byte bf16
+// pieces, where the tiled kernel would re-read them as fp32 for each 64-row
+// weight tile (the folded product at 128 tokens: 208 against 380 us).
+static size_t wo_x16_bytes(int dtype, bool x_f32, int M, int N, int K) {
+  if (!x_f32 || !wo_stream_lds_fits(dtype, x_f32, M, N, K)) return 0;
+  return ((size_t)M * K * 2 + 255) / 256 * 256;
 }
 
 int wo_gemm_ksplit(int dtype, bool x_f32, int M, int N, int K, int target_workgroups) {
@@ -506,6 +536,11 @@ int wo_gemm_ksplit(int dtype, bool x_f32, int M, int N, int K, int target_workgr
   if (ks > nk) ks = nk;
   const int per = (int)((nk + ks - 1) / ks);
   return (nk + per - 1) / per;
+}
+
+size_t wo_gemm_workspace_bytes(int dtype, bool x_f32, int M, int N, int K, int ksplit) {
+  const size_t parts = ksplit > 1 ? ((size_t)ksplit * M * N * sizeof(float) + 255) / 256 * 256 : 0;
+  return wo_x16_bytes(dtype, x_f32, M, N, K) + parts;
 }
 
 hipError_t launch_wo_gemm(int dtype, bool x_f32, const void* x, const void* w, void* y,
@@ -540,10 +575,22 @@ hipError_t launch_wo_gemm(int dtype, bool x_f32, const void* x, const void* w, v
     const int per = (nk + ksplit - 1) / ksplit;
     const long long tiles = (long long)((N + WS_TN - 1) / WS_TN) * ksplit;
     if (tiles > 0x7fffffffLL) return hipErrorInvalidValue;
-    if (ksplit > 1 && part == nullptr) return hipErrorInvalidValue;
+    const size_t x16b = wo_x16_bytes(dtype, x_f32, M, N, K);
+    if ((ksplit > 1 || x16b > 0) && part == nullptr) return hipErrorInvalidValue;
+    const uint16_t* xs = static_cast<const uint16_t*>(x);
+    if (x16b > 0) {  // fp32 token rows: one rounding pass into the workspace
+      uint16_t* x16 = reinterpret_cast<uint16_t*>(part);
+      const size_t n8 = (size_t)M * K / 8;
+      hipLaunchKernelGGL(wo_round_x_kernel, dim3((unsigned)((n8 + 255) / 256)), dim3(256), 0,
+                         stream, static_cast<const float*>(x), x16, n8);
+      hipError_t e0 = hipGetLastError();
+      if (e0 != hipSuccess) return e0;
+      xs = x16;
+      part = reinterpret_cast<float*>(reinterpret_cast<uint8_t*>(part) + x16b);
+    }
     uint16_t* yd = ksplit == 1 ? static_cast<uint16_t*>(y) : nullptr;
     hipLaunchKernelGGL(wo_stream_lds_kernel, dim3((unsigned)tiles), dim3(256),
-                       (size_t)WS_SLOTS * WS_SLOT, stream, static_cast<const uint16_t*>(x),
+                       (size_t)WS_SLOTS * WS_SLOT, stream, xs,
                        static_cast<const uint16_t*>(w), yd, part, M, N, K, per, xcds);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || ksplit == 1) return e;

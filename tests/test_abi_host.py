@@ -306,15 +306,18 @@ def test_producer_and_rope_validation(lib):
 
 def test_output_side_validation(lib):
     """mla_o_proj / mla_fold_uv_o / mla_o_proj_folded: host checks and the
-    split-k workspace (a whole number of fp32 [M, d_model] partial slices)."""
+    split-k workspace (a whole number of fp32 [M, d_model] partial slices; for
+    the folded product's fp32 rows, after their bf16 copy of M x H*d_c)."""
     cfg = v3_cfg(d_v=40)
     c = ctypes.byref(cfg)
     ws = lib.mla_o_proj_workspace_size
     M, d = 128, 5120
+    x16 = -(-(M * cfg.n_heads * cfg.d_c * 2) // 256) * 256
     for folded in (0, 1):
         need = ws(c, M, d, folded)
-        assert need % 256 == 0 and need >= 2 * M * d * 4           # k is split
-        assert need == -(-(need // (M * d * 4) * M * d * 4) // 256) * 256
+        parts = need - (x16 if folded else 0)
+        assert parts % 256 == 0 and parts >= 2 * M * d * 4          # k is split
+        assert parts % (M * d * 4) == 0
     assert ws(c, 0, d, 0) == 0
     assert ws(c, M, 0, 0) == ctypes.c_size_t(-1).value
     assert ws(ctypes.byref(v3_cfg(d_v=0)), M, d, 0) == ctypes.c_size_t(-1).value
