@@ -251,8 +251,9 @@ __global__ __launch_bounds__(WO_NT) void wo_stream_direct_kernel(
   }
 }
 
-// The same product for 16 < M <= 128 bf16 token rows: every token in one
-// tile, so the weight is streamed once, and 128 weight rows per workgroup.
+// The same product for 16 < M <= 128 token rows (bf16, or fp32 rows rounded
+// to bf16 by wo_round_x_kernel first): every token in one tile, so the
+// weight is streamed once, and 128 weight rows per workgroup.
 // The token rows are read again by every workgroup (from L2), half of the
 // bytes a workgroup moves; in exchange the k range needs half as many splits
 // for the same number of workgroups, which halves the fp32 partial sums
@@ -261,15 +262,15 @@ __global__ __launch_bounds__(WO_NT) void wo_stream_direct_kernel(
 // rows, 7.9 MB of partials, took 31.7 us).  Workgroup (128 weight rows, k
 // split): the k range is cut into chunks of one MFMA k-step (32 k); each
 // chunk's 128 weight rows and 128 token rows (clamped to M - 1) reach LDS as
-// direct-to-LDS copies (sixteen
-// 64-byte rows per copy; 16-byte chunk c of row r at position
+// direct-to-LDS copies (sixteen 64-byte rows per copy; 16-byte chunk c of
+// row r at position
 // c ^ ((r >> 2) & 3), so that the 16 rows an operand reads at one k fall in
 // distinct banks) through a ring of WS_SLOTS slots, WS_SLOTS - 1 chunks ahead
 // of the MFMAs: the bytes in flight per compute unit, which bound its rate
 // at this latency (a deeper ring, 8 or 9 slots, was slower).  Wave w takes
 // weight rows 32w .. 32w+31 (2 A tiles) against the 8 token tiles (B).
-// Copies past the
-// split's k range re-read clamped, finite values that are not multiplied.
+// Copies past the split's k range re-read clamped, finite values that are
+// not multiplied.
 constexpr int WS_AT_ = 2;                // 16-row weight tiles per wave
 constexpr int WS_TN = 64 * WS_AT_;       // weight rows per workgroup (128)
 constexpr int WS_TM = 128;      // token rows (all of them)
